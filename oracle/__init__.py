@@ -1,0 +1,22 @@
+"""float64 CPU oracle of the DSV sparse-attention hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only tests/, the smoke check in __graft_entry__ and the bench's CPU-baseline leg
+may import this package.  The product (the HIP library and its binding) never
+does, and the two implementations share no code; they meet only in the seeded
+inputs drawn by the ``synth`` package.
+
+Every function is pinned by tests/test_oracle.py (brute force, a library
+routine, finite differences, closed forms, invariants); none is "parity
+unpinned".
+"""
+from . import dsv_oracle
+from .dsv_oracle import (
+    BLOCK, backward, backward_head, dkdv_blocks, dq_groups, forward, forward_head, group_backward,
+    group_forward, kept_keys, pool_mean, predict, predict_head, reverse_index, select, select_row,
+)
+
+__all__ = [
+    "dsv_oracle", "BLOCK", "backward", "backward_head", "dkdv_blocks", "dq_groups", "forward",
+    "forward_head", "group_backward", "group_forward", "kept_keys", "pool_mean", "predict",
+    "predict_head", "reverse_index", "select", "select_row",
+]

@@ -1,0 +1,237 @@
+"""Plain float64 CPU oracle of DSV's sparse-attention hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product (the HIP library and its
+Python binding) imports, links or calls this module; only the tests, the smoke
+check and the bench's CPU-baseline leg do.  It shares no code with the HIP path.
+
+Source pages: the gist.science explainers (Dutch "nl" and Hindi "hi" editions)
+of "DSV: Exploiting Dynamic Sparsity to Accelerate Large-Scale Video DiT
+Training", cited below by edition and technical-summary section.
+
+What is computed, per batch b and head h, on the exact stored input values
+lifted to float64 (tau = 1/sqrt(d), Bk = 64-token KV blocks, G-token query
+groups of consecutive tokens):
+
+1. pooled proxy query of each group and pooled key of each block (mean);
+2. low-rank projection through the per-head predictor weights W_q, W_k
+   (d x r, r << d)                                   [hi §2.A, nl §2.A]
+3. block score s[g, j] = tau * qhat_g . khat_j -- the predictor's estimate of
+   the group-to-block attention logits              [hi §2.A, §2.B query grouping]
+4. per group, the k_h blocks of largest score, ties to the lowest block id,
+   listed ascending -- the "critical" KV blocks     [hi §2.A, §2.B fused MM + top-k]
+5. exact softmax attention of every query of the group over the keys of its
+   kept blocks only (no mask beyond the selection; bidirectional)
+                                                    [hi §2.A stage 2, nl §2.A fase 2]
+6. the gradient of L = sum(dO * O) with the selection held fixed: dQ, dK, dV
+   (keys in no kept block get exactly zero).  The pages call the method a
+   training system but never write the backward out; this is the standard
+   softmax-attention gradient restricted to the kept keys.
+
+Every function here is pinned by tests/test_oracle.py against brute force on
+tiny inputs, a library routine (torch's scaled_dot_product_attention and
+autograd), central finite differences, closed forms and invariants.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+BLOCK = 64
+
+
+# ----------------------------------------------------------------------------
+# Steps 1-3: predictor (pooling, projection, block scores)
+# ----------------------------------------------------------------------------
+
+def pool_mean(x: np.ndarray, size: int) -> np.ndarray:
+    """Mean over consecutive runs of ``size`` rows: [n, d] -> [n / size, d].
+
+    The proxy query of a query group is the group's centroid, and a KV block is
+    represented by its mean key (hi §2.B query grouping: one proxy per group
+    whose critical indices the whole group reuses).
+    """
+    n, d = x.shape
+    assert n % size == 0
+    return x.reshape(n // size, size, d).mean(axis=1)
+
+
+def predict_head(q: np.ndarray, k: np.ndarray, wq: np.ndarray, wk: np.ndarray,
+                 group: int, block: int = BLOCK) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Low-rank block-score estimate for one (b, h): returns (qhat, khat, scores).
+
+    qhat = pool(Q) W_q [NG, r], khat = pool(K) W_k [NB, r], scores = tau qhat khat^T
+    [NG, NB], tau = 1/sqrt(d) with d the head dimension (hi §2.A: predictors
+    W^Q_lr, W^K_lr estimate QK^T through a d_lr << d_k projection).
+    """
+    d = q.shape[1]
+    tau = 1.0 / np.sqrt(d)
+    qhat = pool_mean(q, group) @ wq
+    khat = pool_mean(k, block) @ wk
+    return qhat, khat, tau * (qhat @ khat.T)
+
+
+def predict(q: np.ndarray, k: np.ndarray, wq: np.ndarray, wk: np.ndarray,
+            group: int, block: int = BLOCK):
+    """predict_head over [B, H, N, d] inputs and [H, d, r] weights."""
+    B, H = q.shape[:2]
+    out = [[predict_head(q[b, h], k[b, h], wq[h], wk[h], group, block) for h in range(H)] for b in range(B)]
+    qhat = np.stack([np.stack([o[0] for o in row]) for row in out])
+    khat = np.stack([np.stack([o[1] for o in row]) for row in out])
+    scores = np.stack([np.stack([o[2] for o in row]) for row in out])
+    return qhat, khat, scores
+
+
+# ----------------------------------------------------------------------------
+# Step 4: top-k critical block selection
+# ----------------------------------------------------------------------------
+
+def select_row(scores_row: np.ndarray, k: int) -> np.ndarray:
+    """The k block ids of largest score, ties to the lowest id, returned ascending.
+
+    Sorting the pairs (-s_j, j) lexicographically and keeping the first k is the
+    definition; -0.0 and +0.0 compare equal, as IEEE equality says (hi §2.A
+    critical KV estimation, §2.B top-k selection).
+    """
+    nb = scores_row.shape[0]
+    assert 1 <= k <= nb
+    s = np.asarray(scores_row)
+    order = np.lexsort((np.arange(nb), -s))      # primary key -s, secondary key j
+    return np.sort(order[:k]).astype(np.int64)
+
+
+def select(scores: np.ndarray, k_per_head: Sequence[int]) -> List[List[np.ndarray]]:
+    """Per (b, h): an [NG, k_h] array of ascending kept block ids."""
+    B, H, NG, _ = scores.shape
+    return [[np.stack([select_row(scores[b, h, g], int(k_per_head[h])) for g in range(NG)])
+             for h in range(H)] for b in range(B)]
+
+
+def reverse_index(idx_bh: np.ndarray, n_blocks: int) -> List[np.ndarray]:
+    """For each KV block j, the ascending list of query groups whose selection holds j."""
+    lists: List[List[int]] = [[] for _ in range(n_blocks)]
+    for g in range(idx_bh.shape[0]):
+        for j in idx_bh[g]:
+            lists[int(j)].append(g)
+    return [np.asarray(l, dtype=np.int64) for l in lists]
+
+
+def kept_keys(idx_row: np.ndarray, block: int = BLOCK) -> np.ndarray:
+    """Key positions covered by the kept blocks of one group, ascending."""
+    return (np.asarray(idx_row, dtype=np.int64)[:, None] * block + np.arange(block)[None, :]).ravel()
+
+
+# ----------------------------------------------------------------------------
+# Step 5: exact attention over the kept keys
+# ----------------------------------------------------------------------------
+
+def group_forward(qg: np.ndarray, k: np.ndarray, v: np.ndarray, keys: np.ndarray):
+    """Softmax attention of the rows of one group over ``keys`` only.
+
+    logits l = tau q k^T; M = row max; LSE = M + ln sum exp(l - M);
+    P = exp(l - LSE); O = P V.  Returns (O [G, d], LSE [G], P [G, |keys|]).
+    """
+    tau = 1.0 / np.sqrt(qg.shape[1])
+    logits = tau * (qg @ k[keys].T)
+    m = logits.max(axis=1, keepdims=True)
+    lse = m[:, 0] + np.log(np.exp(logits - m).sum(axis=1))
+    p = np.exp(logits - lse[:, None])
+    return p @ v[keys], lse, p
+
+
+def forward_head(q, k, v, idx_bh, group, block=BLOCK, groups=None):
+    """O [N, d] and LSE [N] of one (b, h); with ``groups`` only those groups' rows are filled (rest NaN)."""
+    n, d = q.shape
+    o = np.full((n, d), np.nan)
+    lse = np.full(n, np.nan)
+    for g in (range(n // group) if groups is None else groups):
+        rows = slice(g * group, (g + 1) * group)
+        o[rows], lse[rows], _ = group_forward(q[rows], k, v, kept_keys(idx_bh[g], block))
+    return o, lse
+
+
+def forward(q, k, v, idx, group, block=BLOCK):
+    """O [B, H, N, d] and LSE [B, H, N] for per-(b, h) selections ``idx[b][h]``."""
+    B, H = q.shape[:2]
+    o = np.empty(q.shape[:3] + (v.shape[3],))
+    lse = np.empty(q.shape[:3])
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], idx[b][h], group, block)
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# Step 6: gradients with the selection held fixed
+# ----------------------------------------------------------------------------
+
+def group_backward(qg, k, v, dog, keys):
+    """Gradient contributions of one group.
+
+    With P and O from group_forward: D_i = sum_c dO_ic O_ic, dP = dO V^T,
+    dS = P (dP - D), dQ_g = tau dS K, and the key-side terms
+    dK[keys] += tau dS^T Q_g, dV[keys] += P^T dO_g.
+    Returns (dQ_g, dK_part, dV_part, O_g, LSE_g).
+    """
+    tau = 1.0 / np.sqrt(qg.shape[1])
+    og, lse, p = group_forward(qg, k, v, keys)
+    dvec = (dog * og).sum(axis=1)
+    dp = dog @ v[keys].T
+    ds = p * (dp - dvec[:, None])
+    return tau * (ds @ k[keys]), tau * (ds.T @ qg), p.T @ dog, og, lse
+
+
+def backward_head(q, k, v, do, idx_bh, group, block=BLOCK):
+    """dQ, dK, dV [N, d] of one (b, h) for L = sum(dO * O)."""
+    n = q.shape[0]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for g in range(n // group):
+        rows = slice(g * group, (g + 1) * group)
+        keys = kept_keys(idx_bh[g], block)
+        dq_g, dk_p, dv_p, _, _ = group_backward(q[rows], k, v, do[rows], keys)
+        dq[rows] = dq_g
+        dk[keys] += dk_p
+        dv[keys] += dv_p
+    return dq, dk, dv
+
+
+def backward(q, k, v, do, idx, group, block=BLOCK):
+    B, H = q.shape[:2]
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h] = backward_head(q[b, h], k[b, h], v[b, h], do[b, h], idx[b][h], group, block)
+    return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------
+# Sampled evaluation for full-size workloads (same arithmetic, fewer outputs)
+# ----------------------------------------------------------------------------
+
+def dq_groups(q, k, v, do, idx_bh, group, groups, block=BLOCK) -> Dict[int, np.ndarray]:
+    """dQ rows of the listed groups of one (b, h)."""
+    out = {}
+    for g in groups:
+        rows = slice(g * group, (g + 1) * group)
+        out[g] = group_backward(q[rows], k, v, do[rows], kept_keys(idx_bh[g], block))[0]
+    return out
+
+
+def dkdv_blocks(q, k, v, do, idx_bh, group, blocks, block=BLOCK) -> Dict[int, Tuple[np.ndarray, np.ndarray]]:
+    """dK, dV rows of the listed KV blocks of one (b, h), summed over every group that kept them."""
+    rev = reverse_index(idx_bh, k.shape[0] // block)
+    out = {}
+    for j in blocks:
+        dk = np.zeros((block, k.shape[1]))
+        dv = np.zeros((block, v.shape[1]))
+        for g in rev[j]:
+            rows = slice(g * group, (g + 1) * group)
+            keys = kept_keys(idx_bh[g], block)
+            _, dk_p, dv_p, _, _ = group_backward(q[rows], k, v, do[rows], keys)
+            pos = int(np.searchsorted(idx_bh[g], j)) * block
+            dk += dk_p[pos:pos + block]
+            dv += dv_p[pos:pos + block]
+        out[j] = (dk, dv)
+    return out

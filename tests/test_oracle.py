@@ -1,0 +1,338 @@
+"""Pins of the float64 oracle against things other than itself (CPU only).
+
+Each check is a function raising AssertionError; the mutation tests at the end
+plant plausible mistakes into the oracle (on the CPU) and confirm that at least
+one pin fails for each.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import dsv_oracle as O
+from tests import brute
+import synth
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _tiny(seed=0, n=256, d=16, r=8, clustered=True):
+    rng = _rng(seed)
+    q = rng.standard_normal((n, d))
+    k = rng.standard_normal((n, d))
+    if clustered:   # give the selection real structure: a few shared directions
+        cent = rng.standard_normal((4, d)) * 2.0
+        lab = rng.integers(0, 4, size=n)
+        q += cent[lab]
+        k += cent[lab]
+    v = rng.standard_normal((n, d))
+    do = rng.standard_normal((n, d))
+    wq = rng.standard_normal((d, r)) / math.sqrt(d)
+    wk = rng.standard_normal((d, r)) / math.sqrt(d)
+    return q, k, v, do, wq, wk
+
+
+# ---------------------------------------------------------------------------- checks
+
+def check_scores_brute(seed=1, group=64, n=256, d=16, r=8):
+    q, k, _, _, wq, wk = _tiny(seed, n=n, d=d, r=r)
+    qhat, khat, s = O.predict_head(q, k, wq, wk, group)
+    ref = brute.tile_mean_scores(q, k, wq, wk, group)
+    assert qhat.shape == (n // group, r) and khat.shape == (n // 64, r)
+    np.testing.assert_allclose(s, ref, rtol=1e-11, atol=1e-12)
+
+
+def check_identity_predictor(seed=2, group=64):
+    q, k, _, _, _, _ = _tiny(seed, n=384, d=16)
+    eye = np.eye(16)
+    _, _, s = O.predict_head(q, k, eye, eye, group)
+    ref = brute.true_tile_mean(q, k, group)
+    np.testing.assert_allclose(s, ref, rtol=1e-11, atol=1e-12)
+    for kk in (1, 2, 6):
+        for g in range(s.shape[0]):
+            assert list(O.select_row(s[g], kk)) == brute.topk_sorted(ref[g], kk)
+
+
+def check_select_brute(seed=3):
+    rng = _rng(seed)
+    for trial in range(60):
+        nb = int(rng.integers(1, 70))
+        vals = np.array([0.0, -0.0, 1.5, -2.0, 3.25, 1e-30, -1e-30, 7.0])
+        row = rng.choice(vals, size=nb) if trial % 2 else rng.standard_normal(nb)
+        for kk in {1, nb, int(rng.integers(1, nb + 1))}:
+            assert list(O.select_row(row, kk)) == brute.topk_sorted(row, kk), (row, kk)
+
+
+def check_select_special():
+    row = np.array([0.5, 2.0, 2.0, -1.0, 2.0])
+    assert list(O.select_row(row, 1)) == [1]                 # argmax, lowest id among equals
+    assert list(O.select_row(row, 2)) == [1, 2]
+    assert list(O.select_row(row, 5)) == [0, 1, 2, 3, 4]     # k = NB keeps all
+    row0 = np.array([-0.0, 0.0, -3.0])
+    assert list(O.select_row(row0, 1)) == [0]                # -0.0 == +0.0: lowest id
+    row1 = np.array([-1.0, 0.0, -0.0])
+    assert list(O.select_row(row1, 1)) == [1]
+
+
+def check_duplicate_blocks_tie():
+    q, k, _, _, wq, wk = _tiny(4, n=512, d=16)
+    # blocks 1, 4 and 6 are bitwise copies of block 6's keys: their scores are equal
+    for j in (1, 4):
+        k[j * 64:(j + 1) * 64] = k[6 * 64:7 * 64]
+    _, _, s = O.predict_head(q, k, wq, wk, 64)
+    for g in range(s.shape[0]):
+        assert s[g, 1] == s[g, 4] == s[g, 6]
+        order = brute.topk_sorted(s[g], 8)
+        for kk in range(1, 9):
+            sel = list(O.select_row(s[g], kk))
+            assert sel == brute.topk_sorted(s[g], kk)
+            chosen_dup = [j for j in (1, 4, 6) if j in sel]
+            assert chosen_dup == [1, 4, 6][:len(chosen_dup)]   # lowest ids win the tie
+        assert order == list(range(8))
+
+
+def check_linearity(seed=5):
+    q, k, _, _, wq, wk = _tiny(seed)
+    _, _, s = O.predict_head(q, k, wq, wk, 64)
+    _, _, s2 = O.predict_head(q, k, 3.0 * wq, wk, 64)
+    np.testing.assert_allclose(s2, 3.0 * s, rtol=1e-12, atol=1e-13)
+    for g in range(s.shape[0]):
+        assert (O.select_row(s[g], 2) == O.select_row(s2[g], 2)).all()
+
+
+def _sel(s, kk):
+    return np.stack([O.select_row(s[g], kk) for g in range(s.shape[0])])
+
+
+def check_forward_brute(seed=6, group=64, kk=2, n=256):
+    q, k, v, _, wq, wk = _tiny(seed, n=n)
+    _, _, s = O.predict_head(q, k, wq, wk, group)
+    idx = _sel(s, kk)
+    o, lse = O.forward_head(q, k, v, idx, group)
+    mask = brute.mask_from_idx(idx, n, group)
+    o_ref, lse_ref, p_ref = brute.masked_attention(q, k, v, mask)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+    # rows of P sum to one; V = 1 gives O = 1; one-hot V (V = I) exposes P itself
+    for g in range(n // group):
+        rows = slice(g * group, (g + 1) * group)
+        keys = O.kept_keys(idx[g])
+        _, _, p = O.group_forward(q[rows], k, v, keys)
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        ones, _, _ = O.group_forward(q[rows], k, np.ones_like(v), keys)
+        np.testing.assert_allclose(ones, 1.0, rtol=0, atol=1e-12)
+        eye_o, _, _ = O.group_forward(q[rows], k, np.eye(n), keys)
+        np.testing.assert_allclose(eye_o, p_ref[rows], rtol=1e-11, atol=1e-13)
+
+
+def check_dense_equals_sdpa(seed=7, n=256, d=16):
+    q, k, v, do, _, _ = _tiny(seed, n=n, d=d)
+    nb = n // 64
+    idx = np.tile(np.arange(nb), (n // 64, 1))               # k = NB: every block kept
+    o, lse = O.forward_head(q, k, v, idx, 64)
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None])[0]
+    np.testing.assert_allclose(o, ref.detach().numpy(), rtol=1e-11, atol=1e-12)
+    lse_ref = torch.logsumexp(tq @ tk.T / math.sqrt(d), dim=1)
+    np.testing.assert_allclose(lse, lse_ref.detach().numpy(), rtol=1e-12, atol=1e-12)
+    (ref * torch.tensor(do)).sum().backward()
+    dq, dk, dv = O.backward_head(q, k, v, do, idx, 64)
+    for mine, theirs in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(mine, theirs.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def check_sparse_equals_masked_sdpa(seed=8, group=128, n=512, kk=3):
+    q, k, v, do, wq, wk = _tiny(seed, n=n)
+    _, _, s = O.predict_head(q, k, wq, wk, group)
+    idx = _sel(s, kk)
+    mask = torch.tensor(brute.mask_from_idx(idx, n, group))
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None], attn_mask=mask[None])[0]
+    o, _ = O.forward_head(q, k, v, idx, group)
+    np.testing.assert_allclose(o, ref.detach().numpy(), rtol=1e-11, atol=1e-12)
+    (ref * torch.tensor(do)).sum().backward()
+    dq, dk, dv = O.backward_head(q, k, v, do, idx, group)
+    for mine, theirs in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(mine, theirs.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def check_finite_differences(seed=9):
+    n, d = 128, 4
+    q, k, v, do, wq, wk = _tiny(seed, n=n, d=d, r=2)
+    idx = np.array([[1], [0]])                               # group 0 sees block 1, group 1 sees block 0
+    dq, dk, dv = O.backward_head(q, k, v, do, idx, 64)
+    fq, fk, fv = brute.finite_diff_grads(q, k, v, do, brute.mask_from_idx(idx, n, 64))
+    for mine, fd in ((dq, fq), (dk, fk), (dv, fv)):
+        np.testing.assert_allclose(mine, fd, rtol=1e-6, atol=1e-7)
+
+
+def check_gradient_invariants(seed=10, n=512, kk=2):
+    q, k, v, do, wq, wk = _tiny(seed, n=n)
+    _, _, s = O.predict_head(q, k, wq, wk, 64)
+    idx = _sel(s, kk)
+    dq, dk, dv = O.backward_head(q, k, v, do, idx, 64)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-10)            # rows of dS sum to 0
+    np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), atol=1e-10)  # rows of P sum to 1
+    kept = np.zeros(n // 64, dtype=bool)
+    kept[np.unique(idx)] = True
+    for j in np.nonzero(~kept)[0]:
+        assert (dk[j * 64:(j + 1) * 64] == 0).all() and (dv[j * 64:(j + 1) * 64] == 0).all()
+
+
+def check_sampled_match_full(seed=11, n=768, group=64, kk=3):
+    q, k, v, do, wq, wk = _tiny(seed, n=n)
+    _, _, s = O.predict_head(q, k, wq, wk, group)
+    idx = _sel(s, kk)
+    o, lse = O.forward_head(q, k, v, idx, group)
+    o2, lse2 = O.forward_head(q, k, v, idx, group, groups=[0, 5])
+    np.testing.assert_array_equal(o2[:64], o[:64])
+    np.testing.assert_array_equal(lse2[5 * 64:6 * 64], lse[5 * 64:6 * 64])
+    assert np.isnan(o2[64:128]).all()
+    dq, dk, dv = O.backward_head(q, k, v, do, idx, group)
+    for g, rows in O.dq_groups(q, k, v, do, idx, group, [1, 7]).items():
+        np.testing.assert_allclose(rows, dq[g * 64:(g + 1) * 64], rtol=1e-12, atol=1e-13)
+    for j, (dkj, dvj) in O.dkdv_blocks(q, k, v, do, idx, group, [0, 3, 11]).items():
+        np.testing.assert_allclose(dkj, dk[j * 64:(j + 1) * 64], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(dvj, dv[j * 64:(j + 1) * 64], rtol=1e-11, atol=1e-12)
+
+
+def check_reverse_index(seed=12):
+    rng = _rng(seed)
+    nb, ng, kk = 13, 9, 4
+    idx = np.stack([np.sort(rng.choice(nb, kk, replace=False)) for _ in range(ng)])
+    rev = O.reverse_index(idx, nb)
+    for j in range(nb):
+        assert list(rev[j]) == [g for g in range(ng) if j in set(idx[g])]
+
+
+def check_batched_api(seed=13):
+    w = synth.workload(1).with_(grid=(2, 8, 16), heads=2, k=2)
+    inp = synth.generate(w)
+    q, k, v = inp.as_f64("q"), inp.as_f64("k"), inp.as_f64("v")
+    wt = inp.w.astype(np.float64)
+    qhat, khat, s = O.predict(q, k, wt, wt, w.group)
+    idx = O.select(s, inp.k_per_head)
+    o, lse = O.forward(q, k, v, idx, w.group)
+    for h in range(2):
+        _, _, sh = O.predict_head(q[0, h], k[0, h], wt[h], wt[h], w.group)
+        np.testing.assert_array_equal(s[0, h], sh)
+        mask = brute.mask_from_idx(idx[0][h], w.seq_len, w.group)
+        o_ref, lse_ref, _ = brute.masked_attention(q[0, h], k[0, h], v[0, h], mask)
+        np.testing.assert_allclose(o[0, h], o_ref, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(lse[0, h], lse_ref, rtol=1e-12, atol=1e-12)
+
+
+ALL_CHECKS = [
+    check_scores_brute, check_identity_predictor, check_select_brute, check_select_special,
+    check_duplicate_blocks_tie, check_linearity, check_forward_brute, check_dense_equals_sdpa,
+    check_sparse_equals_masked_sdpa, check_finite_differences, check_gradient_invariants,
+    check_sampled_match_full, check_reverse_index, check_batched_api,
+]
+
+
+# ---------------------------------------------------------------------------- tests
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
+def test_pin(check):
+    check()
+
+
+def test_scores_group128():
+    check_scores_brute(seed=21, group=128, n=512)
+
+
+def test_forward_group128():
+    check_forward_brute(seed=22, group=128, kk=3, n=512)
+
+
+# ---------------------------------------------------------------------------- mutations
+
+def _fails_some_pin(monkeypatch, target, replacement, checks):
+    monkeypatch.setattr(O, target, replacement)
+    failed = 0
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            failed += 1
+    monkeypatch.undo()
+    return failed
+
+
+def test_mutation_pool_sum_instead_of_mean(monkeypatch):
+    def bad(x, size):
+        n, d = x.shape
+        return x.reshape(n // size, size, d).sum(axis=1)
+    assert _fails_some_pin(monkeypatch, "pool_mean", bad, [check_scores_brute, check_identity_predictor])
+
+
+def test_mutation_scale_by_rank(monkeypatch):
+    def bad(q, k, wq, wk, group, block=64):
+        qhat = O.pool_mean(q, group) @ wq
+        khat = O.pool_mean(k, block) @ wk
+        return qhat, khat, (qhat @ khat.T) / math.sqrt(wq.shape[1])
+    assert _fails_some_pin(monkeypatch, "predict_head", bad, [check_scores_brute])
+
+
+def test_mutation_swapped_predictors(monkeypatch):
+    orig = O.predict_head
+
+    def bad(q, k, wq, wk, group, block=64):
+        return orig(q, k, wk, wq, group, block)
+    assert _fails_some_pin(monkeypatch, "predict_head", bad, [check_scores_brute])
+
+
+def test_mutation_ties_to_highest_id(monkeypatch):
+    def bad(row, k):
+        nb = row.shape[0]
+        order = np.lexsort((-np.arange(nb), -np.asarray(row)))
+        return np.sort(order[:k])
+    assert _fails_some_pin(monkeypatch, "select_row", bad, [check_select_brute, check_select_special,
+                                                            check_duplicate_blocks_tie])
+
+
+def test_mutation_select_smallest(monkeypatch):
+    def bad(row, k):
+        return np.sort(np.argsort(np.asarray(row), kind="stable")[:k])
+    assert _fails_some_pin(monkeypatch, "select_row", bad, [check_select_brute, check_identity_predictor])
+
+
+def test_mutation_kept_keys_off_by_block(monkeypatch):
+    def bad(idx_row, block=64):
+        return (np.asarray(idx_row)[:, None] * (block - 1) + np.arange(block)[None, :]).ravel()
+    assert _fails_some_pin(monkeypatch, "kept_keys", bad, [check_forward_brute])
+
+
+def test_mutation_no_scale_in_logits(monkeypatch):
+    def bad(qg, k, v, keys):
+        logits = qg @ k[keys].T
+        m = logits.max(axis=1, keepdims=True)
+        lse = m[:, 0] + np.log(np.exp(logits - m).sum(axis=1))
+        p = np.exp(logits - lse[:, None])
+        return p @ v[keys], lse, p
+    assert _fails_some_pin(monkeypatch, "group_forward", bad, [check_forward_brute, check_dense_equals_sdpa])
+
+
+def test_mutation_backward_missing_D(monkeypatch):
+    def bad(qg, k, v, dog, keys):
+        tau = 1.0 / np.sqrt(qg.shape[1])
+        og, lse, p = O.group_forward(qg, k, v, keys)
+        ds = p * (dog @ v[keys].T)
+        return tau * (ds @ k[keys]), tau * (ds.T @ qg), p.T @ dog, og, lse
+    assert _fails_some_pin(monkeypatch, "group_backward", bad, [check_finite_differences, check_gradient_invariants])
+
+
+def test_mutation_backward_transposed_dv(monkeypatch):
+    def bad(qg, k, v, dog, keys):
+        tau = 1.0 / np.sqrt(qg.shape[1])
+        og, lse, p = O.group_forward(qg, k, v, keys)
+        dvec = (dog * og).sum(axis=1)
+        ds = p * (dog @ v[keys].T - dvec[:, None])
+        return tau * (ds @ k[keys]), tau * (ds.T @ qg), (p / p.sum(axis=0, keepdims=True)).T @ dog, og, lse
+    assert _fails_some_pin(monkeypatch, "group_backward", bad, [check_finite_differences, check_sparse_equals_masked_sdpa])

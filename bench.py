@@ -1,0 +1,210 @@
+"""Throughput of the DSV sparse-attention hot path on one MI355X.
+
+One step = predict_block_scores -> select_topk_blocks -> sparse_attn_fwd ->
+sparse_attn_bwd over one batch of seeded synthetic video latents (inputs
+resident in HBM).  Default workload: 57,600 tokens (16x45x80 latent grid),
+24 heads, d = 128, G = 64, 10% of 900 KV blocks kept (k = 90), bf16.
+
+Prints one JSON line.  value = effective TFLOP/s of the step: the counted
+kept-block attention FLOPs (forward 4*G*64*d per kept (group, block) pair,
+backward 2.5x that) divided by the whole step's time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
+PEAK_F32_MFMA = 157.3e12
+PEAK_HBM = 8.0e12       # bytes/s
+METRIC = "sparse-attn fwd+bwd effective TFLOP/s + tokens/s at 57.6k tokens, 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="workload id 1..5 (3 is the headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def kept_pairs(w, kph) -> int:
+    return int(w.batch * w.n_groups * int(np.sum(kph)))
+
+
+def cpu_baseline(inp, target_s: float):
+    """The float64 oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    from tests.parity import f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    w = inp.workload
+    h = 0
+    q, k, v = f64(inp.q[0, h]), f64(inp.k[0, h]), f64(inp.v[0, h])
+    do = f64(inp.do[0, h]) if inp.do is not None else None
+    wt = inp.w[h].astype(np.float64)
+    t0 = time.perf_counter()
+    _, _, s = oracle.predict_head(q, k, wt, wt, w.group)
+    kk = int(inp.k_per_head[h])
+    idx = np.stack([oracle.select_row(s[g], kk) for g in range(w.n_groups)])
+    t_sel = time.perf_counter() - t0
+    per_group_sel = t_sel / w.n_groups
+    G = w.group
+    done, t_att = 0, 0.0
+    while done < w.n_groups and (t_att + done * per_group_sel) < target_s:
+        rows = slice(done * G, (done + 1) * G)
+        keys = oracle.kept_keys(idx[done])
+        t1 = time.perf_counter()
+        if do is not None:
+            oracle.group_backward(q[rows], k, v, do[rows], keys)
+        else:
+            oracle.group_forward(q[rows], k, v, keys)
+        t_att += time.perf_counter() - t1
+        done += 1
+    elapsed = t_att + done * per_group_sel
+    f_fwd = 4.0 * G * 64 * w.head_dim * kk * done
+    flops = f_fwd * (3.5 if do is not None else 1.0)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"head 0: predict+select of all {w.n_groups} groups (time pro-rated) and "
+                       f"{'fwd+bwd' if do is not None else 'fwd'} of {done} of {w.n_groups} groups, "
+                       f"float64 numpy; {elapsed:.1f} s"),
+            "tokens_per_s": done * G / elapsed}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import dynamic_sparse_attention_qk_amd as dsa
+    from tests.parity import problem_of, to_device
+
+    w = synth.workload(args.workload)
+    t0 = time.time()
+    inp = synth.generate(w)
+    print(f"# generated {w.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    p = problem_of(w)
+    kph = [int(x) for x in inp.k_per_head]
+    backward = w.backward
+    plan = dsa.SparseAttentionPlan(p, kph, materialise_scores=not w.streamed, backward=backward)
+    plan.idx.zero_()
+    plan.rev_idx.zero_()
+    Q, K, V = (to_device(getattr(inp, n)) for n in ("q", "k", "v"))
+    Wt = to_device(inp.w)
+    dO = to_device(inp.do) if backward else None
+
+    def step():
+        plan.step(Q, K, V, Wt, Wt, dO)
+
+    # first pass checked on the host: every kept-block id in range before the attention kernels read them
+    plan.predict(Q, K, Wt, Wt)
+    plan.select()
+    torch.cuda.synchronize()
+    idx_host = plan.idx[: int(plan.row_base[-1])].cpu().numpy()
+    assert idx_host.min() >= 0 and idx_host.max() < p.n_blocks, "kept-block list out of range"
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+
+    # per-stage times (separate pass; the backward as its three single-launch stages)
+    names = ["predict", "select", "fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if backward else [])
+    ev = {n: [] for n in names}
+    for _ in range(max(3, args.steps // 2)):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        marks[0].record()
+        plan.predict(Q, K, Wt, Wt)
+        marks[1].record()
+        plan.select()
+        marks[2].record()
+        plan.forward(Q, K, V)
+        marks[3].record()
+        if backward:
+            dvec = plan.ws_bwd.view(torch.float32)[: p.batch * p.heads * p.seq_len]
+            dsa.sparse_attn_bwd_preprocess(p, plan.O, dO, dvec)
+            marks[4].record()
+            dsa.sparse_attn_bwd_dkdv(p, Q, K, V, dO, plan.LSE, dvec, kph, plan.rev_ptr, plan.rev_idx, plan.dK,
+                                     plan.dV)
+            marks[5].record()
+            dsa.sparse_attn_bwd_dq(p, Q, K, V, dO, plan.LSE, dvec, plan.idx, kph, plan.dQ)
+            marks[6].record()
+        torch.cuda.synchronize()
+        for i, n in enumerate(names):
+            ev[n].append(marks[i].elapsed_time(marks[i + 1]))
+    stage_ms = {n: float(np.median(v)) for n, v in ev.items()}
+
+    pairs = kept_pairs(w, kph)
+    unit = 64 * w.group * w.head_dim            # G x Bk x d per kept (group, block) pair
+    f_fwd = 4.0 * unit * pairs
+    f_bwd = 2.5 * f_fwd if backward else 0.0
+    step_s = ms_step / 1e3
+    tflops = (f_fwd + f_bwd) / step_s / 1e12
+    attn_ms = stage_ms["fwd"] + sum(stage_ms.get(n, 0.0) for n in ("bwd_pre", "bwd_dkdv", "bwd_dq"))
+    kernel_flops = {"fwd": 4.0 * unit * pairs, "bwd_dkdv": 8.0 * unit * pairs, "bwd_dq": 6.0 * unit * pairs}
+    cand = [n for n in ("fwd", "bwd_dkdv", "bwd_dq") if n in stage_ms]
+    dom = max(cand, key=lambda n: stage_ms[n])
+    dom_tflops = kernel_flops[dom] / (stage_ms[dom] / 1e3) / 1e12
+    peak = PEAK_BF16 if w.dtype == "bf16" else PEAK_F32_MFMA
+    elt = 2 if w.dtype == "bf16" else 4
+    pred_bytes = 2 * w.batch * w.heads * w.seq_len * w.head_dim * elt + \
+        (w.batch * w.heads * w.n_groups * w.n_blocks * 4 if not w.streamed else 0)
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Voronoi-clustered video latents, Morton token order)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq_len": w.seq_len,
+                   "head_dim": w.head_dim, "rank": w.rank, "group": w.group, "block": 64,
+                   "k_per_head": kph if len(set(kph)) > 1 else kph[0], "backward": backward,
+                   "scores": "streamed" if w.streamed else "materialised"},
+        "tokens_per_s": round(w.batch * w.seq_len / step_s, 1),
+        "attn_fwd_bwd_tflops": round((f_fwd + f_bwd) / (attn_ms / 1e3) / 1e12, 3),
+        "counted_tflop_per_step": round((f_fwd + f_bwd) / 1e12, 4),
+        "stage_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+        "predict_hbm_gbs": round(pred_bytes / (stage_ms["predict"] / 1e3) / 1e9, 1),
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(dom_tflops, 2), "peak": peak / 1e12,
+                     "unit": "TFLOP/s", "frac": round(dom_tflops * 1e12 / peak, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(inp, args.cpu_seconds)
+        rec["cpu_baseline"] = cb
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,263 @@
+"""MI355X (gfx950) dynamic sparse attention: Python binding of libdsa.so.
+
+The four calls of the C ABI (include/dsa.h) are exposed under the same names
+and take torch tensors only as holders of device memory: each wrapper checks
+that the tensors are laid out as the ABI expects, passes their pointers and the
+current HIP stream, and raises on a non-zero status.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.
+
+    predict_block_scores  low-rank predictor -> qhat, khat (and scores)
+    select_topk_blocks    top-k kept blocks per (head, group) + reverse index
+    sparse_attn_fwd       attention over the kept blocks -> O, LSE
+    sparse_attn_bwd       dQ, dK, dV for the fixed selection
+
+``SparseAttentionPlan`` allocates the outputs and workspaces of one problem
+with torch and runs the calls in order.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdsa.so")
+
+DSA_F32, DSA_BF16 = 0, 1
+DSA_WS_SELECT, DSA_WS_BWD = 0, 1
+
+
+class DsaError(RuntimeError):
+    def __init__(self, call: str, status: int, text: str):
+        super().__init__(f"{call} failed: status {status} ({text})")
+        self.status = status
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "heads", "seq_len", "head_dim", "rank", "group", "block", "dtype")]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libdsa.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m dynamic_sparse_attention_qk_amd.build` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32p, i64p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p
+        pp = ctypes.POINTER(_Problem)
+        kph = ctypes.POINTER(ctypes.c_int32)
+        lib.dsa_version.restype = ctypes.c_char_p
+        lib.dsa_status_string.restype = ctypes.c_char_p
+        lib.dsa_status_string.argtypes = [ctypes.c_int]
+        lib.dsa_index_layout.argtypes = [pp, kph, i64p]
+        lib.dsa_workspace_bytes.restype = ctypes.c_size_t
+        lib.dsa_workspace_bytes.argtypes = [pp, kph, ctypes.c_int]
+        lib.dsa_predict_block_scores.argtypes = [pp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp]
+        lib.dsa_select_topk_blocks.argtypes = [pp, f32p, f32p, f32p, kph, i32p, i32p, i32p, f32p, vp,
+                                               ctypes.c_size_t, vp]
+        lib.dsa_sparse_attn_fwd.argtypes = [pp, vp, vp, vp, i32p, kph, f32p, f32p, vp]
+        lib.dsa_sparse_attn_bwd.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, kph, i32p, i32p, f32p, f32p,
+                                            f32p, vp, ctypes.c_size_t, vp]
+        lib.dsa_sparse_attn_bwd_preprocess.argtypes = [pp, f32p, vp, f32p, vp]
+        lib.dsa_sparse_attn_bwd_dkdv.argtypes = [pp, vp, vp, vp, vp, f32p, f32p, kph, i32p, i32p, f32p, f32p, vp]
+        lib.dsa_sparse_attn_bwd_dq.argtypes = [pp, vp, vp, vp, vp, f32p, f32p, i32p, kph, f32p, vp]
+        for name in ("dsa_index_layout", "dsa_predict_block_scores", "dsa_select_topk_blocks",
+                     "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_preprocess",
+                     "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq"):
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+EXPORTED = ("dsa_version", "dsa_status_string", "dsa_index_layout", "dsa_workspace_bytes",
+            "dsa_predict_block_scores", "dsa_select_topk_blocks", "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd",
+            "dsa_sparse_attn_bwd_preprocess", "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq")
+
+
+@dataclass(frozen=True)
+class Problem:
+    batch: int
+    heads: int
+    seq_len: int
+    head_dim: int
+    rank: int
+    group: int
+    block: int = 64
+    dtype: int = DSA_BF16
+
+    def c(self) -> _Problem:
+        return _Problem(self.batch, self.heads, self.seq_len, self.head_dim, self.rank, self.group, self.block,
+                        self.dtype)
+
+    @property
+    def n_groups(self) -> int:
+        return self.seq_len // self.group
+
+    @property
+    def n_blocks(self) -> int:
+        return self.seq_len // self.block
+
+
+def _kph(k_per_head: Sequence[int]):
+    arr = (ctypes.c_int32 * len(k_per_head))(*[int(x) for x in k_per_head])
+    return arr
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libdsa must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(call: str, status: int):
+    if status != 0:
+        raise DsaError(call, status, library().dsa_status_string(status).decode())
+
+
+def status_string(status: int) -> str:
+    return library().dsa_status_string(status).decode()
+
+
+def version() -> str:
+    return library().dsa_version().decode()
+
+
+def index_layout(p: Problem, k_per_head: Sequence[int]) -> np.ndarray:
+    """Host int64 [B*H + 1] offsets of each (b, h) region of the kept-block list."""
+    out = np.zeros(p.batch * p.heads + 1, dtype=np.int64)
+    _check("dsa_index_layout", library().dsa_index_layout(
+        ctypes.byref(p.c()), _kph(k_per_head), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+    return out
+
+
+def workspace_bytes(p: Problem, k_per_head: Sequence[int], which: int) -> int:
+    return int(library().dsa_workspace_bytes(ctypes.byref(p.c()), _kph(k_per_head), which))
+
+
+def predict_block_scores(p: Problem, Q, K, Wq, Wk, qhat, khat, scores=None, stream=None) -> None:
+    _check("dsa_predict_block_scores", library().dsa_predict_block_scores(
+        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(qhat), _ptr(khat), _ptr(scores),
+        _stream(stream)))
+
+
+def select_topk_blocks(p: Problem, scores, qhat, khat, k_per_head, idx, rev_ptr, rev_idx, workspace,
+                       scores_dump=None, stream=None) -> None:
+    _check("dsa_select_topk_blocks", library().dsa_select_topk_blocks(
+        ctypes.byref(p.c()), _ptr(scores), _ptr(qhat), _ptr(khat), _kph(k_per_head), _ptr(idx), _ptr(rev_ptr),
+        _ptr(rev_idx), _ptr(scores_dump), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def sparse_attn_fwd(p: Problem, Q, K, V, idx, k_per_head, O, LSE, stream=None) -> None:
+    _check("dsa_sparse_attn_fwd", library().dsa_sparse_attn_fwd(
+        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _kph(k_per_head), _ptr(O), _ptr(LSE),
+        _stream(stream)))
+
+
+def sparse_attn_bwd(p: Problem, Q, K, V, O, dO, LSE, idx, k_per_head, rev_ptr, rev_idx, dQ, dK, dV, workspace,
+                    stream=None) -> None:
+    _check("dsa_sparse_attn_bwd", library().dsa_sparse_attn_bwd(
+        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(idx), _kph(k_per_head),
+        _ptr(rev_ptr), _ptr(rev_idx), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def sparse_attn_bwd_preprocess(p: Problem, O, dO, Dvec, stream=None) -> None:
+    _check("dsa_sparse_attn_bwd_preprocess", library().dsa_sparse_attn_bwd_preprocess(
+        ctypes.byref(p.c()), _ptr(O), _ptr(dO), _ptr(Dvec), _stream(stream)))
+
+
+def sparse_attn_bwd_dkdv(p: Problem, Q, K, V, dO, LSE, Dvec, k_per_head, rev_ptr, rev_idx, dK, dV,
+                         stream=None) -> None:
+    _check("dsa_sparse_attn_bwd_dkdv", library().dsa_sparse_attn_bwd_dkdv(
+        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), _ptr(Dvec), _kph(k_per_head),
+        _ptr(rev_ptr), _ptr(rev_idx), _ptr(dK), _ptr(dV), _stream(stream)))
+
+
+def sparse_attn_bwd_dq(p: Problem, Q, K, V, dO, LSE, Dvec, idx, k_per_head, dQ, stream=None) -> None:
+    _check("dsa_sparse_attn_bwd_dq", library().dsa_sparse_attn_bwd_dq(
+        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), _ptr(Dvec), _ptr(idx),
+        _kph(k_per_head), _ptr(dQ), _stream(stream)))
+
+
+class SparseAttentionPlan:
+    """Outputs and workspaces of one problem, allocated once with torch, plus the calls in order."""
+
+    def __init__(self, p: Problem, k_per_head: Sequence[int], device="cuda", materialise_scores: bool = True,
+                 backward: bool = True):
+        self.p = p
+        self.k_per_head = [int(x) for x in k_per_head]
+        self.row_base = index_layout(p, self.k_per_head)
+        total = int(self.row_base[-1])
+        B, H, N, D, R = p.batch, p.heads, p.seq_len, p.head_dim, p.rank
+        f32 = dict(dtype=torch.float32, device=device)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.qhat = torch.empty(B, H, p.n_groups, R, **f32)
+        self.khat = torch.empty(B, H, p.n_blocks, R, **f32)
+        self.scores = torch.empty(B, H, p.n_groups, p.n_blocks, **f32) if materialise_scores else None
+        self.idx = torch.empty(max(total, 1), **i32)
+        self.rev_ptr = torch.empty(B * H, p.n_blocks + 1, **i32)
+        self.rev_idx = torch.empty(max(total, 1), **i32)
+        self.ws_select = torch.empty(workspace_bytes(p, self.k_per_head, DSA_WS_SELECT), dtype=torch.uint8,
+                                     device=device)
+        self.O = torch.empty(B, H, N, D, **f32)
+        self.LSE = torch.empty(B, H, N, **f32)
+        if backward:
+            self.dQ = torch.empty(B, H, N, D, **f32)
+            self.dK = torch.empty(B, H, N, D, **f32)
+            self.dV = torch.empty(B, H, N, D, **f32)
+            self.ws_bwd = torch.empty(workspace_bytes(p, self.k_per_head, DSA_WS_BWD), dtype=torch.uint8,
+                                      device=device)
+
+    def predict(self, Q, K, Wq, Wk, stream=None):
+        predict_block_scores(self.p, Q, K, Wq, Wk, self.qhat, self.khat, self.scores, stream)
+
+    def select(self, stream=None, scores_dump=None):
+        select_topk_blocks(self.p, self.scores, self.qhat, self.khat, self.k_per_head, self.idx, self.rev_ptr,
+                           self.rev_idx, self.ws_select, scores_dump=scores_dump, stream=stream)
+
+    def forward(self, Q, K, V, stream=None):
+        sparse_attn_fwd(self.p, Q, K, V, self.idx, self.k_per_head, self.O, self.LSE, stream)
+
+    def backward(self, Q, K, V, dO, stream=None):
+        sparse_attn_bwd(self.p, Q, K, V, self.O, dO, self.LSE, self.idx, self.k_per_head, self.rev_ptr,
+                        self.rev_idx, self.dQ, self.dK, self.dV, self.ws_bwd, stream)
+
+    def backward_stages(self, Q, K, V, dO, stream=None):
+        """The backward as its three single-launch stages (same result as backward())."""
+        dvec = self.ws_bwd.view(torch.float32)[: self.p.batch * self.p.heads * self.p.seq_len]
+        sparse_attn_bwd_preprocess(self.p, self.O, dO, dvec, stream)
+        sparse_attn_bwd_dkdv(self.p, Q, K, V, dO, self.LSE, dvec, self.k_per_head, self.rev_ptr, self.rev_idx,
+                             self.dK, self.dV, stream)
+        sparse_attn_bwd_dq(self.p, Q, K, V, dO, self.LSE, dvec, self.idx, self.k_per_head, self.dQ, stream)
+
+    def step(self, Q, K, V, Wq, Wk, dO=None, stream=None):
+        """predict -> select -> fwd (-> bwd): one pass of the whole hot path."""
+        self.predict(Q, K, Wq, Wk, stream)
+        self.select(stream)
+        self.forward(Q, K, V, stream)
+        if dO is not None:
+            self.backward(Q, K, V, dO, stream)
+
+    def idx_rows(self, b: int, h: int) -> torch.Tensor:
+        """View of the kept-block list of (b, h) as [NG, k_h]."""
+        s = int(self.row_base[b * self.p.heads + h])
+        return self.idx[s:s + self.p.n_groups * self.k_per_head[h]].view(self.p.n_groups, self.k_per_head[h])

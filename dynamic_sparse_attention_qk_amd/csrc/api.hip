@@ -1,0 +1,240 @@
+// C ABI of libdsa.so: argument validation on the host, then asynchronous
+// launches on the caller's stream.  Nothing here allocates device memory.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/dsa.h"
+#include "launch.hpp"
+
+using dsa::HeadTable;
+using dsa::Shape;
+
+namespace {
+
+constexpr int kMaxBlocks = 8192;
+
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+int check_problem(const dsa_problem* p, Shape* s) {
+  if (!p) return DSA_ERR_INVALID_ARG;
+  if (p->dtype != DSA_F32 && p->dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (p->batch < 1 || p->heads < 1 || p->seq_len < 1) return DSA_ERR_SHAPE;
+  if (p->heads > dsa::kMaxHeads) return DSA_ERR_UNSUPPORTED;
+  if (p->block != dsa::kBlock) return DSA_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return DSA_ERR_UNSUPPORTED;
+  if (p->rank != 8 && p->rank != 16 && p->rank != 32 && p->rank != 64) return DSA_ERR_UNSUPPORTED;
+  if (p->group != 64 && p->group != 128) return DSA_ERR_UNSUPPORTED;
+  if (p->seq_len % p->block != 0 || p->seq_len % p->group != 0) return DSA_ERR_SHAPE;
+  if (p->seq_len / p->block > kMaxBlocks) return DSA_ERR_UNSUPPORTED;
+  s->B = p->batch;
+  s->H = p->heads;
+  s->N = p->seq_len;
+  s->D = p->head_dim;
+  s->R = p->rank;
+  s->G = p->group;
+  s->NG = p->seq_len / p->group;
+  s->NB = p->seq_len / p->block;
+  s->bf16 = p->dtype == DSA_BF16;
+  return DSA_OK;
+}
+
+// Fills the per-head table; returns the largest k_h through kmax.
+int check_heads(const Shape& s, const int32_t* kph, HeadTable* ht, int* kmax) {
+  if (!kph) return DSA_ERR_INVALID_ARG;
+  memset(ht, 0, sizeof(*ht));
+  int64_t sum = 0;
+  int mx = 0;
+  for (int h = 0; h < s.H; ++h) {
+    if (kph[h] < 1 || kph[h] > s.NB) return DSA_ERR_SHAPE;
+    ht->k[h] = kph[h];
+    ht->kofs[h] = (int32_t)sum;
+    sum += kph[h];
+    if (kph[h] > mx) mx = kph[h];
+  }
+  ht->kofs[s.H] = (int32_t)sum;
+  ht->ksum = (int32_t)sum;
+  if ((int64_t)s.B * s.NG * sum >= ((int64_t)1 << 31)) return DSA_ERR_UNSUPPORTED;
+  if (kmax) *kmax = mx;
+  return DSA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t select_ws(const Shape& s, const HeadTable& ht) {
+  return align256((size_t)s.B * s.H * s.NB * sizeof(int32_t)) + align256((size_t)s.B * s.NG * ht.ksum * sizeof(int32_t));
+}
+
+size_t bwd_ws(const Shape& s) { return align256((size_t)s.B * s.H * s.N * sizeof(float)); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_version(void) { return "dsa-mi355x 0.1.0 (gfx950)"; }
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_INVALID_ARG: return "invalid argument (null pointer or bad enum)";
+    case DSA_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case DSA_ERR_DTYPE: return "unsupported dtype for this call";
+    case DSA_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case DSA_ERR_UNSUPPORTED: return "problem outside the supported limits";
+    case DSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DSA_ERR_HIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+int dsa_index_layout(const dsa_problem* p, const int32_t* k_per_head, int64_t* row_base) {
+  Shape s;
+  HeadTable ht;
+  int st = check_problem(p, &s);
+  if (st) return st;
+  if ((st = check_heads(s, k_per_head, &ht, nullptr))) return st;
+  if (!row_base) return DSA_ERR_INVALID_ARG;
+  for (int b = 0; b < s.B; ++b)
+    for (int h = 0; h < s.H; ++h) row_base[b * s.H + h] = (int64_t)b * s.NG * ht.ksum + (int64_t)s.NG * ht.kofs[h];
+  row_base[s.B * s.H] = (int64_t)s.B * s.NG * ht.ksum;
+  return DSA_OK;
+}
+
+size_t dsa_workspace_bytes(const dsa_problem* p, const int32_t* k_per_head, int which_call) {
+  Shape s;
+  HeadTable ht;
+  if (check_problem(p, &s) || check_heads(s, k_per_head, &ht, nullptr)) return 0;
+  if (which_call == DSA_WS_SELECT) return select_ws(s, ht);
+  if (which_call == DSA_WS_BWD) return bwd_ws(s);
+  return 0;
+}
+
+int dsa_predict_block_scores(const dsa_problem* p, const void* Q, const void* K, const float* Wq, const float* Wk,
+                             float* qhat, float* khat, float* scores, void* stream) {
+  Shape s;
+  int st = check_problem(p, &s);
+  if (st) return st;
+  if (!Q || !K || !Wq || !Wk || !qhat || !khat) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(qhat) || !aligned16(khat) ||
+      (scores && !aligned16(scores)))
+    return DSA_ERR_ALIGN;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const float tau = 1.0f / sqrtf((float)s.D);
+  hipError_t e = dsa::launch_pool_project(s, Q, Wq, qhat, s.G, hs);
+  if (e == hipSuccess) e = dsa::launch_pool_project(s, K, Wk, khat, dsa::kBlock, hs);
+  if (e == hipSuccess && scores) e = dsa::launch_block_scores(s, qhat, khat, scores, tau, hs);
+  return hip_status(e);
+}
+
+int dsa_select_topk_blocks(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,
+                           const int32_t* k_per_head, int32_t* idx, int32_t* rev_ptr, int32_t* rev_idx,
+                           float* scores_dump, void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  HeadTable ht;
+  int kmax = 0;
+  int st = check_problem(p, &s);
+  if (st) return st;
+  if ((st = check_heads(s, k_per_head, &ht, &kmax))) return st;
+  if (!idx || !rev_ptr || !rev_idx) return DSA_ERR_INVALID_ARG;
+  if (!scores && (!qhat || !khat)) return DSA_ERR_INVALID_ARG;
+  if ((scores && !aligned16(scores)) || (!scores && (!aligned16(qhat) || !aligned16(khat))) || !aligned16(idx) ||
+      !aligned16(rev_ptr) || !aligned16(rev_idx) || (scores_dump && !aligned16(scores_dump)))
+    return DSA_ERR_ALIGN;
+  const size_t need = select_ws(s, ht);
+  if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DSA_ERR_ALIGN;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const float tau = 1.0f / sqrtf((float)s.D);
+  int32_t* counters = static_cast<int32_t*>(workspace);
+  int32_t* scratch = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                                align256((size_t)s.B * s.H * s.NB * sizeof(int32_t)));
+  hipError_t e = dsa::launch_topk_select(s, scores, qhat, khat, idx, scores ? nullptr : scores_dump, ht, tau, kmax, hs);
+  if (e == hipSuccess) e = dsa::launch_reverse_index(s, idx, rev_ptr, rev_idx, counters, scratch, ht, kmax, hs);
+  return hip_status(e);
+}
+
+int dsa_sparse_attn_fwd(const dsa_problem* p, const void* Q, const void* K, const void* V, const int32_t* idx,
+                        const int32_t* k_per_head, float* O, float* LSE, void* stream) {
+  Shape s;
+  HeadTable ht;
+  int st = check_problem(p, &s);
+  if (st) return st;
+  if ((st = check_heads(s, k_per_head, &ht, nullptr))) return st;
+  if (!Q || !K || !V || !idx || !O || !LSE) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(idx) || !aligned16(O) || !aligned16(LSE))
+    return DSA_ERR_ALIGN;
+  return hip_status(dsa::launch_attn_fwd(s, Q, K, V, idx, O, LSE, ht, static_cast<hipStream_t>(stream)));
+}
+
+static int check_bwd_common(const dsa_problem* p, const int32_t* k_per_head, Shape* s, HeadTable* ht) {
+  int st = check_problem(p, s);
+  if (st) return st;
+  if (!s->bf16) return DSA_ERR_DTYPE;
+  return check_heads(*s, k_per_head, ht, nullptr);
+}
+
+int dsa_sparse_attn_bwd_preprocess(const dsa_problem* p, const float* O, const void* dO, float* Dvec, void* stream) {
+  Shape s;
+  int st = check_problem(p, &s);
+  if (st) return st;
+  if (!s.bf16) return DSA_ERR_DTYPE;
+  if (!O || !dO || !Dvec) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(O) || !aligned16(dO) || !aligned16(Dvec)) return DSA_ERR_ALIGN;
+  return hip_status(dsa::launch_bwd_pre(s, O, dO, Dvec, static_cast<hipStream_t>(stream)));
+}
+
+int dsa_sparse_attn_bwd_dkdv(const dsa_problem* p, const void* Q, const void* K, const void* V, const void* dO,
+                             const float* LSE, const float* Dvec, const int32_t* k_per_head, const int32_t* rev_ptr,
+                             const int32_t* rev_idx, float* dK, float* dV, void* stream) {
+  Shape s;
+  HeadTable ht;
+  int st = check_bwd_common(p, k_per_head, &s, &ht);
+  if (st) return st;
+  if (!Q || !K || !V || !dO || !LSE || !Dvec || !rev_ptr || !rev_idx || !dK || !dV) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(LSE) || !aligned16(Dvec) ||
+      !aligned16(rev_ptr) || !aligned16(rev_idx) || !aligned16(dK) || !aligned16(dV))
+    return DSA_ERR_ALIGN;
+  return hip_status(dsa::launch_bwd_dkdv(s, Q, K, V, dO, LSE, Dvec, rev_ptr, rev_idx, dK, dV, ht,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int dsa_sparse_attn_bwd_dq(const dsa_problem* p, const void* Q, const void* K, const void* V, const void* dO,
+                           const float* LSE, const float* Dvec, const int32_t* idx, const int32_t* k_per_head,
+                           float* dQ, void* stream) {
+  Shape s;
+  HeadTable ht;
+  int st = check_bwd_common(p, k_per_head, &s, &ht);
+  if (st) return st;
+  if (!Q || !K || !V || !dO || !LSE || !Dvec || !idx || !dQ) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(LSE) || !aligned16(Dvec) ||
+      !aligned16(idx) || !aligned16(dQ))
+    return DSA_ERR_ALIGN;
+  return hip_status(dsa::launch_bwd_dq(s, Q, K, V, dO, LSE, Dvec, idx, dQ, ht, static_cast<hipStream_t>(stream)));
+}
+
+int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
+                        const void* dO, const float* LSE, const int32_t* idx, const int32_t* k_per_head,
+                        const int32_t* rev_ptr, const int32_t* rev_idx, float* dQ, float* dK, float* dV,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  HeadTable ht;
+  int st = check_bwd_common(p, k_per_head, &s, &ht);
+  if (st) return st;
+  if (!Q || !K || !V || !O || !dO || !LSE || !idx || !rev_ptr || !rev_idx || !dQ || !dK || !dV)
+    return DSA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(LSE) ||
+      !aligned16(idx) || !aligned16(rev_ptr) || !aligned16(rev_idx) || !aligned16(dQ) || !aligned16(dK) ||
+      !aligned16(dV))
+    return DSA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < bwd_ws(s)) return DSA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DSA_ERR_ALIGN;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  float* Dvec = static_cast<float*>(workspace);
+  hipError_t e = dsa::launch_bwd_pre(s, O, dO, Dvec, hs);
+  if (e == hipSuccess) e = dsa::launch_bwd_dkdv(s, Q, K, V, dO, LSE, Dvec, rev_ptr, rev_idx, dK, dV, ht, hs);
+  if (e == hipSuccess) e = dsa::launch_bwd_dq(s, Q, K, V, dO, LSE, Dvec, idx, dQ, ht, hs);
+  return hip_status(e);
+}
+
+}  // extern "C"

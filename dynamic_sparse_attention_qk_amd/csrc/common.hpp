@@ -1,0 +1,178 @@
+// Shared device-side definitions of the gfx950 sparse-attention kernels.
+//
+// MFMA operand/result layouts used throughout (wave64, checked on gfx950):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     lane l supplies A[l%32][8*(l/32) + e] and B[8*(l/32) + e][l%32], e = 0..7;
+//     lane l receives D[8*(e/4) + 4*(l/32) + e%4][l%32], e = 0..15.
+//   v_mfma_f32_32x32x2_f32    same output layout; lane l supplies A[l%32][l/32]
+//     and B[l/32][l%32].
+// The k index inside one MFMA may be permuted freely as long as A and B use
+// the same permutation; the kernels exploit that to feed softmax results
+// straight from accumulators into the next product.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t bf16_t;  // bf16 storage (bit pattern)
+
+constexpr int kBlock = 64;      // KV block size (tokens)
+constexpr int kMaxHeads = 128;  // capacity of the per-head table passed by value
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Per-head kept-block counts, passed by value in the kernel arguments.
+// Row (b, h, g) of a kept-block list starts at
+//   b * NG * ksum + NG * kofs[h] + g * k[h].
+struct HeadTable {
+  int32_t k[kMaxHeads];
+  int32_t kofs[kMaxHeads + 1];
+  int32_t ksum;
+};
+
+__device__ __forceinline__ int64_t row_base(const HeadTable& ht, int b, int h, int ng) {
+  return (int64_t)b * ng * ht.ksum + (int64_t)ng * ht.kofs[h];
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Number of set bits of m held by lanes below this one.
+__device__ __forceinline__ int mask_rank(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(((uint32_t)v) << 16);
+}
+
+// Order-preserving map of an fp32 score to uint32 (larger score -> larger
+// key); -0.0 is folded onto +0.0 first so that IEEE-equal scores tie.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t b = __float_as_uint(s);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// The block score: tau * (qhat . khat) as a fixed fma chain over r, shared by
+// the materialising and the streaming kernels so their scores are bit-equal.
+template <int R>
+__device__ __forceinline__ float score_dot(const float* __restrict__ qh, const float* __restrict__ kh, float tau) {
+  float acc = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc = __builtin_fmaf(qh[r], kh[r], acc);
+  return acc * tau;
+}
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp16 operands: used where one operand is a softmax probability or its
+// gradient (rounded from fp32) so that rounding stays 8x below bf16's.
+__device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32_f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Pack accumulator elements [8c, 8c+8) of a 32x32 tile to bf16: for lane l
+// they hold the 16-key chunk c of the tile at keys 16c + 8*(e/4) + 4*(l/32) + e%4.
+__device__ __forceinline__ bf16x8 pack_bf16(const f32x16& x, int c) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[8 * c + e];
+  return r;
+}
+
+__device__ __forceinline__ f16x8 pack_f16(const f32x16& x, int c) {
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (_Float16)x[8 * c + e];
+  return r;
+}
+
+// hi + lo fp16 split of accumulator elements [8c, 8c+8): hi = fp16(x),
+// lo = fp16(x - hi); hi + lo carries ~22 significant bits of x.
+__device__ __forceinline__ void pack_f16_split(const f32x16& x, int c, f16x8& hi, f16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const _Float16 h = (_Float16)x[8 * c + e];
+    hi[e] = h;
+    lo[e] = (_Float16)(x[8 * c + e] - (float)h);
+  }
+}
+
+// Exact conversion of 8 bf16 values (one 16-byte register) to fp16: every
+// bf16 value of magnitude in [2^-14, 65504] is representable in fp16.
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& v) {
+  uint4 r;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&v);
+  uint32_t* o = reinterpret_cast<uint32_t*>(&r);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float lo = __uint_as_float(w[q] << 16), hi = __uint_as_float(w[q] & 0xFFFF0000u);
+    o[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  return r;
+}
+
+// Two 8-byte LDS reads forming the A operand that matches pack_bf16's key
+// order: row pointer `p` already points at (row, 16c + 4*(l/32)).
+__device__ __forceinline__ bf16x8 lds_pair_b64(const bf16_t* p) {
+  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
+  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 8);
+  bf16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+__device__ __forceinline__ f16x8 lds_pair_b64_h(const uint16_t* p) {
+  f16x4 lo = *reinterpret_cast<const f16x4*>(p);
+  f16x4 hi = *reinterpret_cast<const f16x4*>(p + 8);
+  f16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
+
+// 16-byte global load / store helpers.
+__device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Transposed store of an 8x8 bf16 sub-tile held as 8 rows x 16 bytes:
+// writes column c (8 values from rows 0..7) as 16 contiguous bytes at dst[c*ld].
+__device__ __forceinline__ void store_transposed_8x8(const uint4 (&rows)[8], bf16_t* dst, int ld) {
+  const uint32_t* w[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) w[r] = reinterpret_cast<const uint32_t*>(&rows[r]);
+#pragma unroll
+  for (int c2 = 0; c2 < 4; ++c2) {
+    uint4 even, odd;  // columns 2*c2 and 2*c2+1
+    uint32_t* pe = reinterpret_cast<uint32_t*>(&even);
+    uint32_t* po = reinterpret_cast<uint32_t*>(&odd);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t a = w[2 * p][c2], b = w[2 * p + 1][c2];
+      pe[p] = (a & 0xFFFFu) | (b << 16);
+      po[p] = (a >> 16) | (b & 0xFFFF0000u);
+    }
+    *reinterpret_cast<uint4*>(dst + (2 * c2) * ld) = even;
+    *reinterpret_cast<uint4*>(dst + (2 * c2 + 1) * ld) = odd;
+  }
+}
+
+__device__ __forceinline__ float wave_max_pair(float v) {  // max with lane l^32
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+
+}  // namespace dsa

@@ -1,0 +1,37 @@
+// Host-side launchers of the gfx950 kernels (called by the C ABI in api.hip
+// after argument validation).  Each returns a hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace dsa {
+
+struct Shape {
+  int B, H, N, D, R, G, NG, NB;
+  bool bf16;
+};
+
+hipError_t launch_pool_project(const Shape& s, const void* X, const float* W, float* out, int pool,
+                               hipStream_t st);
+hipError_t launch_block_scores(const Shape& s, const float* qhat, const float* khat, float* scores,
+                               float tau, hipStream_t st);
+hipError_t launch_topk_select(const Shape& s, const float* scores, const float* qhat, const float* khat,
+                              int32_t* idx, float* dump, const HeadTable& ht, float tau, int kmax,
+                              hipStream_t st);
+hipError_t launch_reverse_index(const Shape& s, const int32_t* idx, int32_t* rev_ptr, int32_t* rev_idx,
+                                int32_t* counters, int32_t* scratch, const HeadTable& ht, int kmax,
+                                hipStream_t st);
+hipError_t launch_attn_fwd(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx,
+                           float* O, float* LSE, const HeadTable& ht, hipStream_t st);
+hipError_t launch_bwd_pre(const Shape& s, const float* O, const void* dO, float* Dvec, hipStream_t st);
+hipError_t launch_bwd_dkdv(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
+                           const float* LSE, const float* Dvec, const int32_t* rev_ptr, const int32_t* rev_idx,
+                           float* dK, float* dV, const HeadTable& ht, hipStream_t st);
+hipError_t launch_bwd_dq(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
+                         const float* LSE, const float* Dvec, const int32_t* idx, float* dQ, const HeadTable& ht,
+                         hipStream_t st);
+
+}  // namespace dsa

@@ -1,0 +1,170 @@
+/*
+ * dsa.h -- C ABI of the MI355X (gfx950) dynamic sparse attention library, libdsa.so.
+ *
+ * The method is DSV's ("DSV: Exploiting Dynamic Sparsity to Accelerate
+ * Large-Scale Video DiT Training"; explainer pages at gist.science, Dutch and
+ * Hindi editions, cited below as nl/hi with their technical-summary section):
+ * a low-rank predictor estimates query-group x key-block attention scores, the
+ * top-k "critical" KV blocks are kept per (head, query group), and exact
+ * attention runs forward and backward over the kept blocks only.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are dense, row-major, [B, H, N, d] ("BHND", d innermost) unless
+ *    stated.  Query groups are G consecutive tokens (G in {64, 128}); KV blocks
+ *    are 64 consecutive tokens.  NG = N / G groups, NB = N / 64 blocks.
+ *  - Q, K, V, dO are bf16 (DSA_BF16, stored as 16-bit patterns) or fp32
+ *    (DSA_F32), as problem->dtype says.  Predictor weights and every output
+ *    (scores, qhat, khat, O, LSE, dQ, dK, dV) are fp32.  tau = 1/sqrt(d).
+ *  - Kept-block lists ("idx") are ragged by head: head h keeps k_h blocks per
+ *    group, 1 <= k_h <= NB.  Row (b, h, g) holds k_h int32 block ids in
+ *    ascending order, starting at element row_base[b*H + h] + g * k_h, where
+ *    row_base is given by dsa_index_layout.  rev_idx has the same total length.
+ *  - All pointers except k_per_head are DEVICE pointers owned by the caller;
+ *    the library never allocates, frees or retains memory.  k_per_head is a
+ *    HOST array of H int32, read during the call only.  Device buffers must be
+ *    16-byte aligned.  Scratch memory comes from a caller-provided workspace
+ *    whose size dsa_workspace_bytes returns.
+ *  - Every compute call is asynchronous on the given HIP stream (a
+ *    hipStream_t passed as void*, NULL = the null stream) and does not
+ *    synchronise.  Arguments are validated on the host before anything is
+ *    launched; on error nothing is launched and a negative status is returned.
+ *  - Calls on one stream may be issued from any thread; the library holds no
+ *    mutable global state.
+ *  - Limits: d in {64, 128}; rank r in {8, 16, 32, 64}; H <= 128;
+ *    NB <= 8192 (N <= 524288); B*H*NG*max(k_h) < 2^31.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = -1,   /* null pointer, bad enum, NULL problem */
+  DSA_ERR_SHAPE = -2,         /* sizes not supported / not divisible */
+  DSA_ERR_DTYPE = -3,         /* dtype not supported for this call */
+  DSA_ERR_ALIGN = -4,         /* a device pointer not 16-byte aligned */
+  DSA_ERR_UNSUPPORTED = -5,   /* combination outside the limits above */
+  DSA_ERR_WORKSPACE = -6,     /* workspace missing or too small */
+  DSA_ERR_HIP = -7            /* a HIP launch or runtime call failed */
+} dsa_status;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;
+
+typedef struct {
+  int32_t batch;      /* B */
+  int32_t heads;      /* H */
+  int32_t seq_len;    /* N tokens per sequence */
+  int32_t head_dim;   /* d */
+  int32_t rank;       /* predictor rank r (d_lr) */
+  int32_t group;      /* query-group size G */
+  int32_t block;      /* KV block size, must be 64 */
+  int32_t dtype;      /* dsa_dtype of Q, K, V, dO */
+} dsa_problem;
+
+/* Which call a workspace is sized for. */
+typedef enum { DSA_WS_SELECT = 0, DSA_WS_BWD = 1 } dsa_ws_call;
+
+/* Library version string. */
+const char* dsa_version(void);
+
+/* Static, human-readable text of a status code. */
+const char* dsa_status_string(int status);
+
+/*
+ * dsa_index_layout: host-only helper.  Writes row_base[0 .. B*H] (B*H + 1
+ * int64 entries, host memory): the element offset of each (b, h) region of the
+ * kept-block list; row_base[B*H] is the total number of entries.
+ */
+int dsa_index_layout(const dsa_problem* p, const int32_t* k_per_head, int64_t* row_base);
+
+/* Bytes of workspace the given call needs (0 if the arguments are invalid). */
+size_t dsa_workspace_bytes(const dsa_problem* p, const int32_t* k_per_head, int which_call);
+
+/*
+ * dsa_predict_block_scores -- the low-rank sparsity predictor (hi §2.A, nl §2.A;
+ * query grouping with a proxy query, hi §2.B).
+ *   qhat[b,h,g,:]   = mean_{i in group g} Q[b,h,i,:] . Wq[h]      [B,H,NG,r] fp32
+ *   khat[b,h,j,:]   = mean_{m in block j} K[b,h,m,:] . Wk[h]      [B,H,NB,r] fp32
+ *   scores[b,h,g,j] = tau * qhat[b,h,g,:] . khat[b,h,j,:]         [B,H,NG,NB] fp32
+ * Wq, Wk: [H, d, r] fp32.  scores may be NULL (then only qhat, khat are
+ * written; dsa_select_topk_blocks can stream the scores itself).
+ */
+int dsa_predict_block_scores(const dsa_problem* p, const void* Q, const void* K,
+                             const float* Wq, const float* Wk, float* qhat, float* khat,
+                             float* scores, void* stream);
+
+/*
+ * dsa_select_topk_blocks -- critical KV block selection (hi §2.A critical KV
+ * estimation; hi §2.B / nl §2.B fused low-rank MatMul + top-k).
+ * For each (b, h, g): the k_h block ids j with the largest scores[b,h,g,j],
+ * ties broken towards the lowest j (-0.0 equals +0.0), written ascending to
+ * idx.  If scores is NULL the scores are recomputed from qhat/khat inside the
+ * kernel, bit-identical to dsa_predict_block_scores' and never stored (the
+ * O(S*k) memory mode); scores_dump, if not NULL, then receives them
+ * [B,H,NG,NB] (debug/checking only).
+ * Also builds the reverse index: rev_ptr [B*H, NB+1] int32 holds, per (b, h),
+ * offsets into that (b, h)'s region of rev_idx (same row_base as idx); the
+ * segment of block j lists, ascending, every group g whose row kept j.
+ * Workspace: dsa_workspace_bytes(p, k_per_head, DSA_WS_SELECT).
+ */
+int dsa_select_topk_blocks(const dsa_problem* p, const float* scores, const float* qhat,
+                           const float* khat, const int32_t* k_per_head, int32_t* idx,
+                           int32_t* rev_ptr, int32_t* rev_idx, float* scores_dump,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_sparse_attn_fwd -- exact attention over the kept blocks only (hi §2.A
+ * stage 2; nl §2.A fase 2).  For query i of group g and the keys m of the
+ * blocks in idx row (b,h,g): l_im = tau Q_i.K_m, LSE_i = ln sum_m exp(l_im),
+ * O_i = sum_m exp(l_im - LSE_i) V_m.  No causal mask.
+ * O: [B,H,N,d] fp32; LSE: [B,H,N] fp32 (natural log).
+ */
+int dsa_sparse_attn_fwd(const dsa_problem* p, const void* Q, const void* K, const void* V,
+                        const int32_t* idx, const int32_t* k_per_head, float* O, float* LSE,
+                        void* stream);
+
+/*
+ * dsa_sparse_attn_bwd -- gradient of sum(dO * O) for the forward above, the
+ * selection held fixed (the pages describe a training system, hi §2 and §3;
+ * the gradient itself is the standard softmax-attention one on the kept keys):
+ *   D_i = dO_i.O_i, P = exp(l - LSE), dS = P (dO V^T - D),
+ *   dQ_g = tau dS K, dK_m = tau sum dS^T Q, dV_m = sum P^T dO,
+ * keys of blocks no group kept get dK = dV = 0.  Needs the forward's O and
+ * LSE, and rev_ptr/rev_idx from dsa_select_topk_blocks.  dQ, dK, dV:
+ * [B,H,N,d] fp32.  bf16 inputs only.  Deterministic (no atomics).
+ * Workspace: dsa_workspace_bytes(p, k_per_head, DSA_WS_BWD).
+ */
+int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, const void* V,
+                        const float* O, const void* dO, const float* LSE, const int32_t* idx,
+                        const int32_t* k_per_head, const int32_t* rev_ptr, const int32_t* rev_idx,
+                        float* dQ, float* dK, float* dV, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * The three stages dsa_sparse_attn_bwd runs, exposed one launch each (same
+ * arguments and rules as above; Dvec is [B,H,N] fp32, D_i = dO_i . O_i):
+ *   dsa_sparse_attn_bwd_preprocess  Dvec from O and dO;
+ *   dsa_sparse_attn_bwd_dkdv        dK, dV from the reverse index (every key
+ *                                   row of every block is written);
+ *   dsa_sparse_attn_bwd_dq          dQ from the kept-block lists.
+ */
+int dsa_sparse_attn_bwd_preprocess(const dsa_problem* p, const float* O, const void* dO, float* Dvec, void* stream);
+int dsa_sparse_attn_bwd_dkdv(const dsa_problem* p, const void* Q, const void* K, const void* V, const void* dO,
+                             const float* LSE, const float* Dvec, const int32_t* k_per_head, const int32_t* rev_ptr,
+                             const int32_t* rev_idx, float* dK, float* dV, void* stream);
+int dsa_sparse_attn_bwd_dq(const dsa_problem* p, const void* Q, const void* K, const void* V, const void* dO,
+                           const float* LSE, const float* Dvec, const int32_t* idx, const int32_t* k_per_head,
+                           float* dQ, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

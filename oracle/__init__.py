@@ -12,11 +12,11 @@ unpinned".
 from . import dsv_oracle
 from .dsv_oracle import (
     BLOCK, backward, backward_head, dkdv_blocks, dq_groups, forward, forward_head, group_backward,
-    group_forward, kept_keys, pool_mean, predict, predict_head, reverse_index, select, select_row,
+    group_forward, kept_keys, pool_mean, predict, predict_head, reverse_index, reverse_list, select, select_row,
 )
 
 __all__ = [
     "dsv_oracle", "BLOCK", "backward", "backward_head", "dkdv_blocks", "dq_groups", "forward",
     "forward_head", "group_backward", "group_forward", "kept_keys", "pool_mean", "predict",
-    "predict_head", "reverse_index", "select", "select_row",
+    "predict_head", "reverse_index", "reverse_list", "select", "select_row",
 ]

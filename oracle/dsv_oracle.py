@@ -116,6 +116,11 @@ def reverse_index(idx_bh: np.ndarray, n_blocks: int) -> List[np.ndarray]:
     return [np.asarray(l, dtype=np.int64) for l in lists]
 
 
+def reverse_list(idx_bh: np.ndarray, j: int) -> np.ndarray:
+    """Ascending query groups whose selection holds block j (one entry of reverse_index)."""
+    return np.nonzero((np.asarray(idx_bh) == j).any(axis=1))[0].astype(np.int64)
+
+
 def kept_keys(idx_row: np.ndarray, block: int = BLOCK) -> np.ndarray:
     """Key positions covered by the kept blocks of one group, ascending."""
     return (np.asarray(idx_row, dtype=np.int64)[:, None] * block + np.arange(block)[None, :]).ravel()

@@ -7,9 +7,9 @@ to the storage dtype.  Both the HIP path and the CPU oracle consume the exact
 stored values it returns.
 """
 from .workloads import WORKLOADS, Workload, keep_to_k, workload
-from .latents import Inputs, generate, bf16_bits_to_f32, f32_to_bf16_bits, random_dense, morton_order
+from .latents import Inputs, generate, bf16_bits_to_f32, f32_to_bf16_bits, random_dense, morton_order, per_head_k
 
 __all__ = [
     "WORKLOADS", "Workload", "workload", "keep_to_k",
-    "Inputs", "generate", "bf16_bits_to_f32", "f32_to_bf16_bits", "random_dense", "morton_order",
+    "Inputs", "generate", "bf16_bits_to_f32", "f32_to_bf16_bits", "random_dense", "morton_order", "per_head_k",
 ]

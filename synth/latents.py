@@ -27,7 +27,7 @@ from __future__ import annotations
 
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
-from typing import Dict, Optional
+from typing import Dict, Optional, Sequence
 
 import numpy as np
 
@@ -119,8 +119,12 @@ def _structure(w: Workload, rng: np.random.Generator, coords: np.ndarray):
     return centres, emb, scale, keep, kph, wts
 
 
-def generate(w: Workload, threads: int = 8) -> Inputs:
-    """Draw the inputs of workload ``w`` (deterministic for a given workload)."""
+def generate(w: Workload, threads: int = 8, heads: Optional[Sequence[int]] = None) -> Inputs:
+    """Draw the inputs of workload ``w`` (deterministic for a given workload).
+
+    ``heads`` restricts the draw to a subset of heads; each drawn head holds
+    exactly the values the full draw gives it (per-head streams).
+    """
     if w.seq_len % w.block or w.seq_len % w.group:
         raise ValueError("token count must be a multiple of the block and group sizes")
     coords = morton_order(w.grid)
@@ -131,26 +135,36 @@ def generate(w: Workload, threads: int = 8) -> Inputs:
     owner = nearest_centre(coords, centres)
 
     n, d = w.seq_len, w.head_dim
+    hsel = list(range(w.heads)) if heads is None else [int(h) for h in heads]
     store = np.uint16 if w.dtype == "bf16" else np.float32
-    shape = (w.batch, w.heads, n, d)
+    shape = (w.batch, len(hsel), n, d)
     outs = [np.empty(shape, dtype=store) for _ in range(n_tensors)]
 
     def fill(job):
-        t, b, h = job
+        t, b, hi = job
+        h = hsel[hi]
         rng = np.random.Generator(np.random.PCG64(children[1 + (t * w.batch + b) * w.heads + h]))
         x = rng.standard_normal((n, d), dtype=np.float32)
         if t < 2:
             x += (scale[h] * emb[h]).astype(np.float32)[owner]
-        outs[t][b, h] = f32_to_bf16_bits(x) if w.dtype == "bf16" else x
+        outs[t][b, hi] = f32_to_bf16_bits(x) if w.dtype == "bf16" else x
 
-    jobs = [(t, b, h) for t in range(n_tensors) for b in range(w.batch) for h in range(w.heads)]
+    jobs = [(t, b, hi) for t in range(n_tensors) for b in range(w.batch) for hi in range(len(hsel))]
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         list(ex.map(fill, jobs))
 
     return Inputs(
         workload=w, q=outs[0], k=outs[1], v=outs[2], do=outs[3] if w.backward else None,
-        w=wts, k_per_head=kph, coords=coords, cell_centre=owner, head_scale=scale, head_keep=keep,
+        w=wts[hsel], k_per_head=kph[hsel], coords=coords, cell_centre=owner, head_scale=scale[hsel],
+        head_keep=keep[hsel],
     )
+
+
+def per_head_k(w: Workload) -> np.ndarray:
+    """The kept-block counts k_h of a workload without drawing its tensors."""
+    coords = morton_order(w.grid)
+    child = np.random.SeedSequence(w.seed).spawn(1)[0]
+    return _structure(w, np.random.Generator(np.random.PCG64(child)), coords)[4]
 
 
 def random_dense(shape, seed: int, dtype: str = "bf16", scale: float = 1.0) -> np.ndarray:

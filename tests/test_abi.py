@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: the library loads, exports what include/dsa.h declares,
+and host-side validation rejects bad arguments before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_sparse_attention_qk_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", f)).read()
+            names += re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(dsa_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("dsa_predict_block_scores", "dsa_select_topk_blocks", "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dsa.library()
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(_declared()) == set(dsa.EXPORTED)
+    assert "gfx950" in dsa.version()
+
+
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below fails validation first
+
+
+def _p(**kw):
+    base = dict(batch=1, heads=2, seq_len=1024, head_dim=64, rank=16, group=64, block=64, dtype=dsa.DSA_BF16)
+    base.update(kw)
+    return dsa.Problem(**base)
+
+
+def _fwd(p, kph, ptr=FAKE):
+    lib = dsa.library()
+    return lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), ptr, ptr, ptr, ptr, dsa._kph(kph), ptr, ptr, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(seq_len=1000), -2),            # not a multiple of the block
+    (dict(seq_len=64 * 3, group=128), -2),  # not a multiple of the group
+    (dict(head_dim=96), -5),
+    (dict(rank=12), -5),
+    (dict(group=32), -5),
+    (dict(block=32), -5),
+    (dict(dtype=7), -3),
+    (dict(heads=0), -2),
+    (dict(heads=129), -5),
+    (dict(seq_len=64 * 8193), -5),       # more than 8192 blocks
+])
+def test_bad_problem_rejected(kw, status):
+    p = _p(**kw)
+    assert _fwd(p, [1] * max(p.heads, 1)) == status
+
+
+def test_bad_k_rejected():
+    p = _p()
+    assert _fwd(p, [0, 1]) == -2
+    assert _fwd(p, [1, 17]) == -2      # k > NB = 16
+
+
+def test_null_and_misaligned_pointers():
+    lib = dsa.library()
+    p = _p()
+    kph = dsa._kph([4, 4])
+    assert lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), None, FAKE, FAKE, FAKE, kph, FAKE, FAKE, None) == -1
+    bad = ctypes.c_void_p(0x100004)
+    assert lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), FAKE, bad, FAKE, FAKE, kph, FAKE, FAKE, None) == -4
+    assert lib.dsa_sparse_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, kph, FAKE, FAKE, None) == -1
+    assert lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == -1
+
+
+def test_workspace_checks():
+    lib = dsa.library()
+    p = _p()
+    kph = [4, 4]
+    need = dsa.workspace_bytes(p, kph, dsa.DSA_WS_SELECT)
+    assert need >= 2 * 16 * 4 + 16 * 8 * 4  # counters + scratch reverse list
+    assert dsa.workspace_bytes(p, kph, dsa.DSA_WS_BWD) >= 2 * 1024 * 4
+    assert dsa.workspace_bytes(_p(seq_len=1000), kph, 0) == 0
+    st = lib.dsa_select_topk_blocks(ctypes.byref(p.c()), FAKE, FAKE, FAKE, dsa._kph(kph), FAKE, FAKE, FAKE, None,
+                                    FAKE, need - 1, None)
+    assert st == -6
+    st = lib.dsa_select_topk_blocks(ctypes.byref(p.c()), FAKE, FAKE, FAKE, dsa._kph(kph), FAKE, FAKE, FAKE, None,
+                                    None, need, None)
+    assert st == -6
+    st = lib.dsa_sparse_attn_bwd(ctypes.byref(p.c()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dsa._kph(kph), FAKE,
+                                 FAKE, FAKE, FAKE, FAKE, FAKE, 16, None)
+    assert st == -6
+    pf = _p(dtype=dsa.DSA_F32)
+    st = lib.dsa_sparse_attn_bwd(ctypes.byref(pf.c()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dsa._kph(kph), FAKE,
+                                 FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert st == -3                      # backward is bf16-only
+
+
+def test_index_layout_ragged():
+    p = _p(batch=2, heads=3, seq_len=640)
+    kph = [1, 5, 10]
+    rb = dsa.index_layout(p, kph)
+    ng = 10
+    assert list(rb) == [0, ng * 1, ng * 6, ng * 16, ng * 17, ng * 22, ng * 32]
+    with pytest.raises(dsa.DsaError):
+        dsa.index_layout(p, [1, 5, 11])
+
+
+def test_status_strings():
+    for s in range(0, -8, -1):
+        assert dsa.status_string(s) != "unknown status"
+    assert dsa.status_string(5) == "unknown status"

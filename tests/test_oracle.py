@@ -209,6 +209,7 @@ def check_reverse_index(seed=12):
     rev = O.reverse_index(idx, nb)
     for j in range(nb):
         assert list(rev[j]) == [g for g in range(ng) if j in set(idx[g])]
+        assert list(O.reverse_list(idx, j)) == list(rev[j])
 
 
 def check_batched_api(seed=13):

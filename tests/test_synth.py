@@ -74,3 +74,14 @@ def test_clusters_shared_by_q_and_k():
     qk = q @ k.T
     assert qk[same].mean() > qk[~same].mean() + 20.0      # scale 3 clusters: ~9*64 shared energy
     assert abs((q @ v.T).mean()) < 1.0
+
+
+def test_head_subset_is_exact():
+    w = synth.workload(5).with_(grid=(2, 8, 16), n_centres=8)
+    full = synth.generate(w)
+    sub = synth.generate(w, heads=[3, 17])
+    for name in ("q", "k", "v", "do"):
+        np.testing.assert_array_equal(getattr(sub, name)[:, 0], getattr(full, name)[:, 3])
+        np.testing.assert_array_equal(getattr(sub, name)[:, 1], getattr(full, name)[:, 17])
+    assert list(sub.k_per_head) == [full.k_per_head[3], full.k_per_head[17]]
+    np.testing.assert_array_equal(sub.w[1], full.w[17])

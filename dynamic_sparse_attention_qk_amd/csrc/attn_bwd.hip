@@ -19,50 +19,6 @@ namespace dsa {
 
 namespace {
 
-template <int D, int NT>
-struct Mover {  // 64 x D bf16 tile as 8 x 8 sub-blocks held in registers
-  static constexpr int NSB = 8 * (D / 8);
-  static constexpr int SBT = (NSB + NT - 1) / NT;
-  uint4 r[SBT][8];
-
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ src) {
-#pragma unroll
-    for (int s = 0; s < SBT; ++s) {
-      const int sb = threadIdx.x + s * NT;
-      if (sb < NSB) {
-        const int rb = sb / (D / 8), cb = sb % (D / 8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r[s][i] = ldg16(src + (size_t)(8 * rb + i) * D + 8 * cb);
-      }
-    }
-  }
-  __device__ __forceinline__ void store_rows(bf16_t* dst, int ld) const {
-#pragma unroll
-    for (int s = 0; s < SBT; ++s) {
-      const int sb = threadIdx.x + s * NT;
-      if (sb < NSB) {
-        const int rb = sb / (D / 8), cb = sb % (D / 8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(dst + (8 * rb + i) * ld + 8 * cb) = r[s][i];
-      }
-    }
-  }
-  // transposed, as fp16 (exact conversion of the bf16 values)
-  __device__ __forceinline__ void store_cols_f16(uint16_t* dst, int ld) const {
-#pragma unroll
-    for (int s = 0; s < SBT; ++s) {
-      const int sb = threadIdx.x + s * NT;
-      if (sb < NSB) {
-        const int rb = sb / (D / 8), cb = sb % (D / 8);
-        uint4 h[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = bf16x8_to_f16x8(r[s][i]);
-        store_transposed_8x8(h, dst + (8 * cb) * ld + 8 * rb, ld);
-      }
-    }
-  }
-};
-
 // D_i = sum_c dO_ic O_ic; one 16-lane slice per row, 8 columns per lane.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__ dO, const float* __restrict__ O,
@@ -92,10 +48,10 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(const bf16_t* __restrict_
                                                        const int32_t* __restrict__ rev_ptr,
                                                        const int32_t* __restrict__ rev_idx, float* __restrict__ dK,
                                                        float* __restrict__ dV, HeadTable ht, int N, int H, int NB,
-                                                       float scale_log2, float tau) {
+                                                       int B, float scale_log2, float tau) {
   constexpr int NT = 128;
-  constexpr int LD = D + 8;       // row-major tiles
-  constexpr int TLD = 64 + 8;     // transposed tiles
+  constexpr int LD = kRowLd<D>;   // row-major tiles
+  constexpr int TLD = kColLd;     // transposed tiles
   constexpr int SUB = G / 64;     // 64-row query sub-tiles per group
   __shared__ __attribute__((aligned(16))) bf16_t sQ[64 * LD];
   __shared__ __attribute__((aligned(16))) bf16_t sdO[64 * LD];
@@ -104,7 +60,8 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(const bf16_t* __restrict_
   __shared__ __attribute__((aligned(16))) float sL[64];
   __shared__ __attribute__((aligned(16))) float sD[64];
 
-  const int b = blockIdx.z, h = blockIdx.y, j = blockIdx.x;
+  const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NB * H * B));
+  const int j = L % NB, h = (L / NB) % H, b = L / (NB * H);
   const int NG = N / G;
   const size_t bh = (size_t)b * H + h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -131,7 +88,7 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(const bf16_t* __restrict_
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) { dk[c] = f32x16{}; dv[c] = f32x16{}; }
 
-  Mover<D, NT> mq, mo;
+  TileMover<D, NT> mq, mo;
   float lse_pre = 0.f, d_pre = 0.f;
   auto fetch = [&](int it) {
     const int g = min(max(rlist[it / SUB], 0), NG - 1);  // valid by contract; never read out of bounds
@@ -147,10 +104,10 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(const bf16_t* __restrict_
 
   for (int it = 0; it < iters; ++it) {
     __syncthreads();
-    mq.store_rows(sQ, LD);
-    mq.store_cols_f16(sQt, TLD);
-    mo.store_rows(sdO, LD);
-    mo.store_cols_f16(sdOt, TLD);
+    mq.store_rows(sQ);
+    mq.store_cols_f16(sQt);
+    mo.store_rows(sdO);
+    mo.store_cols_f16(sdOt);
     if (threadIdx.x < 64) { sL[threadIdx.x] = lse_pre; sD[threadIdx.x] = d_pre; }
     __syncthreads();
     if (it + 1 < iters) fetch(it + 1);
@@ -221,16 +178,17 @@ __global__ __launch_bounds__(G * 2) void bwd_dq_kernel(const bf16_t* __restrict_
                                                        const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
                                                        const float* __restrict__ LSE, const float* __restrict__ Dvec,
                                                        const int32_t* __restrict__ idx, float* __restrict__ dQ,
-                                                       HeadTable ht, int N, int H, float scale_log2, float tau) {
+                                                       HeadTable ht, int N, int H, int B, float scale_log2, float tau) {
   constexpr int NT = G * 2;
-  constexpr int LD = D + 8;
-  constexpr int TLD = 64 + 8;
+  constexpr int LD = kRowLd<D>;
+  constexpr int TLD = kColLd;
   __shared__ __attribute__((aligned(16))) bf16_t sK[64 * LD];
   __shared__ __attribute__((aligned(16))) bf16_t sV[64 * LD];
   __shared__ __attribute__((aligned(16))) uint16_t sKt[D * TLD];  // fp16
 
-  const int b = blockIdx.z, h = blockIdx.y, g = blockIdx.x;
   const int NG = N / G;
+  const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NG * H * B));
+  const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
   const int k = ht.k[h];
   const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * k;
   const size_t bh = (size_t)b * H + h;
@@ -259,7 +217,7 @@ __global__ __launch_bounds__(G * 2) void bwd_dq_kernel(const bf16_t* __restrict_
 
   const int NB = N / kBlock;
   auto block_id = [&](int t) { return min(max(irow[t], 0), NB - 1); };
-  Mover<D, NT> mk, mv;
+  TileMover<D, NT> mk, mv;
   {
     const int j = block_id(0);
     mk.load(Kbh + (size_t)j * kBlock * D);
@@ -267,9 +225,9 @@ __global__ __launch_bounds__(G * 2) void bwd_dq_kernel(const bf16_t* __restrict_
   }
   for (int t = 0; t < k; ++t) {
     __syncthreads();
-    mk.store_rows(sK, LD);
-    mk.store_cols_f16(sKt, TLD);
-    mv.store_rows(sV, LD);
+    mk.store_rows(sK);
+    mk.store_cols_f16(sKt);
+    mv.store_rows(sV);
     __syncthreads();
     if (t + 1 < k) {
       const int j = block_id(t + 1);
@@ -333,8 +291,8 @@ hipError_t dkdv_launch(const Shape& s, const bf16_t* Q, const bf16_t* K, const b
                        const float* LSE, const float* Dvec, const int32_t* rev_ptr, const int32_t* rev_idx, float* dK,
                        float* dV, const HeadTable& ht, hipStream_t st) {
   const float tau = 1.0f / sqrtf((float)D);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3(s.NB, s.H, s.B), dim3(128), 0, st, Q, K, V, dO, LSE, Dvec,
-                     rev_ptr, rev_idx, dK, dV, ht, s.N, s.H, s.NB, tau * kLog2e, tau);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3((unsigned)(s.NB * s.H * s.B)), dim3(128), 0, st, Q, K, V, dO, LSE,
+                     Dvec, rev_ptr, rev_idx, dK, dV, ht, s.N, s.H, s.NB, s.B, tau * kLog2e, tau);
   return hipGetLastError();
 }
 
@@ -343,8 +301,8 @@ hipError_t dq_launch(const Shape& s, const bf16_t* Q, const bf16_t* K, const bf1
                      const float* LSE, const float* Dvec, const int32_t* idx, float* dQ, const HeadTable& ht,
                      hipStream_t st) {
   const float tau = 1.0f / sqrtf((float)D);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3(s.NG, s.H, s.B), dim3(G * 2), 0, st, Q, K, V, dO, LSE, Dvec, idx, dQ,
-                     ht, s.N, s.H, tau * kLog2e, tau);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3((unsigned)(s.NG * s.H * s.B)), dim3(G * 2), 0, st, Q, K, V, dO, LSE,
+                     Dvec, idx, dQ, ht, s.N, s.H, s.B, tau * kLog2e, tau);
   return hipGetLastError();
 }
 

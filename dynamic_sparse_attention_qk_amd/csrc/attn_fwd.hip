@@ -20,67 +20,22 @@ namespace dsa {
 
 namespace {
 
-// Cooperative tile movement: a 64 x D bf16 tile is cut into 8 x 8 sub-blocks,
-// each thread moving at most SBT of them (8 rows x 16 bytes in registers).
-template <int D, int NT>
-struct TileMover {
-  static constexpr int NSB = 8 * (D / 8);
-  static constexpr int SBT = (NSB + NT - 1) / NT;
-  uint4 r[SBT][8];
-
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ src) {  // src: first row of the tile
-#pragma unroll
-    for (int s = 0; s < SBT; ++s) {
-      const int sb = threadIdx.x + s * NT;
-      if (sb < NSB) {
-        const int rb = sb / (D / 8), cb = sb % (D / 8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r[s][i] = ldg16(src + (size_t)(8 * rb + i) * D + 8 * cb);
-      }
-    }
-  }
-  __device__ __forceinline__ void store_rows(bf16_t* dst, int ld) const {  // dst[m * ld + c]
-#pragma unroll
-    for (int s = 0; s < SBT; ++s) {
-      const int sb = threadIdx.x + s * NT;
-      if (sb < NSB) {
-        const int rb = sb / (D / 8), cb = sb % (D / 8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(dst + (8 * rb + i) * ld + 8 * cb) = r[s][i];
-      }
-    }
-  }
-  // dst[c * ld + m] as fp16 (exact conversion of the bf16 values)
-  __device__ __forceinline__ void store_cols_f16(uint16_t* dst, int ld) const {
-#pragma unroll
-    for (int s = 0; s < SBT; ++s) {
-      const int sb = threadIdx.x + s * NT;
-      if (sb < NSB) {
-        const int rb = sb / (D / 8), cb = sb % (D / 8);
-        uint4 h[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = bf16x8_to_f16x8(r[s][i]);
-        store_transposed_8x8(h, dst + (8 * cb) * ld + 8 * rb, ld);
-      }
-    }
-  }
-};
-
 template <int D, int G>
 __global__ __launch_bounds__(G * 2) void attn_fwd_bf16_kernel(const bf16_t* __restrict__ Q,
                                                               const bf16_t* __restrict__ K,
                                                               const bf16_t* __restrict__ V,
                                                               const int32_t* __restrict__ idx, float* __restrict__ O,
                                                               float* __restrict__ LSE, HeadTable ht, int N, int H,
-                                                              float scale_log2) {
+                                                              int B, float scale_log2) {
   constexpr int NT = G * 2;      // G/32 waves
-  constexpr int KLD = D + 8;     // K tile row stride (elements)
-  constexpr int VLD = 64 + 8;    // V^T tile row stride
+  constexpr int KLD = kRowLd<D>;
+  constexpr int VLD = kColLd;
   __shared__ __attribute__((aligned(16))) bf16_t sK[64 * KLD];
   __shared__ __attribute__((aligned(16))) uint16_t sVt[D * VLD];  // fp16
 
-  const int b = blockIdx.z, h = blockIdx.y, g = blockIdx.x;
   const int NG = N / G;
+  const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NG * H * B));
+  const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
   const int k = ht.k[h];
   const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * k;
   const size_t bh = (size_t)b * H + h;
@@ -114,8 +69,8 @@ __global__ __launch_bounds__(G * 2) void attn_fwd_bf16_kernel(const bf16_t* __re
 
   for (int t = 0; t < k; ++t) {
     __syncthreads();
-    kt.store_rows(sK, KLD);
-    vt.store_cols_f16(sVt, VLD);
+    kt.store_rows(sK);
+    vt.store_cols_f16(sVt);
     __syncthreads();
     if (t + 1 < k) {
       const int j = block_id(t + 1);
@@ -179,14 +134,15 @@ __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __rest
                                                              const float* __restrict__ V,
                                                              const int32_t* __restrict__ idx, float* __restrict__ O,
                                                              float* __restrict__ LSE, HeadTable ht, int N, int H,
-                                                             float scale_log2) {
+                                                             int B, float scale_log2) {
   constexpr int NT = G * 2;
   constexpr int LD = D + 1;
   __shared__ float sK[64 * LD];
   __shared__ float sV[64 * LD];
 
-  const int b = blockIdx.z, h = blockIdx.y, g = blockIdx.x;
   const int NG = N / G;
+  const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NG * H * B));
+  const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
   const int k = ht.k[h];
   const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * k;
   const size_t bh = (size_t)b * H + h;
@@ -270,15 +226,15 @@ template <int D, int G>
 hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx, float* O,
                       float* LSE, const HeadTable& ht, hipStream_t st) {
   const float scale_log2 = (1.0f / sqrtf((float)D)) * kLog2e;
-  dim3 grid(s.NG, s.H, s.B);
+  dim3 grid((unsigned)(s.NG * s.H * s.B));
   if (s.bf16)
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, G>), grid, dim3(G * 2), 0, st, static_cast<const bf16_t*>(Q),
                        static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V), idx, O, LSE, ht, s.N, s.H,
-                       scale_log2);
+                       s.B, scale_log2);
   else
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D, G>), grid, dim3(G * 2), 0, st, static_cast<const float*>(Q),
                        static_cast<const float*>(K), static_cast<const float*>(V), idx, O, LSE, ht, s.N, s.H,
-                       scale_log2);
+                       s.B, scale_log2);
   return hipGetLastError();
 }
 

@@ -149,26 +149,102 @@ __device__ __forceinline__ f16x8 lds_pair_b64_h(const uint16_t* p) {
 // 16-byte global load / store helpers.
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Transposed store of an 8x8 bf16 sub-tile held as 8 rows x 16 bytes:
-// writes column c (8 values from rows 0..7) as 16 contiguous bytes at dst[c*ld].
-__device__ __forceinline__ void store_transposed_8x8(const uint4 (&rows)[8], bf16_t* dst, int ld) {
+// Transposed store of an 8x8 16-bit sub-tile held as 8 rows x 16 bytes:
+// writes column c (8 values from rows 0..7) as 16 contiguous bytes at dst[c*ld]
+// (two 8-byte stores: transposed tiles use a row stride of 2 mod 4 dwords).
+__device__ __forceinline__ void store_transposed_8x8(const uint4 (&rows)[8], uint16_t* dst, int ld) {
   const uint32_t* w[8];
 #pragma unroll
   for (int r = 0; r < 8; ++r) w[r] = reinterpret_cast<const uint32_t*>(&rows[r]);
 #pragma unroll
   for (int c2 = 0; c2 < 4; ++c2) {
-    uint4 even, odd;  // columns 2*c2 and 2*c2+1
-    uint32_t* pe = reinterpret_cast<uint32_t*>(&even);
-    uint32_t* po = reinterpret_cast<uint32_t*>(&odd);
+    uint32_t pe[4], po[4];  // columns 2*c2 and 2*c2+1
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      uint32_t a = w[2 * p][c2], b = w[2 * p + 1][c2];
+      const uint32_t a = w[2 * p][c2], b = w[2 * p + 1][c2];
       pe[p] = (a & 0xFFFFu) | (b << 16);
       po[p] = (a >> 16) | (b & 0xFFFF0000u);
     }
-    *reinterpret_cast<uint4*>(dst + (2 * c2) * ld) = even;
-    *reinterpret_cast<uint4*>(dst + (2 * c2 + 1) * ld) = odd;
+    uint2* de = reinterpret_cast<uint2*>(dst + (2 * c2) * ld);
+    uint2* dd = reinterpret_cast<uint2*>(dst + (2 * c2 + 1) * ld);
+    de[0] = make_uint2(pe[0], pe[1]);
+    de[1] = make_uint2(pe[2], pe[3]);
+    dd[0] = make_uint2(po[0], po[1]);
+    dd[1] = make_uint2(po[2], po[3]);
   }
+}
+
+// Row stride (16-bit elements) of row-major LDS tiles of width D: 16 bytes of
+// padding keep the 8 rows read by one 128-bit pass on distinct banks.
+template <int D>
+constexpr int kRowLd = D + 8;
+// Row stride of transposed tiles (64 columns): 34 dwords, so 16 lanes reading
+// 8 bytes from 16 consecutive rows hit 16 distinct bank pairs.
+constexpr int kColLd = 64 + 4;
+
+// Cooperative movement of a 64 x D bf16 tile (rows of D contiguous values)
+// through registers into LDS, as 8 x 8 sub-blocks.  Sub-block sb of a thread
+// is (row block rb, column chunk cb) with rb = sb % 8 and cb = (sb / 8 + rb)
+// mod D/8: the 8 lanes of one LDS pass take a diagonal, which keeps both the
+// row-major and the transposed stores free of bank conflicts.
+template <int D, int NT>
+struct TileMover {
+  static constexpr int NC = D / 8;
+  static constexpr int NSB = 8 * NC;
+  static constexpr int SBT = (NSB + NT - 1) / NT;
+  uint4 r[SBT][8];
+
+  __device__ __forceinline__ static int rb_of(int sb) { return sb % 8; }
+  __device__ __forceinline__ static int cb_of(int sb) { return (sb / 8 + sb % 8) % NC; }
+
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src) {  // src: first row of the tile
+#pragma unroll
+    for (int s = 0; s < SBT; ++s) {
+      const int sb = threadIdx.x + s * NT;
+      if (NSB % NT == 0 || sb < NSB) {
+        const int rb = rb_of(sb), cb = cb_of(sb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[s][i] = ldg16(src + (size_t)(8 * rb + i) * D + 8 * cb);
+      }
+    }
+  }
+  __device__ __forceinline__ void store_rows(uint16_t* dst) const {  // dst[m * kRowLd + c]
+#pragma unroll
+    for (int s = 0; s < SBT; ++s) {
+      const int sb = threadIdx.x + s * NT;
+      if (NSB % NT == 0 || sb < NSB) {
+        const int rb = rb_of(sb), cb = cb_of(sb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<uint4*>(dst + (8 * rb + i) * kRowLd<D> + 8 * cb) = r[s][i];
+      }
+    }
+  }
+  // dst[c * kColLd + m] as fp16 (exact conversion of the bf16 values)
+  __device__ __forceinline__ void store_cols_f16(uint16_t* dst) const {
+#pragma unroll
+    for (int s = 0; s < SBT; ++s) {
+      const int sb = threadIdx.x + s * NT;
+      if (NSB % NT == 0 || sb < NSB) {
+        const int rb = rb_of(sb), cb = cb_of(sb);
+        uint4 h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) h[i] = bf16x8_to_f16x8(r[s][i]);
+        store_transposed_8x8(h, dst + (8 * cb) * kColLd + 8 * rb, kColLd);
+      }
+    }
+  }
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Map the hardware id w (of n) to a logical index such that every XCD
+// runs one contiguous range of the logical order -- neighbouring query groups,
+// which share most kept blocks, then meet in the same L2.
+constexpr uint32_t kXcds = 8;
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t n) {
+  const uint32_t q = n / kXcds, r = n % kXcds;
+  const uint32_t x = w % kXcds, i = w / kXcds;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
 }
 
 __device__ __forceinline__ float wave_max_pair(float v) {  // max with lane l^32

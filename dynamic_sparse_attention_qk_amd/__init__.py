@@ -28,7 +28,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdsa.so")
 
 DSA_F32, DSA_BF16 = 0, 1
-DSA_WS_SELECT, DSA_WS_BWD = 0, 1
+DSA_WS_SELECT, DSA_WS_BWD, DSA_WS_FWD = 0, 1, 2
 
 
 class DsaError(RuntimeError):
@@ -65,7 +65,7 @@ def library() -> ctypes.CDLL:
         lib.dsa_predict_block_scores.argtypes = [pp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp]
         lib.dsa_select_topk_blocks.argtypes = [pp, f32p, f32p, f32p, kph, i32p, i32p, i32p, f32p, vp,
                                                ctypes.c_size_t, vp]
-        lib.dsa_sparse_attn_fwd.argtypes = [pp, vp, vp, vp, i32p, kph, f32p, f32p, vp]
+        lib.dsa_sparse_attn_fwd.argtypes = [pp, vp, vp, vp, i32p, kph, f32p, f32p, vp, ctypes.c_size_t, vp]
         lib.dsa_sparse_attn_bwd.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, kph, i32p, i32p, f32p, f32p,
                                             f32p, vp, ctypes.c_size_t, vp]
         lib.dsa_sparse_attn_bwd_preprocess.argtypes = [pp, f32p, vp, f32p, vp]
@@ -166,10 +166,11 @@ def select_topk_blocks(p: Problem, scores, qhat, khat, k_per_head, idx, rev_ptr,
         _stream(stream)))
 
 
-def sparse_attn_fwd(p: Problem, Q, K, V, idx, k_per_head, O, LSE, stream=None) -> None:
+def sparse_attn_fwd(p: Problem, Q, K, V, idx, k_per_head, O, LSE, workspace=None, stream=None) -> None:
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("dsa_sparse_attn_fwd", library().dsa_sparse_attn_fwd(
         ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _kph(k_per_head), _ptr(O), _ptr(LSE),
-        _stream(stream)))
+        _ptr(workspace), nbytes, _stream(stream)))
 
 
 def sparse_attn_bwd(p: Problem, Q, K, V, O, dO, LSE, idx, k_per_head, rev_ptr, rev_idx, dQ, dK, dV, workspace,
@@ -218,6 +219,8 @@ class SparseAttentionPlan:
         self.rev_idx = torch.empty(max(total, 1), **i32)
         self.ws_select = torch.empty(workspace_bytes(p, self.k_per_head, DSA_WS_SELECT), dtype=torch.uint8,
                                      device=device)
+        self.ws_fwd = torch.empty(max(workspace_bytes(p, self.k_per_head, DSA_WS_FWD), 16), dtype=torch.uint8,
+                                  device=device)
         self.O = torch.empty(B, H, N, D, **f32)
         self.LSE = torch.empty(B, H, N, **f32)
         if backward:
@@ -235,7 +238,7 @@ class SparseAttentionPlan:
                            self.rev_idx, self.ws_select, scores_dump=scores_dump, stream=stream)
 
     def forward(self, Q, K, V, stream=None):
-        sparse_attn_fwd(self.p, Q, K, V, self.idx, self.k_per_head, self.O, self.LSE, stream)
+        sparse_attn_fwd(self.p, Q, K, V, self.idx, self.k_per_head, self.O, self.LSE, self.ws_fwd, stream)
 
     def backward(self, Q, K, V, dO, stream=None):
         sparse_attn_bwd(self.p, Q, K, V, self.O, dO, self.LSE, self.idx, self.k_per_head, self.rev_ptr,

@@ -66,6 +66,9 @@ size_t select_ws(const Shape& s, const HeadTable& ht) {
 
 size_t bwd_ws(const Shape& s) { return align256((size_t)s.B * s.H * s.N * sizeof(float)); }
 
+// forward: an fp16 copy of V (bf16 inputs only)
+size_t fwd_ws(const Shape& s) { return s.bf16 ? align256((size_t)s.B * s.H * s.N * s.D * 2) : 0; }
+
 int hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
 }  // namespace
@@ -107,6 +110,7 @@ size_t dsa_workspace_bytes(const dsa_problem* p, const int32_t* k_per_head, int 
   if (check_problem(p, &s) || check_heads(s, k_per_head, &ht, nullptr)) return 0;
   if (which_call == DSA_WS_SELECT) return select_ws(s, ht);
   if (which_call == DSA_WS_BWD) return bwd_ws(s);
+  if (which_call == DSA_WS_FWD) return fwd_ws(s);
   return 0;
 }
 
@@ -155,7 +159,8 @@ int dsa_select_topk_blocks(const dsa_problem* p, const float* scores, const floa
 }
 
 int dsa_sparse_attn_fwd(const dsa_problem* p, const void* Q, const void* K, const void* V, const int32_t* idx,
-                        const int32_t* k_per_head, float* O, float* LSE, void* stream) {
+                        const int32_t* k_per_head, float* O, float* LSE, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   Shape s;
   HeadTable ht;
   int st = check_problem(p, &s);
@@ -164,7 +169,11 @@ int dsa_sparse_attn_fwd(const dsa_problem* p, const void* Q, const void* K, cons
   if (!Q || !K || !V || !idx || !O || !LSE) return DSA_ERR_INVALID_ARG;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(idx) || !aligned16(O) || !aligned16(LSE))
     return DSA_ERR_ALIGN;
-  return hip_status(dsa::launch_attn_fwd(s, Q, K, V, idx, O, LSE, ht, static_cast<hipStream_t>(stream)));
+  const size_t need = fwd_ws(s);
+  if (need && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return DSA_ERR_ALIGN;
+  return hip_status(dsa::launch_attn_fwd(s, Q, K, V, idx, O, LSE, static_cast<uint16_t*>(workspace), ht,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 static int check_bwd_common(const dsa_problem* p, const int32_t* k_per_head, Shape* s, HeadTable* ht) {

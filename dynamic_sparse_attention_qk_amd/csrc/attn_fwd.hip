@@ -20,30 +20,48 @@ namespace dsa {
 
 namespace {
 
+// bf16 -> fp16 shadow copy (exact for |x| in [2^-14, 65504]); 8 values per thread step.
+__global__ __launch_bounds__(256) void cvt_bf16_f16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                           int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    dst[i] = bf16x8_to_f16x8(src[i]);
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(G * 2) void attn_fwd_bf16_kernel(const bf16_t* __restrict__ Q,
-                                                              const bf16_t* __restrict__ K,
-                                                              const bf16_t* __restrict__ V,
-                                                              const int32_t* __restrict__ idx, float* __restrict__ O,
-                                                              float* __restrict__ LSE, HeadTable ht, int N, int H,
-                                                              int B, float scale_log2) {
-  constexpr int NT = G * 2;      // G/32 waves
-  constexpr int KLD = kRowLd<D>;
-  constexpr int VLD = kColLd;
-  __shared__ __attribute__((aligned(16))) bf16_t sK[64 * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * VLD];  // fp16
+__global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* __restrict__ Q,
+                                                                 const bf16_t* __restrict__ K,
+                                                                 const uint16_t* __restrict__ V16,
+                                                                 const int32_t* __restrict__ idx,
+                                                                 float* __restrict__ O, float* __restrict__ LSE,
+                                                                 HeadTable ht, int N, int H, int B,
+                                                                 float scale_log2) {
+  constexpr int NRT = G / 32;                  // 32-row tiles of the group
+  constexpr int NW = 2 * NRT;                  // waves: row tile x key half
+  constexpr int RB = 2 * D;                    // bytes per tile row
+  constexpr int TILE = 64 * RB;                // one 64 x D 16-bit tile
+  constexpr int OBUF = D * 128;                // one row tile's O partial: 64 lanes x D/2 floats
+  // two stages (K bf16 + V fp16 each), separate objects so the compiler can see
+  // that reads of one stage never alias the DMA filling the other
+  __shared__ __attribute__((aligned(1024))) char st0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char st1[2 * TILE];
+  __shared__ float sml[NRT][2][64];            // m and l of the key-half-1 waves
+  static_assert(NRT * OBUF <= 4 * TILE, "merge buffers must fit in the stages");
 
   const int NG = N / G;
   const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NG * H * B));
   const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
   const int k = ht.k[h];
+  const int NB = N / kBlock;
   const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * k;
   const size_t bh = (size_t)b * H + h;
   const bf16_t* Kbh = K + bh * (size_t)N * D;
-  const bf16_t* Vbh = V + bh * (size_t)N * D;
+  const uint16_t* Vbh = V16 + bh * (size_t)N * D;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int qrow = g * G + wave * 32 + l32;
+  const int rt = wave % NRT, kh = wave / NRT;  // rows 32*rt.., keys 32*kh.. of every block
+  const int qrow = g * G + rt * 32 + l32;
+  // block ids are valid by contract; clamping keeps a bad list from reading out of bounds
+  auto block_id = [&](int t) { return min(max(irow[t], 0), NB - 1); };
 
   bf16x8 qreg[D / 16];
   {
@@ -51,81 +69,105 @@ __global__ __launch_bounds__(G * 2) void attn_fwd_bf16_kernel(const bf16_t* __re
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) qreg[t] = *reinterpret_cast<const bf16x8*>(qp + 16 * t);
   }
+  // LDS byte offsets: K rows for S^T = K Q^T, and the transpose-read windows of V for O^T += V^T P^T
+  int kofs[D / 16];
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) kofs[c] = tile_off<D>(32 * kh + l32, 2 * c + hh);
+  // transpose read r (0/1) of column tile c: lane addresses row 32*kh + 8*r + rl of the 16-key chunk,
+  // columns 32*c + 16*(g16 & 1) + 4*(li & 3); the chunk at +16 rows has the same swizzle
+  const int li = lane & 15, g16 = lane >> 4;
+  const int rl = 4 * hh + (li >> 2);
+  int vofs[D / 32][2];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      vofs[c][r] = TILE + tile_off<D>(32 * kh + 8 * r + rl, 4 * c + 2 * (g16 & 1) + ((li & 3) >> 1)) + 8 * (li & 1);
 
-  const int NB = N / kBlock;
-  // block ids are valid by contract; clamping keeps a bad list from reading out of bounds
-  auto block_id = [&](int t) { return min(max(irow[t], 0), NB - 1); };
-  TileMover<D, NT> kt, vt;
-  {
-    const int j = block_id(0);
-    kt.load(Kbh + (size_t)j * kBlock * D);
-    vt.load(Vbh + (size_t)j * kBlock * D);
-  }
-
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_used = -INFINITY, l_run = 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) oacc[c] = f32x16{};
 
-  for (int t = 0; t < k; ++t) {
-    __syncthreads();
-    kt.store_rows(sK);
-    vt.store_cols_f16(sVt);
-    __syncthreads();
-    if (t + 1 < k) {
-      const int j = block_id(t + 1);
-      kt.load(Kbh + (size_t)j * kBlock * D);
-      vt.load(Vbh + (size_t)j * kBlock * D);
-    }
-    // S^T tiles: keys 0..31 and 32..63 of the block against the wave's 32 queries
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+  auto fetch = [&](int t, char* dst) {
+    const int j = block_id(t);
+    dma_tile<D, NW>(Kbh + (size_t)j * kBlock * D, dst, wave, lane);
+    dma_tile<D, NW>(Vbh + (size_t)j * kBlock * D, dst + TILE, wave, lane);
+  };
+  auto step = [&](int t, const char* cur, char* nxt) {
+    wait_vmem();
+    __syncthreads();  // block t is in LDS and every wave is done with block t-1
+    if (t + 1 < k) fetch(t + 1, nxt);
+    f32x16 sacc = f32x16{};  // element e: key 32*kh + 8*(e/4) + 4*hh + e%4, query row l32
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&sK[l32 * KLD + 16 * c + 8 * hh]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&sK[(32 + l32) * KLD + 16 * c + 8 * hh]);
-      s0 = mfma32(a0, qreg[c], s0);
-      s1 = mfma32(a1, qreg[c], s1);
-    }
-    float mx = s0[0];
+    for (int c = 0; c < D / 16; ++c)
+      sacc = mfma32(*reinterpret_cast<const bf16x8*>(cur + kofs[c]), qreg[c], sacc);
+    float bm = sacc[0];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fmaxf(s0[e], s1[e]));
-    mx = wave_max_pair(mx) * scale_log2;
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float rs = 0.f;
+    for (int e = 1; e < 16; ++e) bm = fmaxf(bm, sacc[e]);
+    bm = wave_max_pair(bm) * scale_log2;
+    // lazy rescale: keep the running max unless the block exceeds it by 2^8
+    if (__ballot(bm > m_used + 8.0f)) {
+      const float m_new = fmaxf(m_used, bm);
+      const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) oacc[c] *= alpha;
+      m_used = m_new;
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      s0[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[e], scale_log2, -m_new));
-      s1[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[e], scale_log2, -m_new));
-      rs += s0[e] + s1[e];
+      sacc[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], scale_log2, -m_used));
+      l_run += sacc[e];
     }
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) oacc[c] *= alpha;
-    const f16x8 p0 = pack_f16(s0, 0), p1 = pack_f16(s0, 1), p2 = pack_f16(s1, 0), p3 = pack_f16(s1, 1);
+    const f16x8 p0 = pack_f16(sacc, 0), p1 = pack_f16(sacc, 1);
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
-      const uint16_t* vrow = &sVt[(32 * c + l32) * VLD + 4 * hh];
-      oacc[c] = mfma32h(lds_pair_b64_h(vrow + 0), p0, oacc[c]);
-      oacc[c] = mfma32h(lds_pair_b64_h(vrow + 16), p1, oacc[c]);
-      oacc[c] = mfma32h(lds_pair_b64_h(vrow + 32), p2, oacc[c]);
-      oacc[c] = mfma32h(lds_pair_b64_h(vrow + 48), p3, oacc[c]);
+      const char* v0 = cur + vofs[c][0];
+      const char* v1 = cur + vofs[c][1];
+      oacc[c] = mfma32h(join_f16(lds_read_tr16(v0), lds_read_tr16(v1)), p0, oacc[c]);
+      oacc[c] = mfma32h(join_f16(lds_read_tr16(v0 + 16 * RB), lds_read_tr16(v1 + 16 * RB)), p1, oacc[c]);
     }
+  };
+
+  fetch(0, st0);
+  for (int t = 0; t < k; t += 2) {
+    step(t, st0, st1);
+    if (t + 1 < k) step(t + 1, st1, st0);
   }
 
+  // merge the two key halves of each row tile (O partials parked in the stage buffers)
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  float* orow = O + (bh * N + qrow) * (size_t)D;
+  __syncthreads();
+  float* mb = reinterpret_cast<float*>((rt < 2 ? st0 : st1) + (rt & 1) * OBUF);
+  if (kh == 1) {
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c)
+    for (int c = 0; c < D / 32; ++c)
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      float4 v = make_float4(oacc[c][4 * q4] * inv, oacc[c][4 * q4 + 1] * inv, oacc[c][4 * q4 + 2] * inv,
-                             oacc[c][4 * q4 + 3] * inv);
-      *reinterpret_cast<float4*>(orow + 32 * c + 8 * q4 + 4 * hh) = v;
-    }
-  if (hh == 0) LSE[bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
+      for (int e = 0; e < 16; ++e) mb[(c * 16 + e) * 64 + lane] = oacc[c][e];
+    sml[rt][0][lane] = m_used;
+    sml[rt][1][lane] = l_tot;
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m1 = sml[rt][0][lane], l1 = sml[rt][1][lane];
+    const float m = fmaxf(m_used, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_used - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+    const float lsum = a0 * l_tot + a1 * l1;
+    const float inv = 1.0f / lsum;
+    const float w0 = a0 * inv, w1 = a1 * inv;
+    float* orow = O + (bh * N + qrow) * (size_t)D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = oacc[c][4 * q4 + r] * w0 + mb[(c * 16 + 4 * q4 + r) * 64 + lane] * w1;
+        *reinterpret_cast<float4*>(orow + 32 * c + 8 * q4 + 4 * hh) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    if (hh == 0) LSE[bh * N + qrow] = (m + __log2f(lsum)) * kLn2;
+  }
 }
 
 // fp32 operands: v_mfma_f32_32x32x2_f32, K and V row-major in LDS.
@@ -224,14 +266,17 @@ __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __rest
 
 template <int D, int G>
 hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx, float* O,
-                      float* LSE, const HeadTable& ht, hipStream_t st) {
+                      float* LSE, uint16_t* V16, const HeadTable& ht, hipStream_t st) {
   const float scale_log2 = (1.0f / sqrtf((float)D)) * kLog2e;
   dim3 grid((unsigned)(s.NG * s.H * s.B));
-  if (s.bf16)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, G>), grid, dim3(G * 2), 0, st, static_cast<const bf16_t*>(Q),
-                       static_cast<const bf16_t*>(K), static_cast<const bf16_t*>(V), idx, O, LSE, ht, s.N, s.H,
-                       s.B, scale_log2);
-  else
+  if (s.bf16) {
+    const int64_t n16 = (int64_t)s.B * s.H * s.N * D / 8;
+    const int64_t nwg = (n16 + 255) / 256;
+    hipLaunchKernelGGL(cvt_bf16_f16_kernel, dim3((unsigned)(nwg < 8192 ? nwg : 8192)), dim3(256), 0, st,
+                       static_cast<const uint4*>(V), reinterpret_cast<uint4*>(V16), n16);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, G>), grid, dim3(G * 4), 0, st, static_cast<const bf16_t*>(Q),
+                       static_cast<const bf16_t*>(K), V16, idx, O, LSE, ht, s.N, s.H, s.B, scale_log2);
+  } else
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D, G>), grid, dim3(G * 2), 0, st, static_cast<const float*>(Q),
                        static_cast<const float*>(K), static_cast<const float*>(V), idx, O, LSE, ht, s.N, s.H,
                        s.B, scale_log2);
@@ -241,9 +286,13 @@ hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* 
 }  // namespace
 
 hipError_t launch_attn_fwd(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx, float* O,
-                           float* LSE, const HeadTable& ht, hipStream_t st) {
-  if (s.D == 64) return s.G == 64 ? fwd_launch<64, 64>(s, Q, K, V, idx, O, LSE, ht, st) : fwd_launch<64, 128>(s, Q, K, V, idx, O, LSE, ht, st);
-  if (s.D == 128) return s.G == 64 ? fwd_launch<128, 64>(s, Q, K, V, idx, O, LSE, ht, st) : fwd_launch<128, 128>(s, Q, K, V, idx, O, LSE, ht, st);
+                           float* LSE, uint16_t* V16, const HeadTable& ht, hipStream_t st) {
+  if (s.D == 64)
+    return s.G == 64 ? fwd_launch<64, 64>(s, Q, K, V, idx, O, LSE, V16, ht, st)
+                     : fwd_launch<64, 128>(s, Q, K, V, idx, O, LSE, V16, ht, st);
+  if (s.D == 128)
+    return s.G == 64 ? fwd_launch<128, 64>(s, Q, K, V, idx, O, LSE, V16, ht, st)
+                     : fwd_launch<128, 128>(s, Q, K, V, idx, O, LSE, V16, ht, st);
   return hipErrorInvalidValue;
 }
 

@@ -236,10 +236,103 @@ struct TileMover {
   }
 };
 
+// ---------------------------------------------------------------- LDS tiles filled by DMA
+// A 64 x D 16-bit tile is stored row-major without padding (row = 2*D bytes)
+// with its 16-byte chunks XOR-swizzled per row: physical chunk p of row r holds
+// logical chunk p ^ tile_swz<D>(r).  gfx950's LDS serves 64 banks (256 bytes)
+// per cycle; the swizzle makes
+//   - 16 consecutive rows read at one logical chunk (a 128-bit row read of 16
+//     lanes) fall on 16 distinct 16-byte bank groups, and
+//   - any 8-row x 4-chunk window at a 4-aligned chunk (one transpose read of a
+//     wave) cover every bank group exactly twice.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+__device__ __forceinline__ int tile_swz(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {  // D == 64: two rows share a 256-byte bank window
+    const int x = (r >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
+  }
+}
+
+// Byte offset of logical chunk q of row r.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int q) { return r * (2 * D) + 16 * (q ^ tile_swz<D>(r)); }
+
+// Issue the global->LDS copies of one 64 x D tile (rows of D contiguous 16-bit
+// values starting at src) into the LDS tile at lds_base; the NW waves of the
+// workgroup share the D/8 one-kilobyte copies.  Completion is awaited with
+// wait_vmem() before the workgroup barrier that publishes the tile.
+template <int D, int NW>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, char* lds_base, int wave, int lane) {
+  constexpr int RB = 2 * D;            // bytes per row
+  constexpr int RPI = 1024 / RB;       // rows per 1 KB copy
+  const int rin = (lane * 16) / RB;    // row within the copy
+  const int p = ((lane * 16) % RB) / 16;
+#pragma unroll
+  for (int j = wave; j < D / 8; j += NW) {
+    const int r = j * RPI + rin;
+    const uint16_t* g = src + (size_t)r * D + 8 * (p ^ tile_swz<D>(r));
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_base + j * 1024), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane i
+// receives element i%4 of the 8-byte chunks addressed by lanes 4e + i/4 of the
+// group, e = 0..3.  If lane L addresses row (r0 + L/4), columns c0 + 4*(L%4),
+// lane i receives column c0 + i of rows r0..r0+3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
+__device__ __forceinline__ f16x8 join_f16(i16x4 a, i16x4 b) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(f16x8, v);
+}
+
+// A 64 x D bf16 tile staged through registers and written to a swizzled LDS
+// tile as fp16 (exact conversion); chunk c of the tile (row c / (D/8), logical
+// chunk c % (D/8)) belongs to thread c % NT.  Consecutive lanes take
+// consecutive chunks of a row: coalesced loads and conflict-free stores.
+template <int D, int NT>
+struct F16Stager {
+  static constexpr int NCH = 64 * D / 8;
+  static constexpr int PER = (NCH + NT - 1) / NT;
+  uint4 r[PER];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * NT;
+      if (NCH % NT == 0 || c < NCH) r[i] = ldg16(src + (size_t)(c / (D / 8)) * D + 8 * (c % (D / 8)));
+    }
+  }
+  __device__ __forceinline__ void store(char* tile) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * NT;
+      if (NCH % NT == 0 || c < NCH)
+        *reinterpret_cast<uint4*>(tile + tile_off<D>(c / (D / 8), c % (D / 8))) = bf16x8_to_f16x8(r[i]);
+    }
+  }
+};
+
+__device__ __forceinline__ bf16x8 join_bf16(i16x4 a, i16x4 b) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2).  Map the hardware id w (of n) to a logical index such that every XCD
 // runs one contiguous range of the logical order -- neighbouring query groups,
-// which share most kept blocks, then meet in the same L2.
+// which share most kept blocks, then meet in the same L2.  (Interleaving
+// 64-item runs across the XCDs measured slower on the 57.6k-token workload.)
 constexpr uint32_t kXcds = 8;
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t n) {
   const uint32_t q = n / kXcds, r = n % kXcds;

@@ -25,7 +25,7 @@ hipError_t launch_reverse_index(const Shape& s, const int32_t* idx, int32_t* rev
                                 int32_t* counters, int32_t* scratch, const HeadTable& ht, int kmax,
                                 hipStream_t st);
 hipError_t launch_attn_fwd(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx,
-                           float* O, float* LSE, const HeadTable& ht, hipStream_t st);
+                           float* O, float* LSE, uint16_t* V16, const HeadTable& ht, hipStream_t st);
 hipError_t launch_bwd_pre(const Shape& s, const float* O, const void* dO, float* Dvec, hipStream_t st);
 hipError_t launch_bwd_dkdv(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
                            const float* LSE, const float* Dvec, const int32_t* rev_ptr, const int32_t* rev_idx,

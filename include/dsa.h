@@ -69,7 +69,7 @@ typedef struct {
 } dsa_problem;
 
 /* Which call a workspace is sized for. */
-typedef enum { DSA_WS_SELECT = 0, DSA_WS_BWD = 1 } dsa_ws_call;
+typedef enum { DSA_WS_SELECT = 0, DSA_WS_BWD = 1, DSA_WS_FWD = 2 } dsa_ws_call;
 
 /* Library version string. */
 const char* dsa_version(void);
@@ -125,10 +125,14 @@ int dsa_select_topk_blocks(const dsa_problem* p, const float* scores, const floa
  * blocks in idx row (b,h,g): l_im = tau Q_i.K_m, LSE_i = ln sum_m exp(l_im),
  * O_i = sum_m exp(l_im - LSE_i) V_m.  No causal mask.
  * O: [B,H,N,d] fp32; LSE: [B,H,N] fp32 (natural log).
+ * Workspace: dsa_workspace_bytes(p, k_per_head, DSA_WS_FWD) (an fp16 copy of V
+ * for bf16 inputs; 0 bytes, NULL allowed, for fp32 inputs).  bf16 V, and every
+ * bf16 input of the backward, must be below 65504 in magnitude (products with
+ * softmax probabilities run on fp16 operands, converted exactly from bf16).
  */
 int dsa_sparse_attn_fwd(const dsa_problem* p, const void* Q, const void* K, const void* V,
                         const int32_t* idx, const int32_t* k_per_head, float* O, float* LSE,
-                        void* stream);
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dsa_sparse_attn_bwd -- gradient of sum(dO * O) for the forward above, the

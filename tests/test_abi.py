@@ -45,7 +45,8 @@ def _p(**kw):
 
 def _fwd(p, kph, ptr=FAKE):
     lib = dsa.library()
-    return lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), ptr, ptr, ptr, ptr, dsa._kph(kph), ptr, ptr, None)
+    return lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), ptr, ptr, ptr, ptr, dsa._kph(kph), ptr, ptr, ptr, 1 << 40,
+                                   None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -75,11 +76,19 @@ def test_null_and_misaligned_pointers():
     lib = dsa.library()
     p = _p()
     kph = dsa._kph([4, 4])
-    assert lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), None, FAKE, FAKE, FAKE, kph, FAKE, FAKE, None) == -1
+    big = 1 << 40
+    assert lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), None, FAKE, FAKE, FAKE, kph, FAKE, FAKE, FAKE, big, None) == -1
     bad = ctypes.c_void_p(0x100004)
-    assert lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), FAKE, bad, FAKE, FAKE, kph, FAKE, FAKE, None) == -4
-    assert lib.dsa_sparse_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, kph, FAKE, FAKE, None) == -1
-    assert lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == -1
+    assert lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), FAKE, bad, FAKE, FAKE, kph, FAKE, FAKE, FAKE, big, None) == -4
+    assert lib.dsa_sparse_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, kph, FAKE, FAKE, FAKE, big, None) == -1
+    assert lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, big,
+                                   None) == -1
+    # bf16 forward needs the fp16 copy of V
+    assert lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), FAKE, FAKE, FAKE, FAKE, kph, FAKE, FAKE, None, 0, None) == -6
+    need = dsa.workspace_bytes(p, [4, 4], dsa.DSA_WS_FWD)
+    assert need >= 2 * 1024 * 64 * 2
+    assert lib.dsa_sparse_attn_fwd(ctypes.byref(p.c()), FAKE, FAKE, FAKE, FAKE, kph, FAKE, FAKE, FAKE, need - 1,
+                                   None) == -6
 
 
 def test_workspace_checks():

@@ -151,13 +151,11 @@ def main():
         plan.forward(Q, K, V)
         marks[3].record()
         if backward:
-            dvec = plan.ws_bwd.view(torch.float32)[: p.batch * p.heads * p.seq_len]
-            dsa.sparse_attn_bwd_preprocess(p, plan.O, dO, dvec)
+            dsa.sparse_attn_bwd_preprocess(p, Q, K, V, plan.O, dO, plan.LSE, plan.ws_bwd)
             marks[4].record()
-            dsa.sparse_attn_bwd_dkdv(p, Q, K, V, dO, plan.LSE, dvec, kph, plan.rev_ptr, plan.rev_idx, plan.dK,
-                                     plan.dV)
+            dsa.sparse_attn_bwd_dkdv(p, kph, plan.rev_ptr, plan.rev_idx, plan.dK, plan.dV, plan.ws_bwd)
             marks[5].record()
-            dsa.sparse_attn_bwd_dq(p, Q, K, V, dO, plan.LSE, dvec, plan.idx, kph, plan.dQ)
+            dsa.sparse_attn_bwd_dq(p, plan.idx, kph, plan.dQ, plan.ws_bwd)
             marks[6].record()
         torch.cuda.synchronize()
         for i, n in enumerate(names):

@@ -68,9 +68,10 @@ def library() -> ctypes.CDLL:
         lib.dsa_sparse_attn_fwd.argtypes = [pp, vp, vp, vp, i32p, kph, f32p, f32p, vp, ctypes.c_size_t, vp]
         lib.dsa_sparse_attn_bwd.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, kph, i32p, i32p, f32p, f32p,
                                             f32p, vp, ctypes.c_size_t, vp]
-        lib.dsa_sparse_attn_bwd_preprocess.argtypes = [pp, f32p, vp, f32p, vp]
-        lib.dsa_sparse_attn_bwd_dkdv.argtypes = [pp, vp, vp, vp, vp, f32p, f32p, kph, i32p, i32p, f32p, f32p, vp]
-        lib.dsa_sparse_attn_bwd_dq.argtypes = [pp, vp, vp, vp, vp, f32p, f32p, i32p, kph, f32p, vp]
+        sz = ctypes.c_size_t
+        lib.dsa_sparse_attn_bwd_preprocess.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, vp, sz, vp]
+        lib.dsa_sparse_attn_bwd_dkdv.argtypes = [pp, kph, i32p, i32p, f32p, f32p, vp, sz, vp]
+        lib.dsa_sparse_attn_bwd_dq.argtypes = [pp, i32p, kph, f32p, vp, sz, vp]
         for name in ("dsa_index_layout", "dsa_predict_block_scores", "dsa_select_topk_blocks",
                      "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_preprocess",
                      "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq"):
@@ -181,22 +182,26 @@ def sparse_attn_bwd(p: Problem, Q, K, V, O, dO, LSE, idx, k_per_head, rev_ptr, r
         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def sparse_attn_bwd_preprocess(p: Problem, O, dO, Dvec, stream=None) -> None:
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def sparse_attn_bwd_preprocess(p: Problem, Q, K, V, O, dO, LSE, workspace, stream=None) -> None:
     _check("dsa_sparse_attn_bwd_preprocess", library().dsa_sparse_attn_bwd_preprocess(
-        ctypes.byref(p.c()), _ptr(O), _ptr(dO), _ptr(Dvec), _stream(stream)))
+        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(workspace),
+        _nbytes(workspace), _stream(stream)))
 
 
-def sparse_attn_bwd_dkdv(p: Problem, Q, K, V, dO, LSE, Dvec, k_per_head, rev_ptr, rev_idx, dK, dV,
-                         stream=None) -> None:
+def sparse_attn_bwd_dkdv(p: Problem, k_per_head, rev_ptr, rev_idx, dK, dV, workspace, stream=None) -> None:
     _check("dsa_sparse_attn_bwd_dkdv", library().dsa_sparse_attn_bwd_dkdv(
-        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), _ptr(Dvec), _kph(k_per_head),
-        _ptr(rev_ptr), _ptr(rev_idx), _ptr(dK), _ptr(dV), _stream(stream)))
+        ctypes.byref(p.c()), _kph(k_per_head), _ptr(rev_ptr), _ptr(rev_idx), _ptr(dK), _ptr(dV), _ptr(workspace),
+        _nbytes(workspace), _stream(stream)))
 
 
-def sparse_attn_bwd_dq(p: Problem, Q, K, V, dO, LSE, Dvec, idx, k_per_head, dQ, stream=None) -> None:
+def sparse_attn_bwd_dq(p: Problem, idx, k_per_head, dQ, workspace, stream=None) -> None:
     _check("dsa_sparse_attn_bwd_dq", library().dsa_sparse_attn_bwd_dq(
-        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), _ptr(Dvec), _ptr(idx),
-        _kph(k_per_head), _ptr(dQ), _stream(stream)))
+        ctypes.byref(p.c()), _ptr(idx), _kph(k_per_head), _ptr(dQ), _ptr(workspace), _nbytes(workspace),
+        _stream(stream)))
 
 
 class SparseAttentionPlan:
@@ -245,12 +250,11 @@ class SparseAttentionPlan:
                         self.rev_idx, self.dQ, self.dK, self.dV, self.ws_bwd, stream)
 
     def backward_stages(self, Q, K, V, dO, stream=None):
-        """The backward as its three single-launch stages (same result as backward())."""
-        dvec = self.ws_bwd.view(torch.float32)[: self.p.batch * self.p.heads * self.p.seq_len]
-        sparse_attn_bwd_preprocess(self.p, self.O, dO, dvec, stream)
-        sparse_attn_bwd_dkdv(self.p, Q, K, V, dO, self.LSE, dvec, self.k_per_head, self.rev_ptr, self.rev_idx,
-                             self.dK, self.dV, stream)
-        sparse_attn_bwd_dq(self.p, Q, K, V, dO, self.LSE, dvec, self.idx, self.k_per_head, self.dQ, stream)
+        """The backward as its three stages (same result as backward())."""
+        sparse_attn_bwd_preprocess(self.p, Q, K, V, self.O, dO, self.LSE, self.ws_bwd, stream)
+        sparse_attn_bwd_dkdv(self.p, self.k_per_head, self.rev_ptr, self.rev_idx, self.dK, self.dV, self.ws_bwd,
+                             stream)
+        sparse_attn_bwd_dq(self.p, self.idx, self.k_per_head, self.dQ, self.ws_bwd, stream)
 
     def step(self, Q, K, V, Wq, Wk, dO=None, stream=None):
         """predict -> select -> fwd (-> bwd): one pass of the whole hot path."""

@@ -64,7 +64,22 @@ size_t select_ws(const Shape& s, const HeadTable& ht) {
   return align256((size_t)s.B * s.H * s.NB * sizeof(int32_t)) + align256((size_t)s.B * s.NG * ht.ksum * sizeof(int32_t));
 }
 
-size_t bwd_ws(const Shape& s) { return align256((size_t)s.B * s.H * s.N * sizeof(float)); }
+size_t bwd_row_bytes(const Shape& s) { return align256((size_t)s.B * s.H * s.N * sizeof(float)); }
+size_t bwd_tensor_bytes(const Shape& s) { return align256((size_t)s.B * s.H * s.N * s.D * 2); }
+size_t bwd_ws(const Shape& s) { return 2 * bwd_row_bytes(s) + 4 * bwd_tensor_bytes(s); }
+
+dsa::BwdWork bwd_work(const Shape& s, void* ws) {
+  char* p = static_cast<char*>(ws);
+  dsa::BwdWork w;
+  w.Dvec = reinterpret_cast<float*>(p);
+  w.nl2 = reinterpret_cast<float*>(p + bwd_row_bytes(s));
+  char* t = p + 2 * bwd_row_bytes(s);
+  w.Q16 = reinterpret_cast<uint16_t*>(t);
+  w.K16 = reinterpret_cast<uint16_t*>(t + bwd_tensor_bytes(s));
+  w.V16 = reinterpret_cast<uint16_t*>(t + 2 * bwd_tensor_bytes(s));
+  w.dO16 = reinterpret_cast<uint16_t*>(t + 3 * bwd_tensor_bytes(s));
+  return w;
+}
 
 // forward: an fp16 copy of V (bf16 inputs only)
 size_t fwd_ws(const Shape& s) { return s.bf16 ? align256((size_t)s.B * s.H * s.N * s.D * 2) : 0; }
@@ -183,43 +198,50 @@ static int check_bwd_common(const dsa_problem* p, const int32_t* k_per_head, Sha
   return check_heads(*s, k_per_head, ht, nullptr);
 }
 
-int dsa_sparse_attn_bwd_preprocess(const dsa_problem* p, const float* O, const void* dO, float* Dvec, void* stream) {
+static int check_ws(const Shape& s, const void* workspace, size_t workspace_bytes) {
+  if (!workspace || workspace_bytes < bwd_ws(s)) return DSA_ERR_WORKSPACE;
+  return aligned16(workspace) ? DSA_OK : DSA_ERR_ALIGN;
+}
+
+int dsa_sparse_attn_bwd_preprocess(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
+                                   const void* dO, const float* LSE, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
   Shape s;
   int st = check_problem(p, &s);
   if (st) return st;
   if (!s.bf16) return DSA_ERR_DTYPE;
-  if (!O || !dO || !Dvec) return DSA_ERR_INVALID_ARG;
-  if (!aligned16(O) || !aligned16(dO) || !aligned16(Dvec)) return DSA_ERR_ALIGN;
-  return hip_status(dsa::launch_bwd_pre(s, O, dO, Dvec, static_cast<hipStream_t>(stream)));
+  if (!Q || !K || !V || !O || !dO || !LSE) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(LSE))
+    return DSA_ERR_ALIGN;
+  if ((st = check_ws(s, workspace, workspace_bytes))) return st;
+  return hip_status(dsa::launch_bwd_pre(s, Q, K, V, O, dO, LSE, bwd_work(s, workspace),
+                                        static_cast<hipStream_t>(stream)));
 }
 
-int dsa_sparse_attn_bwd_dkdv(const dsa_problem* p, const void* Q, const void* K, const void* V, const void* dO,
-                             const float* LSE, const float* Dvec, const int32_t* k_per_head, const int32_t* rev_ptr,
-                             const int32_t* rev_idx, float* dK, float* dV, void* stream) {
+int dsa_sparse_attn_bwd_dkdv(const dsa_problem* p, const int32_t* k_per_head, const int32_t* rev_ptr,
+                             const int32_t* rev_idx, float* dK, float* dV, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   Shape s;
   HeadTable ht;
   int st = check_bwd_common(p, k_per_head, &s, &ht);
   if (st) return st;
-  if (!Q || !K || !V || !dO || !LSE || !Dvec || !rev_ptr || !rev_idx || !dK || !dV) return DSA_ERR_INVALID_ARG;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(LSE) || !aligned16(Dvec) ||
-      !aligned16(rev_ptr) || !aligned16(rev_idx) || !aligned16(dK) || !aligned16(dV))
-    return DSA_ERR_ALIGN;
-  return hip_status(dsa::launch_bwd_dkdv(s, Q, K, V, dO, LSE, Dvec, rev_ptr, rev_idx, dK, dV, ht,
+  if (!rev_ptr || !rev_idx || !dK || !dV) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(rev_ptr) || !aligned16(rev_idx) || !aligned16(dK) || !aligned16(dV)) return DSA_ERR_ALIGN;
+  if ((st = check_ws(s, workspace, workspace_bytes))) return st;
+  return hip_status(dsa::launch_bwd_dkdv(s, bwd_work(s, workspace), rev_ptr, rev_idx, dK, dV, ht,
                                          static_cast<hipStream_t>(stream)));
 }
 
-int dsa_sparse_attn_bwd_dq(const dsa_problem* p, const void* Q, const void* K, const void* V, const void* dO,
-                           const float* LSE, const float* Dvec, const int32_t* idx, const int32_t* k_per_head,
-                           float* dQ, void* stream) {
+int dsa_sparse_attn_bwd_dq(const dsa_problem* p, const int32_t* idx, const int32_t* k_per_head, float* dQ,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   Shape s;
   HeadTable ht;
   int st = check_bwd_common(p, k_per_head, &s, &ht);
   if (st) return st;
-  if (!Q || !K || !V || !dO || !LSE || !Dvec || !idx || !dQ) return DSA_ERR_INVALID_ARG;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(LSE) || !aligned16(Dvec) ||
-      !aligned16(idx) || !aligned16(dQ))
-    return DSA_ERR_ALIGN;
-  return hip_status(dsa::launch_bwd_dq(s, Q, K, V, dO, LSE, Dvec, idx, dQ, ht, static_cast<hipStream_t>(stream)));
+  if (!idx || !dQ) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(idx) || !aligned16(dQ)) return DSA_ERR_ALIGN;
+  if ((st = check_ws(s, workspace, workspace_bytes))) return st;
+  return hip_status(dsa::launch_bwd_dq(s, bwd_work(s, workspace), idx, dQ, ht, static_cast<hipStream_t>(stream)));
 }
 
 int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
@@ -236,13 +258,12 @@ int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, cons
       !aligned16(idx) || !aligned16(rev_ptr) || !aligned16(rev_idx) || !aligned16(dQ) || !aligned16(dK) ||
       !aligned16(dV))
     return DSA_ERR_ALIGN;
-  if (!workspace || workspace_bytes < bwd_ws(s)) return DSA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return DSA_ERR_ALIGN;
+  if ((st = check_ws(s, workspace, workspace_bytes))) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  float* Dvec = static_cast<float*>(workspace);
-  hipError_t e = dsa::launch_bwd_pre(s, O, dO, Dvec, hs);
-  if (e == hipSuccess) e = dsa::launch_bwd_dkdv(s, Q, K, V, dO, LSE, Dvec, rev_ptr, rev_idx, dK, dV, ht, hs);
-  if (e == hipSuccess) e = dsa::launch_bwd_dq(s, Q, K, V, dO, LSE, Dvec, idx, dQ, ht, hs);
+  const dsa::BwdWork w = bwd_work(s, workspace);
+  hipError_t e = dsa::launch_bwd_pre(s, Q, K, V, O, dO, LSE, w, hs);
+  if (e == hipSuccess) e = dsa::launch_bwd_dkdv(s, w, rev_ptr, rev_idx, dK, dV, ht, hs);
+  if (e == hipSuccess) e = dsa::launch_bwd_dq(s, w, idx, dQ, ht, hs);
   return hip_status(e);
 }
 

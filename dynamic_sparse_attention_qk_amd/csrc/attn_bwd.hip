@@ -7,22 +7,30 @@
 //   D_i = dO_i . O_i,  dP = dO V^T,  dS = P (dP - D),
 //   dV_j = sum_g P^T dO_g,  dK_j = tau sum_g dS^T Q_g,  dQ_g = tau sum_j dS K_j.
 //
-// bwd_pre computes D.  bwd_dkdv runs one workgroup per (b, h, KV block) over
-// the groups of the block's reverse list; each of its 2 waves owns 32 keys and
-// keeps dK/dV in registers.  bwd_dq runs one workgroup per (b, h, group) over
-// the group's kept blocks; each wave owns 32 query rows.  Operands whose
-// contraction index is the row index in memory (Q and dO in dkdv, K in dq) are
-// staged transposed in LDS so every MFMA operand is a contiguous LDS read.
+// bwd_pre computes D and -LSE*log2(e) and writes exact fp16 copies of Q, K, V
+// and dO into the workspace, so every product below runs on fp16 MFMA with
+// tiles DMA-loaded into XOR-swizzled LDS (no register staging or conversion in
+// the loops) and transposed operands read with ds_read_b64_tr_b16.
+//
+// bwd_dq: one workgroup per (b, h, group) over the group's kept blocks; waves
+// = 32-row tile x key half, partial dQ of the two halves summed at the end.
+// bwd_dkdv: one workgroup per (b, h, KV block) over the block's reverse list;
+// waves = key half x 32-query half of each 64-row tile, dK/dV in registers,
+// partials of the two query halves summed at the end.  dK's dS operand is
+// split hi + lo in fp16 (dK sums a cancelling dS against clustered Q rows).
 #include "launch.hpp"
 
 namespace dsa {
 
 namespace {
 
-// D_i = sum_c dO_ic O_ic; one 16-lane slice per row, 8 columns per lane.
+// D_i = sum_c dO_ic O_ic, nl2_i = -LSE_i * log2(e), and the fp16 copy of dO;
+// one 16-lane slice per row (D = 128) or 8 (D = 64), 8 columns per lane.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__ dO, const float* __restrict__ O,
-                                                      float* __restrict__ Dvec, int64_t rows) {
+                                                      const float* __restrict__ LSE, float* __restrict__ Dvec,
+                                                      float* __restrict__ nl2, uint16_t* __restrict__ dO16,
+                                                      int64_t rows) {
   constexpr int LPR = D / 8;           // lanes per row
   constexpr int RPB = 256 / LPR;       // rows per workgroup pass
   const int sub = threadIdx.x % LPR;
@@ -35,30 +43,165 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__
               __uint_as_float(w[1] << 16) * o0.z + __uint_as_float(w[1] & 0xFFFF0000u) * o0.w +
               __uint_as_float(w[2] << 16) * o1.x + __uint_as_float(w[2] & 0xFFFF0000u) * o1.y +
               __uint_as_float(w[3] << 16) * o1.z + __uint_as_float(w[3] & 0xFFFF0000u) * o1.w;
+    *reinterpret_cast<uint4*>(dO16 + row * D + 8 * sub) = bf16x8_to_f16x8(d);
 #pragma unroll
     for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off);
-    if (sub == 0) Dvec[row] = s;
+    if (sub == 0) {
+      Dvec[row] = s;
+      nl2[row] = -LSE[row] * kLog2e;
+    }
   }
 }
 
+__device__ __forceinline__ f16x8 ldg_f16x8(const uint16_t* p) { return __builtin_bit_cast(f16x8, ldg16(p)); }
+
+// ---------------------------------------------------------------- dQ
+
 template <int D, int G>
-__global__ __launch_bounds__(128) void bwd_dkdv_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
-                                                       const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
-                                                       const float* __restrict__ LSE, const float* __restrict__ Dvec,
-                                                       const int32_t* __restrict__ rev_ptr,
-                                                       const int32_t* __restrict__ rev_idx, float* __restrict__ dK,
-                                                       float* __restrict__ dV, HeadTable ht, int N, int H, int NB,
-                                                       int B, float scale_log2, float tau) {
-  constexpr int NT = 128;
-  constexpr int LD = kRowLd<D>;   // row-major tiles
-  constexpr int TLD = kColLd;     // transposed tiles
-  constexpr int SUB = G / 64;     // 64-row query sub-tiles per group
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[64 * LD];
-  __shared__ __attribute__((aligned(16))) bf16_t sdO[64 * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[D * TLD];   // fp16
-  __shared__ __attribute__((aligned(16))) uint16_t sdOt[D * TLD];  // fp16
-  __shared__ __attribute__((aligned(16))) float sL[64];
-  __shared__ __attribute__((aligned(16))) float sD[64];
+__global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __restrict__ Q16,
+                                                          const uint16_t* __restrict__ K16,
+                                                          const uint16_t* __restrict__ V16,
+                                                          const uint16_t* __restrict__ dO16,
+                                                          const float* __restrict__ NL2, const float* __restrict__ Dvec,
+                                                          const int32_t* __restrict__ idx, float* __restrict__ dQ,
+                                                          HeadTable ht, int N, int H, int B, float scale_log2,
+                                                          float tau) {
+  constexpr int NRT = G / 32;
+  constexpr int NW = 2 * NRT;
+  constexpr int RB = 2 * D;
+  constexpr int TILE = 64 * RB;
+  constexpr int OBUF = D * 128;  // one wave's dQ partial: 64 lanes x D/2 floats
+  __shared__ __attribute__((aligned(1024))) char st0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char st1[2 * TILE];
+  static_assert(NRT * OBUF <= 4 * TILE, "merge buffers must fit in the stages");
+
+  const int NG = N / G;
+  const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NG * H * B));
+  const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
+  const int k = ht.k[h];
+  const int NB = N / kBlock;
+  const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * k;
+  const size_t bh = (size_t)b * H + h;
+  const uint16_t* Kbh = K16 + bh * (size_t)N * D;
+  const uint16_t* Vbh = V16 + bh * (size_t)N * D;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int rt = wave % NRT, kh = wave / NRT;
+  const size_t qrow = bh * N + (size_t)g * G + rt * 32 + l32;
+  auto block_id = [&](int t) { return min(max(irow[t], 0), NB - 1); };
+
+  f16x8 qreg[D / 16], oreg[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    qreg[t] = ldg_f16x8(Q16 + qrow * D + 16 * t + 8 * hh);
+    oreg[t] = ldg_f16x8(dO16 + qrow * D + 16 * t + 8 * hh);
+  }
+  const float nl2 = NL2[qrow];
+  const float dvec = Dvec[qrow];
+
+  int kofs[D / 16];  // K and V rows (keys of this half) as A operands
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) kofs[c] = tile_off<D>(32 * kh + l32, 2 * c + hh);
+  const int li = lane & 15, g16 = lane >> 4;
+  const int rl = 4 * hh + (li >> 2);
+  int tofs[D / 32][2];  // transpose reads of K (K^T as the A operand of dQ^T)
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      tofs[c][r] = tile_off<D>(32 * kh + 8 * r + rl, 4 * c + 2 * (g16 & 1) + ((li & 3) >> 1)) + 8 * (li & 1);
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) acc[c] = f32x16{};
+
+  auto fetch = [&](int t, char* dst) {
+    const int j = block_id(t);
+    dma_tile<D, NW>(Kbh + (size_t)j * kBlock * D, dst, wave, lane);
+    dma_tile<D, NW>(Vbh + (size_t)j * kBlock * D, dst + TILE, wave, lane);
+  };
+  auto step = [&](int t, const char* cur, char* nxt) {
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < k) fetch(t + 1, nxt);
+    // S^T and dP^T: rows = this half's 32 keys, columns = the wave's 32 queries
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      s = mfma32h(*reinterpret_cast<const f16x8*>(cur + kofs[c]), qreg[c], s);
+      dp = mfma32h(*reinterpret_cast<const f16x8*>(cur + TILE + kofs[c]), oreg[c], dp);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, nl2));
+      dp[e] = p * (dp[e] - dvec);
+    }
+    const f16x8 d0 = pack_f16(dp, 0), d1 = pack_f16(dp, 1);
+    // dQ^T[c][i] += K^T[c][m] dS^T[m][i]
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const char* t0 = cur + tofs[c][0];
+      const char* t1 = cur + tofs[c][1];
+      acc[c] = mfma32h(join_f16(lds_read_tr16(t0), lds_read_tr16(t1)), d0, acc[c]);
+      acc[c] = mfma32h(join_f16(lds_read_tr16(t0 + 16 * RB), lds_read_tr16(t1 + 16 * RB)), d1, acc[c]);
+    }
+  };
+
+  fetch(0, st0);
+  for (int t = 0; t < k; t += 2) {
+    step(t, st0, st1);
+    if (t + 1 < k) step(t + 1, st1, st0);
+  }
+
+  // sum the two key halves of each row tile
+  __syncthreads();
+  float* mb = reinterpret_cast<float*>((rt < 2 ? st0 : st1) + (rt & 1) * OBUF);
+  if (kh == 1) {
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mb[(c * 16 + e) * 64 + lane] = acc[c][e];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    float* orow = dQ + qrow * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (acc[c][4 * q4 + r] + mb[(c * 16 + 4 * q4 + r) * 64 + lane]) * tau;
+        *reinterpret_cast<float4*>(orow + 32 * c + 8 * q4 + 4 * hh) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+template <int D, int G>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q16,
+                                                          const uint16_t* __restrict__ K16,
+                                                          const uint16_t* __restrict__ V16,
+                                                          const uint16_t* __restrict__ dO16,
+                                                          const float* __restrict__ NL2,
+                                                          const float* __restrict__ Dvec,
+                                                          const int32_t* __restrict__ rev_ptr,
+                                                          const int32_t* __restrict__ rev_idx, float* __restrict__ dK,
+                                                          float* __restrict__ dV, HeadTable ht, int N, int H, int NB,
+                                                          int B, float tau) {
+  constexpr int NW = 4;
+  constexpr int RB = 2 * D;
+  constexpr int TILE = 64 * RB;
+  constexpr int STAGE = 2 * TILE + 512;  // Q16 tile, dO16 tile, -LSE*log2e row, D row
+  constexpr int SUB = G / 64;            // 64-row query tiles per group
+  constexpr int NDMA = 2 * (D / 8) / NW + 1;  // copies one wave issues per fetch
+  constexpr int OBUF = D * 256;          // one wave's dK + dV partial: 64 lanes x D floats
+  __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[STAGE];
+  static_assert(OBUF <= STAGE, "merge buffers must fit in the stages");
+  const float scale_log2 = tau * kLog2e;
 
   const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NB * H * B));
   const int j = L % NB, h = (L / NB) % H, b = L / (NB * H);
@@ -66,279 +209,188 @@ __global__ __launch_bounds__(128) void bwd_dkdv_kernel(const bf16_t* __restrict_
   const size_t bh = (size_t)b * H + h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
+  const int kw = wave & 1, qw = wave >> 1;  // keys 32*kw.., queries 32*qw.. of each 64-row tile
   const int32_t* rp = rev_ptr + bh * (NB + 1);
   const int32_t total = NG * ht.k[h];  // size of the (b, h) region of the reverse list
   const int32_t s0 = min(max(rp[j], 0), total), s1 = min(max(rp[j + 1], s0), total);
   const int32_t* rlist = rev_idx + row_base(ht, b, h, NG) + s0;
   const int iters = (s1 - s0) * SUB;
 
-  // the wave's 32 keys as B operands (K for S = Q K^T, V for dP = dO V^T)
-  bf16x8 kreg[D / 16], vreg[D / 16];
+  // this wave's 32 keys as B operands: K for S = Q K^T, V for dP = dO V^T
+  f16x8 kreg[D / 16], vreg[D / 16];
   {
-    const size_t key = bh * N + (size_t)j * kBlock + 32 * wave + l32;
-    const bf16_t* kp = K + key * D + 8 * hh;
-    const bf16_t* vp = V + key * D + 8 * hh;
+    const size_t key = bh * N + (size_t)j * kBlock + 32 * kw + l32;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
-      kreg[t] = *reinterpret_cast<const bf16x8*>(kp + 16 * t);
-      vreg[t] = *reinterpret_cast<const bf16x8*>(vp + 16 * t);
+      kreg[t] = ldg_f16x8(K16 + key * D + 16 * t + 8 * hh);
+      vreg[t] = ldg_f16x8(V16 + key * D + 16 * t + 8 * hh);
     }
   }
+  int aofs[D / 16];  // Q and dO rows of this query half as A operands
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) aofs[c] = tile_off<D>(32 * qw + l32, 2 * c + hh);
+  const int li = lane & 15, g16 = lane >> 4;
+  const int rl = 4 * hh + (li >> 2);
+  int tofs[D / 32][2];  // transpose reads of dO and Q (B operands of dV and dK)
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      tofs[c][r] = tile_off<D>(32 * qw + 8 * r + rl, 4 * c + 2 * (g16 & 1) + ((li & 3) >> 1)) + 8 * (li & 1);
+
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) { dk[c] = f32x16{}; dv[c] = f32x16{}; }
 
-  TileMover<D, NT> mq, mo;
-  float lse_pre = 0.f, d_pre = 0.f;
-  auto fetch = [&](int it) {
+  // every wave issues NDMA copies per fetch (the two row copies go to odd/even waves)
+  auto fetch = [&](int it, char* dst) {
     const int g = min(max(rlist[it / SUB], 0), NG - 1);  // valid by contract; never read out of bounds
     const size_t row0 = bh * N + (size_t)g * G + (size_t)(it % SUB) * 64;
-    mq.load(Q + row0 * D);
-    mo.load(dO + row0 * D);
-    if (threadIdx.x < 64) {
-      lse_pre = LSE[row0 + threadIdx.x] * kLog2e;
-      d_pre = Dvec[row0 + threadIdx.x];
-    }
+    dma_tile<D, NW>(Q16 + row0 * D, dst, wave, lane);
+    dma_tile<D, NW>(dO16 + row0 * D, dst + TILE, wave, lane);
+    if (wave & 1) dma_row64_f32(Dvec + row0, dst + 2 * TILE + 256, lane);
+    else dma_row64_f32(NL2 + row0, dst + 2 * TILE, lane);
   };
-  if (iters > 0) fetch(0);
-
-  for (int it = 0; it < iters; ++it) {
-    __syncthreads();
-    mq.store_rows(sQ);
-    mq.store_cols_f16(sQt);
-    mo.store_rows(sdO);
-    mo.store_cols_f16(sdOt);
-    if (threadIdx.x < 64) { sL[threadIdx.x] = lse_pre; sD[threadIdx.x] = d_pre; }
-    __syncthreads();
-    if (it + 1 < iters) fetch(it + 1);
-
-    // S[i][m] and dP[i][m] for the 64 queries (two 32-row tiles) x the wave's 32 keys
-    f32x16 s[2], dp[2];
+  auto step = [&](int it, const char* cur, char* nxt2) {
+    if (it + 1 < iters) wait_vmem_le<NDMA>(); else wait_vmem();  // this tile has landed, the next may still fly
+    wg_barrier();  // tile it is visible and every wave is done with tile it-1
+    if (it + 2 < iters) fetch(it + 2, nxt2);
+    // S[i][m], dP[i][m]: rows = the wave's 32 queries, columns = its 32 keys
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      s[qt] = f32x16{};
-      dp[qt] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&sQ[(32 * qt + l32) * LD + 16 * c + 8 * hh]);
-        const bf16x8 ao = *reinterpret_cast<const bf16x8*>(&sdO[(32 * qt + l32) * LD + 16 * c + 8 * hh]);
-        s[qt] = mfma32(aq, kreg[c], s[qt]);
-        dp[qt] = mfma32(ao, vreg[c], dp[qt]);
-      }
+    for (int c = 0; c < D / 16; ++c) {
+      s = mfma32h(*reinterpret_cast<const f16x8*>(cur + aofs[c]), kreg[c], s);
+      dp = mfma32h(*reinterpret_cast<const f16x8*>(cur + TILE + aofs[c]), vreg[c], dp);
     }
-    // P and dS; accumulator element e of tile qt is query 32*qt + 8*(e/4) + 4*hh + e%4
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 l4 = *reinterpret_cast<const float4*>(&sL[32 * qt + 8 * q4 + 4 * hh]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&sD[32 * qt + 8 * q4 + 4 * hh]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * q4 + r;
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][e], scale_log2, -lv[r]));
-          s[qt][e] = p;
-          dp[qt][e] = p * (dp[qt][e] - dvv[r]);
-        }
-      }
-    // dV[m][c] += P^T dO, dK[m][c] += dS^T Q  (A from accumulators, B transposed tiles)
-#pragma unroll
-    for (int qc = 0; qc < 4; ++qc) {
-      // dK sums dS (which cancels across queries) against Q of clustered rows: its
-      // operand is split hi + lo so fp16 rounding of dS does not reach the result.
-      const f16x8 pa = pack_f16(s[qc >> 1], qc & 1);
-      f16x8 da, da_lo;
-      pack_f16_split(dp[qc >> 1], qc & 1, da, da_lo);
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
-        dv[c] = mfma32h(pa, lds_pair_b64_h(&sdOt[(32 * c + l32) * TLD + 16 * qc + 4 * hh]), dv[c]);
-        const f16x8 qb = lds_pair_b64_h(&sQt[(32 * c + l32) * TLD + 16 * qc + 4 * hh]);
-        dk[c] = mfma32h(da, qb, dk[c]);
-        dk[c] = mfma32h(da_lo, qb, dk[c]);
-      }
-    }
-  }
-
-  // accumulator element e: key 8*(e/4) + 4*hh + e%4 of the wave's 32, column 32*c + l32
-  const size_t key0 = bh * N + (size_t)j * kBlock + 32 * wave;
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const size_t key = key0 + 8 * (e / 4) + 4 * hh + (e % 4);
-      dK[key * D + 32 * c + l32] = dk[c][e] * tau;
-      dV[key * D + 32 * c + l32] = dv[c][e];
-    }
-}
-
-template <int D, int G>
-__global__ __launch_bounds__(G * 2) void bwd_dq_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
-                                                       const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
-                                                       const float* __restrict__ LSE, const float* __restrict__ Dvec,
-                                                       const int32_t* __restrict__ idx, float* __restrict__ dQ,
-                                                       HeadTable ht, int N, int H, int B, float scale_log2, float tau) {
-  constexpr int NT = G * 2;
-  constexpr int LD = kRowLd<D>;
-  constexpr int TLD = kColLd;
-  __shared__ __attribute__((aligned(16))) bf16_t sK[64 * LD];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[64 * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * TLD];  // fp16
-
-  const int NG = N / G;
-  const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NG * H * B));
-  const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
-  const int k = ht.k[h];
-  const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * k;
-  const size_t bh = (size_t)b * H + h;
-  const bf16_t* Kbh = K + bh * (size_t)N * D;
-  const bf16_t* Vbh = V + bh * (size_t)N * D;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, hh = lane >> 5;
-  const size_t qrow = bh * N + (size_t)g * G + wave * 32 + l32;
-
-  bf16x8 qreg[D / 16], oreg[D / 16];
-  {
-    const bf16_t* qp = Q + qrow * D + 8 * hh;
-    const bf16_t* op = dO + qrow * D + 8 * hh;
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      qreg[t] = *reinterpret_cast<const bf16x8*>(qp + 16 * t);
-      oreg[t] = *reinterpret_cast<const bf16x8*>(op + 16 * t);
-    }
-  }
-  const float lse2 = LSE[qrow] * kLog2e;
-  const float dvec = Dvec[qrow];
-
-  f32x16 acc[D / 32];
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c) acc[c] = f32x16{};
-
-  const int NB = N / kBlock;
-  auto block_id = [&](int t) { return min(max(irow[t], 0), NB - 1); };
-  TileMover<D, NT> mk, mv;
-  {
-    const int j = block_id(0);
-    mk.load(Kbh + (size_t)j * kBlock * D);
-    mv.load(Vbh + (size_t)j * kBlock * D);
-  }
-  for (int t = 0; t < k; ++t) {
-    __syncthreads();
-    mk.store_rows(sK);
-    mk.store_cols_f16(sKt);
-    mv.store_rows(sV);
-    __syncthreads();
-    if (t + 1 < k) {
-      const int j = block_id(t + 1);
-      mk.load(Kbh + (size_t)j * kBlock * D);
-      mv.load(Vbh + (size_t)j * kBlock * D);
-    }
-    // S^T and dP^T: rows = the block's keys (two 32-key tiles), columns = the wave's queries
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x16{};
-      dp[kt] = f32x16{};
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sK[(32 * kt + l32) * LD + 16 * c + 8 * hh]);
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sV[(32 * kt + l32) * LD + 16 * c + 8 * hh]);
-        s[kt] = mfma32(ak, qreg[c], s[kt]);
-        dp[kt] = mfma32(av, oreg[c], dp[kt]);
-      }
-    }
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][e], scale_log2, -lse2));
-        dp[kt][e] = p * (dp[kt][e] - dvec);
-      }
-    // dQ^T[c][i] += K^T[c][m] dS^T[m][i]
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      const f16x8 db = pack_f16(dp[kc >> 1], kc & 1);
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c)
-        acc[c] = mfma32h(lds_pair_b64_h(&sKt[(32 * c + l32) * TLD + 16 * kc + 4 * hh]), db, acc[c]);
-    }
-  }
-
-  float* orow = dQ + qrow * D;
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c)
+    // element e: query 32*qw + 8*(e/4) + 4*hh + e%4
+    const float* nrow = reinterpret_cast<const float*>(cur + 2 * TILE) + 32 * qw + 4 * hh;
+    const float* drow = reinterpret_cast<const float*>(cur + 2 * TILE + 256) + 32 * qw + 4 * hh;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      float4 v = make_float4(acc[c][4 * q4] * tau, acc[c][4 * q4 + 1] * tau, acc[c][4 * q4 + 2] * tau,
-                             acc[c][4 * q4 + 3] * tau);
-      *reinterpret_cast<float4*>(orow + 32 * c + 8 * q4 + 4 * hh) = v;
+      const float4 n4 = *reinterpret_cast<const float4*>(nrow + 8 * q4);
+      const float4 d4 = *reinterpret_cast<const float4*>(drow + 8 * q4);
+      const float nv[4] = {n4.x, n4.y, n4.z, n4.w};
+      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = 4 * q4 + r;
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, nv[r]));
+        s[e] = p;
+        dp[e] = p * (dp[e] - dd[r]);
+      }
     }
+    const f16x8 pa0 = pack_f16(s, 0), pa1 = pack_f16(s, 1);
+    f16x8 dh0, dl0, dh1, dl1;
+    pack_f16_split(dp, 0, dh0, dl0);
+    pack_f16_split(dp, 1, dh1, dl1);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const char* o0 = cur + TILE + tofs[c][0];
+      const char* o1 = cur + TILE + tofs[c][1];
+      dv[c] = mfma32h(pa0, join_f16(lds_read_tr16(o0), lds_read_tr16(o1)), dv[c]);
+      dv[c] = mfma32h(pa1, join_f16(lds_read_tr16(o0 + 16 * RB), lds_read_tr16(o1 + 16 * RB)), dv[c]);
+      const char* q0 = cur + tofs[c][0];
+      const char* q1 = cur + tofs[c][1];
+      const f16x8 qb0 = join_f16(lds_read_tr16(q0), lds_read_tr16(q1));
+      const f16x8 qb1 = join_f16(lds_read_tr16(q0 + 16 * RB), lds_read_tr16(q1 + 16 * RB));
+      dk[c] = mfma32h(dh0, qb0, dk[c]);
+      dk[c] = mfma32h(dl0, qb0, dk[c]);
+      dk[c] = mfma32h(dh1, qb1, dk[c]);
+      dk[c] = mfma32h(dl1, qb1, dk[c]);
+    }
+  };
+
+  if (iters > 0) fetch(0, st0);
+  if (iters > 1) fetch(1, st1);
+  for (int it = 0; it < iters; it += 3) {
+    step(it, st0, st2);
+    if (it + 1 < iters) step(it + 1, st1, st0);
+    if (it + 2 < iters) step(it + 2, st2, st1);
+  }
+
+  // sum the two query halves; accumulator element e: key 8*(e/4) + 4*hh + e%4 of the
+  // wave's 32, column 32*c + l32
+  __syncthreads();
+  float* mb = reinterpret_cast<float*>(kw == 0 ? st0 : st1);
+  if (qw == 1) {
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        mb[(c * 16 + e) * 64 + lane] = dk[c][e];
+        mb[((D / 32) * 16 + c * 16 + e) * 64 + lane] = dv[c][e];
+      }
+  }
+  __syncthreads();
+  if (qw == 0) {
+    const size_t key0 = bh * N + (size_t)j * kBlock + 32 * kw;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const size_t key = key0 + 8 * (e / 4) + 4 * hh + (e % 4);
+        dK[key * D + 32 * c + l32] = (dk[c][e] + mb[(c * 16 + e) * 64 + lane]) * tau;
+        dV[key * D + 32 * c + l32] = dv[c][e] + mb[((D / 32) * 16 + c * 16 + e) * 64 + lane];
+      }
+  }
 }
 
 template <int D>
-hipError_t pre_launch(const Shape& s, const float* O, const bf16_t* dO, float* Dvec, hipStream_t st) {
+hipError_t pre_launch(const Shape& s, const float* O, const bf16_t* dO, const float* LSE, const BwdWork& w,
+                      hipStream_t st) {
   const int64_t rows = (int64_t)s.B * s.H * s.N;
   constexpr int RPB = 256 / (D / 8);
   const int64_t nwg = (rows + RPB - 1) / RPB;
-  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(nwg < 65536 ? nwg : 65536)), dim3(256), 0, st, dO, O, Dvec,
-                     rows);
+  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(nwg < 65536 ? nwg : 65536)), dim3(256), 0, st, dO, O, LSE,
+                     w.Dvec, w.nl2, w.dO16, rows);
   return hipGetLastError();
 }
 
 template <int D, int G>
-hipError_t dkdv_launch(const Shape& s, const bf16_t* Q, const bf16_t* K, const bf16_t* V, const bf16_t* dO,
-                       const float* LSE, const float* Dvec, const int32_t* rev_ptr, const int32_t* rev_idx, float* dK,
+hipError_t dkdv_launch(const Shape& s, const BwdWork& w, const int32_t* rev_ptr, const int32_t* rev_idx, float* dK,
                        float* dV, const HeadTable& ht, hipStream_t st) {
   const float tau = 1.0f / sqrtf((float)D);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3((unsigned)(s.NB * s.H * s.B)), dim3(128), 0, st, Q, K, V, dO, LSE,
-                     Dvec, rev_ptr, rev_idx, dK, dV, ht, s.N, s.H, s.NB, s.B, tau * kLog2e, tau);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3((unsigned)(s.NB * s.H * s.B)), dim3(256), 0, st, w.Q16, w.K16,
+                     w.V16, w.dO16, w.nl2, w.Dvec, rev_ptr, rev_idx, dK, dV, ht, s.N, s.H, s.NB, s.B, tau);
   return hipGetLastError();
 }
 
 template <int D, int G>
-hipError_t dq_launch(const Shape& s, const bf16_t* Q, const bf16_t* K, const bf16_t* V, const bf16_t* dO,
-                     const float* LSE, const float* Dvec, const int32_t* idx, float* dQ, const HeadTable& ht,
+hipError_t dq_launch(const Shape& s, const BwdWork& w, const int32_t* idx, float* dQ, const HeadTable& ht,
                      hipStream_t st) {
   const float tau = 1.0f / sqrtf((float)D);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3((unsigned)(s.NG * s.H * s.B)), dim3(G * 2), 0, st, Q, K, V, dO, LSE,
-                     Dvec, idx, dQ, ht, s.N, s.H, s.B, tau * kLog2e, tau);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3((unsigned)(s.NG * s.H * s.B)), dim3(G * 4), 0, st, w.Q16, w.K16,
+                     w.V16, w.dO16, w.nl2, w.Dvec, idx, dQ, ht, s.N, s.H, s.B, tau * kLog2e, tau);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_pre(const Shape& s, const float* O, const void* dO, float* Dvec, hipStream_t st) {
+hipError_t launch_bwd_pre(const Shape& s, const void* Q, const void* K, const void* V, const float* O,
+                          const void* dO, const float* LSE, const BwdWork& w, hipStream_t st) {
+  const int64_t elems = (int64_t)s.B * s.H * s.N * s.D;
+  hipError_t e = launch_cvt_f16(Q, w.Q16, elems, st);
+  if (e == hipSuccess) e = launch_cvt_f16(K, w.K16, elems, st);
+  if (e == hipSuccess) e = launch_cvt_f16(V, w.V16, elems, st);
+  if (e != hipSuccess) return e;
   const bf16_t* o = static_cast<const bf16_t*>(dO);
-  return s.D == 64 ? pre_launch<64>(s, O, o, Dvec, st) : pre_launch<128>(s, O, o, Dvec, st);
+  return s.D == 64 ? pre_launch<64>(s, O, o, LSE, w, st) : pre_launch<128>(s, O, o, LSE, w, st);
 }
 
-hipError_t launch_bwd_dkdv(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
-                           const float* LSE, const float* Dvec, const int32_t* rev_ptr, const int32_t* rev_idx,
+hipError_t launch_bwd_dkdv(const Shape& s, const BwdWork& w, const int32_t* rev_ptr, const int32_t* rev_idx,
                            float* dK, float* dV, const HeadTable& ht, hipStream_t st) {
-  const bf16_t* q = static_cast<const bf16_t*>(Q);
-  const bf16_t* k = static_cast<const bf16_t*>(K);
-  const bf16_t* v = static_cast<const bf16_t*>(V);
-  const bf16_t* o = static_cast<const bf16_t*>(dO);
   if (s.D == 64)
-    return s.G == 64 ? dkdv_launch<64, 64>(s, q, k, v, o, LSE, Dvec, rev_ptr, rev_idx, dK, dV, ht, st)
-                     : dkdv_launch<64, 128>(s, q, k, v, o, LSE, Dvec, rev_ptr, rev_idx, dK, dV, ht, st);
-  return s.G == 64 ? dkdv_launch<128, 64>(s, q, k, v, o, LSE, Dvec, rev_ptr, rev_idx, dK, dV, ht, st)
-                   : dkdv_launch<128, 128>(s, q, k, v, o, LSE, Dvec, rev_ptr, rev_idx, dK, dV, ht, st);
+    return s.G == 64 ? dkdv_launch<64, 64>(s, w, rev_ptr, rev_idx, dK, dV, ht, st)
+                     : dkdv_launch<64, 128>(s, w, rev_ptr, rev_idx, dK, dV, ht, st);
+  return s.G == 64 ? dkdv_launch<128, 64>(s, w, rev_ptr, rev_idx, dK, dV, ht, st)
+                   : dkdv_launch<128, 128>(s, w, rev_ptr, rev_idx, dK, dV, ht, st);
 }
 
-hipError_t launch_bwd_dq(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
-                         const float* LSE, const float* Dvec, const int32_t* idx, float* dQ, const HeadTable& ht,
+hipError_t launch_bwd_dq(const Shape& s, const BwdWork& w, const int32_t* idx, float* dQ, const HeadTable& ht,
                          hipStream_t st) {
-  const bf16_t* q = static_cast<const bf16_t*>(Q);
-  const bf16_t* k = static_cast<const bf16_t*>(K);
-  const bf16_t* v = static_cast<const bf16_t*>(V);
-  const bf16_t* o = static_cast<const bf16_t*>(dO);
   if (s.D == 64)
-    return s.G == 64 ? dq_launch<64, 64>(s, q, k, v, o, LSE, Dvec, idx, dQ, ht, st)
-                     : dq_launch<64, 128>(s, q, k, v, o, LSE, Dvec, idx, dQ, ht, st);
-  return s.G == 64 ? dq_launch<128, 64>(s, q, k, v, o, LSE, Dvec, idx, dQ, ht, st)
-                   : dq_launch<128, 128>(s, q, k, v, o, LSE, Dvec, idx, dQ, ht, st);
+    return s.G == 64 ? dq_launch<64, 64>(s, w, idx, dQ, ht, st) : dq_launch<64, 128>(s, w, idx, dQ, ht, st);
+  return s.G == 64 ? dq_launch<128, 64>(s, w, idx, dQ, ht, st) : dq_launch<128, 128>(s, w, idx, dQ, ht, st);
 }
 
 }  // namespace dsa

@@ -20,13 +20,6 @@ namespace dsa {
 
 namespace {
 
-// bf16 -> fp16 shadow copy (exact for |x| in [2^-14, 65504]); 8 values per thread step.
-__global__ __launch_bounds__(256) void cvt_bf16_f16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                                           int64_t n16) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
-    dst[i] = bf16x8_to_f16x8(src[i]);
-}
-
 template <int D, int G>
 __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* __restrict__ Q,
                                                                  const bf16_t* __restrict__ K,
@@ -270,10 +263,8 @@ hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* 
   const float scale_log2 = (1.0f / sqrtf((float)D)) * kLog2e;
   dim3 grid((unsigned)(s.NG * s.H * s.B));
   if (s.bf16) {
-    const int64_t n16 = (int64_t)s.B * s.H * s.N * D / 8;
-    const int64_t nwg = (n16 + 255) / 256;
-    hipLaunchKernelGGL(cvt_bf16_f16_kernel, dim3((unsigned)(nwg < 8192 ? nwg : 8192)), dim3(256), 0, st,
-                       static_cast<const uint4*>(V), reinterpret_cast<uint4*>(V16), n16);
+    const hipError_t e = launch_cvt_f16(V, V16, (int64_t)s.B * s.H * s.N * D, st);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, G>), grid, dim3(G * 4), 0, st, static_cast<const bf16_t*>(Q),
                        static_cast<const bf16_t*>(K), V16, idx, O, LSE, ht, s.N, s.H, s.B, scale_log2);
   } else

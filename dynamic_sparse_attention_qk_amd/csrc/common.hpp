@@ -282,6 +282,23 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, char*
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Workgroup barrier for loops whose LDS tiles arrive by DMA: the caller has
+// already waited (vmcnt) for exactly the copies that must be visible; this
+// completes the wave's own LDS reads/writes (lgkmcnt) and synchronises, without
+// the release fence of __syncthreads(), which would also wait for copies
+// still in flight to other stages.  The memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// 4-byte-per-lane DMA of 64 consecutive floats (one wave) into LDS.
+__device__ __forceinline__ void dma_row64_f32(const float* __restrict__ src, char* lds, int lane) {
+  __builtin_amdgcn_global_load_lds(src + lane, (lds_void*)lds, 4, 0, 0);
+}
+
 // Transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane i
 // receives element i%4 of the 8-byte chunks addressed by lanes 4e + i/4 of the
 // group, e = 0..3.  If lane L addresses row (r0 + L/4), columns c0 + 4*(L%4),
@@ -338,6 +355,23 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t n) {
   const uint32_t q = n / kXcds, r = n % kXcds;
   const uint32_t x = w % kXcds, i = w / kXcds;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
+// bf16 -> fp16 shadow copy (exact for |x| in [2^-14, 65504]); 8 values per thread step.
+namespace {
+__global__ __launch_bounds__(256) void cvt_bf16_f16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                           int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    dst[i] = bf16x8_to_f16x8(src[i]);
+}
+}  // namespace
+
+inline hipError_t launch_cvt_f16(const void* src, void* dst, int64_t elems, hipStream_t st) {
+  const int64_t n16 = elems / 8;
+  const int64_t nwg = (n16 + 255) / 256;
+  hipLaunchKernelGGL(cvt_bf16_f16_kernel, dim3((unsigned)(nwg < 8192 ? nwg : 8192)), dim3(256), 0, st,
+                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), n16);
+  return hipGetLastError();
 }
 
 __device__ __forceinline__ float wave_max_pair(float v) {  // max with lane l^32

@@ -26,12 +26,21 @@ hipError_t launch_reverse_index(const Shape& s, const int32_t* idx, int32_t* rev
                                 hipStream_t st);
 hipError_t launch_attn_fwd(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx,
                            float* O, float* LSE, uint16_t* V16, const HeadTable& ht, hipStream_t st);
-hipError_t launch_bwd_pre(const Shape& s, const float* O, const void* dO, float* Dvec, hipStream_t st);
-hipError_t launch_bwd_dkdv(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
-                           const float* LSE, const float* Dvec, const int32_t* rev_ptr, const int32_t* rev_idx,
+// Backward workspace: D, -LSE*log2(e) and exact fp16 copies of Q, K, V, dO.
+struct BwdWork {
+  float* Dvec;
+  float* nl2;
+  uint16_t* Q16;
+  uint16_t* K16;
+  uint16_t* V16;
+  uint16_t* dO16;
+};
+
+hipError_t launch_bwd_pre(const Shape& s, const void* Q, const void* K, const void* V, const float* O,
+                          const void* dO, const float* LSE, const BwdWork& w, hipStream_t st);
+hipError_t launch_bwd_dkdv(const Shape& s, const BwdWork& w, const int32_t* rev_ptr, const int32_t* rev_idx,
                            float* dK, float* dV, const HeadTable& ht, hipStream_t st);
-hipError_t launch_bwd_dq(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
-                         const float* LSE, const float* Dvec, const int32_t* idx, float* dQ, const HeadTable& ht,
+hipError_t launch_bwd_dq(const Shape& s, const BwdWork& w, const int32_t* idx, float* dQ, const HeadTable& ht,
                          hipStream_t st);
 
 }  // namespace dsa

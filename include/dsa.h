@@ -152,20 +152,22 @@ int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, cons
                         void* stream);
 
 /*
- * The three stages dsa_sparse_attn_bwd runs, exposed one launch each (same
- * arguments and rules as above; Dvec is [B,H,N] fp32, D_i = dO_i . O_i):
- *   dsa_sparse_attn_bwd_preprocess  Dvec from O and dO;
+ * The three stages dsa_sparse_attn_bwd runs, exposed one launch group each,
+ * sharing the DSA_WS_BWD workspace (D_i = dO_i . O_i, -LSE*log2(e) and exact
+ * fp16 copies of Q, K, V, dO, written by the preprocess stage):
+ *   dsa_sparse_attn_bwd_preprocess  fills the workspace from Q, K, V, O, dO, LSE;
  *   dsa_sparse_attn_bwd_dkdv        dK, dV from the reverse index (every key
  *                                   row of every block is written);
  *   dsa_sparse_attn_bwd_dq          dQ from the kept-block lists.
  */
-int dsa_sparse_attn_bwd_preprocess(const dsa_problem* p, const float* O, const void* dO, float* Dvec, void* stream);
-int dsa_sparse_attn_bwd_dkdv(const dsa_problem* p, const void* Q, const void* K, const void* V, const void* dO,
-                             const float* LSE, const float* Dvec, const int32_t* k_per_head, const int32_t* rev_ptr,
-                             const int32_t* rev_idx, float* dK, float* dV, void* stream);
-int dsa_sparse_attn_bwd_dq(const dsa_problem* p, const void* Q, const void* K, const void* V, const void* dO,
-                           const float* LSE, const float* Dvec, const int32_t* idx, const int32_t* k_per_head,
-                           float* dQ, void* stream);
+int dsa_sparse_attn_bwd_preprocess(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
+                                   const void* dO, const float* LSE, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+int dsa_sparse_attn_bwd_dkdv(const dsa_problem* p, const int32_t* k_per_head, const int32_t* rev_ptr,
+                             const int32_t* rev_idx, float* dK, float* dV, void* workspace, size_t workspace_bytes,
+                             void* stream);
+int dsa_sparse_attn_bwd_dq(const dsa_problem* p, const int32_t* idx, const int32_t* k_per_head, float* dQ,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

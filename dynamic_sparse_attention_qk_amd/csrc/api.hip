@@ -3,7 +3,7 @@
 #include <math.h>
 #include <string.h>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 #include "launch.hpp"
 
 using dsa::HeadTable;

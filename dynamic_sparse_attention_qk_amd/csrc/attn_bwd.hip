@@ -15,9 +15,9 @@
 // bwd_dq: one workgroup per (b, h, group) over the group's kept blocks; waves
 // = 32-row tile x key half, partial dQ of the two halves summed at the end.
 // bwd_dkdv: one workgroup per (b, h, KV block) over the block's reverse list;
-// waves = key half x 32-query half of each 64-row tile, dK/dV in registers,
-// partials of the two query halves summed at the end.  dK's dS operand is
-// split hi + lo in fp16 (dK sums a cancelling dS against clustered Q rows).
+// each wave owns 16 keys and every query row, dK/dV in registers.  dK's dS
+// operand is split hi + lo in fp16 (dK sums a cancelling dS against clustered
+// Q rows).
 #include "launch.hpp"
 
 namespace dsa {
@@ -178,9 +178,34 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------- dK, dV
+//
+// Wave w owns keys 16w..16w+15 of the block and all 64 query rows of each
+// tile, on 16x16x32 MFMAs: its dK and dV accumulators are 16 x D each (2*D/16
+// registers per lane), small enough for two waves per SIMD.
+
+__device__ __forceinline__ f16x8 join4_f16(const f32x4& a, const f32x4& b) {
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (_Float16)a[e];
+    r[4 + e] = (_Float16)b[e];
+  }
+  return r;
+}
+
+__device__ __forceinline__ void join4_f16_split(const f32x4& a, const f32x4& b, f16x8& hi, f16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const _Float16 ha = (_Float16)a[e], hb = (_Float16)b[e];
+    hi[e] = ha;
+    hi[4 + e] = hb;
+    lo[e] = (_Float16)(a[e] - (float)ha);
+    lo[4 + e] = (_Float16)(b[e] - (float)hb);
+  }
+}
 
 template <int D, int G>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q16,
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q16,
                                                           const uint16_t* __restrict__ K16,
                                                           const uint16_t* __restrict__ V16,
                                                           const uint16_t* __restrict__ dO16,
@@ -195,12 +220,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
   constexpr int TILE = 64 * RB;
   constexpr int STAGE = 2 * TILE + 512;  // Q16 tile, dO16 tile, -LSE*log2e row, D row
   constexpr int SUB = G / 64;            // 64-row query tiles per group
-  constexpr int NDMA = 2 * (D / 8) / NW + 1;  // copies one wave issues per fetch
-  constexpr int OBUF = D * 256;          // one wave's dK + dV partial: 64 lanes x D floats
+  constexpr int NS = D / 32;             // 32-wide steps of the head dimension
+  constexpr int NC = D / 16;             // 16-wide column tiles of dK, dV
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
-  __shared__ __attribute__((aligned(1024))) char st2[STAGE];
-  static_assert(OBUF <= STAGE, "merge buffers must fit in the stages");
   const float scale_log2 = tau * kLog2e;
 
   const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NB * H * B));
@@ -208,131 +231,109 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(const uint16_t* __rest
   const int NG = N / G;
   const size_t bh = (size_t)b * H + h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int kw = wave & 1, qw = wave >> 1;  // keys 32*kw.., queries 32*qw.. of each 64-row tile
+  const int l16 = lane & 15, q4 = lane >> 4;
   const int32_t* rp = rev_ptr + bh * (NB + 1);
   const int32_t total = NG * ht.k[h];  // size of the (b, h) region of the reverse list
   const int32_t s0 = min(max(rp[j], 0), total), s1 = min(max(rp[j + 1], s0), total);
   const int32_t* rlist = rev_idx + row_base(ht, b, h, NG) + s0;
   const int iters = (s1 - s0) * SUB;
 
-  // this wave's 32 keys as B operands: K for S = Q K^T, V for dP = dO V^T
-  f16x8 kreg[D / 16], vreg[D / 16];
+  // this wave's 16 keys as B operands: K for S = Q K^T, V for dP = dO V^T
+  f16x8 kreg[NS], vreg[NS];
   {
-    const size_t key = bh * N + (size_t)j * kBlock + 32 * kw + l32;
+    const size_t key = bh * N + (size_t)j * kBlock + 16 * wave + l16;
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      kreg[t] = ldg_f16x8(K16 + key * D + 16 * t + 8 * hh);
-      vreg[t] = ldg_f16x8(V16 + key * D + 16 * t + 8 * hh);
+    for (int t = 0; t < NS; ++t) {
+      kreg[t] = ldg_f16x8(K16 + key * D + 32 * t + 8 * q4);
+      vreg[t] = ldg_f16x8(V16 + key * D + 32 * t + 8 * q4);
     }
   }
-  int aofs[D / 16];  // Q and dO rows of this query half as A operands
+  // A operands: query row 16*rb + l16, logical chunk 4*t + q4 (same swizzle for every rb)
+  int aofs[NS];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) aofs[c] = tile_off<D>(32 * qw + l32, 2 * c + hh);
-  const int li = lane & 15, g16 = lane >> 4;
-  const int rl = 4 * hh + (li >> 2);
-  int tofs[D / 32][2];  // transpose reads of dO and Q (B operands of dV and dK)
+  for (int t = 0; t < NS; ++t) aofs[t] = tile_off<D>(l16, 4 * t + q4);
+  // transpose reads (B operands of dV, dK): rows 32*kc + 4*q4 + l16/4 (+16), columns 16*c + 4*(l16%4)
+  int tofs[NC];
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-      tofs[c][r] = tile_off<D>(32 * qw + 8 * r + rl, 4 * c + 2 * (g16 & 1) + ((li & 3) >> 1)) + 8 * (li & 1);
+  for (int c = 0; c < NC; ++c) tofs[c] = tile_off<D>(4 * q4 + (l16 >> 2), 2 * c + ((l16 & 3) >> 1)) + 8 * (l16 & 1);
 
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x4 dk[NC], dv[NC];
 #pragma unroll
-  for (int c = 0; c < D / 32; ++c) { dk[c] = f32x16{}; dv[c] = f32x16{}; }
+  for (int c = 0; c < NC; ++c) { dk[c] = f32x4{}; dv[c] = f32x4{}; }
 
-  // every wave issues NDMA copies per fetch (the two row copies go to odd/even waves)
   auto fetch = [&](int it, char* dst) {
     const int g = min(max(rlist[it / SUB], 0), NG - 1);  // valid by contract; never read out of bounds
     const size_t row0 = bh * N + (size_t)g * G + (size_t)(it % SUB) * 64;
     dma_tile<D, NW>(Q16 + row0 * D, dst, wave, lane);
     dma_tile<D, NW>(dO16 + row0 * D, dst + TILE, wave, lane);
-    if (wave & 1) dma_row64_f32(Dvec + row0, dst + 2 * TILE + 256, lane);
-    else dma_row64_f32(NL2 + row0, dst + 2 * TILE, lane);
+    if (wave == 0) dma_row64_f32(NL2 + row0, dst + 2 * TILE, lane);
+    if (wave == 1) dma_row64_f32(Dvec + row0, dst + 2 * TILE + 256, lane);
   };
-  auto step = [&](int it, const char* cur, char* nxt2) {
-    if (it + 1 < iters) wait_vmem_le<NDMA>(); else wait_vmem();  // this tile has landed, the next may still fly
-    wg_barrier();  // tile it is visible and every wave is done with tile it-1
-    if (it + 2 < iters) fetch(it + 2, nxt2);
-    // S[i][m], dP[i][m]: rows = the wave's 32 queries, columns = its 32 keys
-    f32x16 s = f32x16{}, dp = f32x16{};
+  auto step = [&](int it, const char* cur, char* nxt) {
+    wait_vmem();
+    __syncthreads();  // tile it is in LDS and every wave is done with tile it-1
+    if (it + 1 < iters) fetch(it + 1, nxt);
+    // S[i][m], dP[i][m] for the 64 queries (4 row blocks) x this wave's 16 keys;
+    // element e of row block rb: query 16*rb + 4*q4 + e
+    f32x4 s[4], dp[4];
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      s = mfma32h(*reinterpret_cast<const f16x8*>(cur + aofs[c]), kreg[c], s);
-      dp = mfma32h(*reinterpret_cast<const f16x8*>(cur + TILE + aofs[c]), vreg[c], dp);
-    }
-    // element e: query 32*qw + 8*(e/4) + 4*hh + e%4
-    const float* nrow = reinterpret_cast<const float*>(cur + 2 * TILE) + 32 * qw + 4 * hh;
-    const float* drow = reinterpret_cast<const float*>(cur + 2 * TILE + 256) + 32 * qw + 4 * hh;
+    for (int rb = 0; rb < 4; ++rb) {
+      s[rb] = f32x4{};
+      dp[rb] = f32x4{};
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const float4 n4 = *reinterpret_cast<const float4*>(nrow + 8 * q4);
-      const float4 d4 = *reinterpret_cast<const float4*>(drow + 8 * q4);
-      const float nv[4] = {n4.x, n4.y, n4.z, n4.w};
-      const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = 4 * q4 + r;
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, nv[r]));
-        s[e] = p;
-        dp[e] = p * (dp[e] - dd[r]);
+      for (int t = 0; t < NS; ++t) {
+        s[rb] = mfma16h(*reinterpret_cast<const f16x8*>(cur + 16 * rb * RB + aofs[t]), kreg[t], s[rb]);
+        dp[rb] = mfma16h(*reinterpret_cast<const f16x8*>(cur + TILE + 16 * rb * RB + aofs[t]), vreg[t], dp[rb]);
       }
     }
-    const f16x8 pa0 = pack_f16(s, 0), pa1 = pack_f16(s, 1);
-    f16x8 dh0, dl0, dh1, dl1;
-    pack_f16_split(dp, 0, dh0, dl0);
-    pack_f16_split(dp, 1, dh1, dl1);
+    const float* nrow = reinterpret_cast<const float*>(cur + 2 * TILE) + 4 * q4;
+    const float* drow = reinterpret_cast<const float*>(cur + 2 * TILE + 256) + 4 * q4;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      const char* o0 = cur + TILE + tofs[c][0];
-      const char* o1 = cur + TILE + tofs[c][1];
-      dv[c] = mfma32h(pa0, join_f16(lds_read_tr16(o0), lds_read_tr16(o1)), dv[c]);
-      dv[c] = mfma32h(pa1, join_f16(lds_read_tr16(o0 + 16 * RB), lds_read_tr16(o1 + 16 * RB)), dv[c]);
-      const char* q0 = cur + tofs[c][0];
-      const char* q1 = cur + tofs[c][1];
-      const f16x8 qb0 = join_f16(lds_read_tr16(q0), lds_read_tr16(q1));
-      const f16x8 qb1 = join_f16(lds_read_tr16(q0 + 16 * RB), lds_read_tr16(q1 + 16 * RB));
-      dk[c] = mfma32h(dh0, qb0, dk[c]);
-      dk[c] = mfma32h(dl0, qb0, dk[c]);
-      dk[c] = mfma32h(dh1, qb1, dk[c]);
-      dk[c] = mfma32h(dl1, qb1, dk[c]);
+    for (int rb = 0; rb < 4; ++rb) {
+      const f32x4 n4 = *reinterpret_cast<const f32x4*>(nrow + 16 * rb);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(drow + 16 * rb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][e], scale_log2, n4[e]));
+        s[rb][e] = p;
+        dp[rb][e] = p * (dp[rb][e] - d4[e]);
+      }
+    }
+    // A operands over 32-query chunks kc: element e' <-> query 32*kc + 16*(e'/4) + 4*q4 + e'%4
+    const f16x8 pa0 = join4_f16(s[0], s[1]), pa1 = join4_f16(s[2], s[3]);
+    f16x8 dh0, dl0, dh1, dl1;
+    join4_f16_split(dp[0], dp[1], dh0, dl0);
+    join4_f16_split(dp[2], dp[3], dh1, dl1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const char* o = cur + TILE + tofs[c];
+      dv[c] = mfma16h(pa0, join_f16(lds_read_tr16(o), lds_read_tr16(o + 16 * RB)), dv[c]);
+      dv[c] = mfma16h(pa1, join_f16(lds_read_tr16(o + 32 * RB), lds_read_tr16(o + 48 * RB)), dv[c]);
+      const char* q = cur + tofs[c];
+      const f16x8 qb0 = join_f16(lds_read_tr16(q), lds_read_tr16(q + 16 * RB));
+      const f16x8 qb1 = join_f16(lds_read_tr16(q + 32 * RB), lds_read_tr16(q + 48 * RB));
+      dk[c] = mfma16h(dh0, qb0, dk[c]);
+      dk[c] = mfma16h(dl0, qb0, dk[c]);
+      dk[c] = mfma16h(dh1, qb1, dk[c]);
+      dk[c] = mfma16h(dl1, qb1, dk[c]);
     }
   };
 
   if (iters > 0) fetch(0, st0);
-  if (iters > 1) fetch(1, st1);
-  for (int it = 0; it < iters; it += 3) {
-    step(it, st0, st2);
+  for (int it = 0; it < iters; it += 2) {
+    step(it, st0, st1);
     if (it + 1 < iters) step(it + 1, st1, st0);
-    if (it + 2 < iters) step(it + 2, st2, st1);
   }
 
-  // sum the two query halves; accumulator element e: key 8*(e/4) + 4*hh + e%4 of the
-  // wave's 32, column 32*c + l32
-  __syncthreads();
-  float* mb = reinterpret_cast<float*>(kw == 0 ? st0 : st1);
-  if (qw == 1) {
+  // accumulator element e of column tile c: key 16*wave + 4*q4 + e, column 16*c + l16
+  const size_t key0 = bh * N + (size_t)j * kBlock + 16 * wave + 4 * q4;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c)
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        mb[(c * 16 + e) * 64 + lane] = dk[c][e];
-        mb[((D / 32) * 16 + c * 16 + e) * 64 + lane] = dv[c][e];
-      }
-  }
-  __syncthreads();
-  if (qw == 0) {
-    const size_t key0 = bh * N + (size_t)j * kBlock + 32 * kw;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const size_t key = key0 + 8 * (e / 4) + 4 * hh + (e % 4);
-        dK[key * D + 32 * c + l32] = (dk[c][e] + mb[(c * 16 + e) * 64 + lane]) * tau;
-        dV[key * D + 32 * c + l32] = dv[c][e] + mb[((D / 32) * 16 + c * 16 + e) * 64 + lane];
-      }
-  }
+    for (int e = 0; e < 4; ++e) {
+      dK[(key0 + e) * D + 16 * c + l16] = dk[c][e] * tau;
+      dV[(key0 + e) * D + 16 * c + l16] = dv[c][e];
+    }
 }
 
 template <int D>

@@ -81,6 +81,12 @@ __device__ __forceinline__ f32x16 mfma32h(const f16x8& a, const f16x8& b, const 
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x32 fp16: lane l supplies A[l%16][8*(l/16) + e] and B[8*(l/16) + e][l%16],
+// e = 0..7, and receives D[4*(l/16) + e][l%16], e = 0..3.
+__device__ __forceinline__ f32x4 mfma16h(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x16 mfma32_f32(float a, float b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
@@ -240,21 +246,28 @@ struct TileMover {
 // A 64 x D 16-bit tile is stored row-major without padding (row = 2*D bytes)
 // with its 16-byte chunks XOR-swizzled per row: physical chunk p of row r holds
 // logical chunk p ^ tile_swz<D>(r).  gfx950's LDS serves 64 banks (256 bytes)
-// per cycle; the swizzle makes
-//   - 16 consecutive rows read at one logical chunk (a 128-bit row read of 16
-//     lanes) fall on 16 distinct 16-byte bank groups, and
-//   - any 8-row x 4-chunk window at a 4-aligned chunk (one transpose read of a
-//     wave) cover every bank group exactly twice.
+// per cycle; the swizzle puts each hardware pass of every access pattern of
+// the kernels on distinct 16-byte bank groups:
+//   - 8 or 16 consecutive rows read at one logical chunk (128-bit reads),
+//   - 4 consecutive rows x 4 chunks, 4 rows x 2 chunks and 8 rows x 2 chunks
+//     at aligned positions (the lane groups of transpose reads feeding 32x32
+//     and 16x16 MFMAs).
+// For D = 128 (256-byte rows) the row bits r3 r2 r1 r0 map to r1 r0 (r2^r3) r2,
+// the one map among those measured with no conflict in any of the four
+// patterns (the plain reordering r1 r0 r2 r3 costs the 16x16 operand reads of
+// the dK/dV kernel one extra pass in two); for D = 64 two rows share a
+// 256-byte window, r0 picks the half, and the 3-bit chunk map is r1 (r2^r3) r2.
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 __device__ __forceinline__ int tile_swz(int r) {
   if constexpr (D == 128) {
-    return ((r & 3) << 2) | ((r >> 2) & 3);
-  } else {  // D == 64: two rows share a 256-byte bank window
-    const int x = (r >> 1) & 7;
-    return ((x & 1) << 2) | (x >> 1);
+    const int r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+    return ((r & 3) << 2) | ((r2 ^ r3) << 1) | r2;
+  } else {
+    const int r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+    return (r1 << 2) | ((r2 ^ r3) << 1) | r2;
   }
 }
 

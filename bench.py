@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=3, help="workload id 1..5 (3 is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
 
 
@@ -89,6 +91,38 @@ def cpu_baseline(inp, target_s: float):
             "tokens_per_s": groups_done * G / elapsed}
 
 
+KERNEL_SOURCES = ("dynamic_sparse_attention_qk_amd/csrc/attn_fwd.hip", "dynamic_sparse_attention_qk_amd/csrc/attn_bwd.hip",
+                  "dynamic_sparse_attention_qk_amd/csrc/common.hpp", "dynamic_sparse_attention_qk_amd/csrc/launch.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernels_bf16_57k_tokens_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources the attention kernels are compiled from; a stored
+    traffic figure is used only while this still matches."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (lines 'TRAFFIC kernel=... workload=... source_sha256=...
+    fetch_bytes=... write_bytes=...'), or None when absent or stale."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    cur = kernel_source_hash()
+    for line in open(TRAFFIC_FILE):
+        if not line.startswith("TRAFFIC "):
+            continue
+        kv = dict(item.split("=", 1) for item in line.split()[1:])
+        if kv.get("kernel") == kernel and kv.get("workload") == workload and kv.get("source_sha256") == cur:
+            return int(float(kv["fetch_bytes"]) + float(kv["write_bytes"]))
+    return None
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -106,6 +140,20 @@ def main():
     print(f"# generated {w.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream(device=dev)          # every launch and every event of the step is on this stream
+    if args.copy_probe_mib:
+        # one elementwise kernel that reads n bytes and writes n bytes (a copy with
+        # the bits inverted; a same-type copy_ would go to the DMA engines and
+        # never show in the shader counters): the reference point that scales the
+        # FETCH_SIZE / WRITE_SIZE counters of a --pmc run to bytes
+        n = args.copy_probe_mib << 20
+        src = torch.full((n // 4,), 7, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     p = problem_of(w)
     kph = [int(x) for x in inp.k_per_head]
     backward = w.backward
@@ -115,13 +163,32 @@ def main():
     Q, K, V = (to_device(getattr(inp, n)) for n in ("q", "k", "v"))
     Wt = to_device(inp.w)
     dO = to_device(inp.do) if backward else None
+    torch.cuda.synchronize()
 
-    def step():
-        plan.step(Q, K, V, Wt, Wt, dO)
+    names = ["predict", "select", "fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if backward else [])
+
+    def step(marks=None):
+        """One pass of the hot path, stage by stage (the backward as its three
+        single-kernel stages, the same launches sparse_attn_bwd makes)."""
+        rec = (lambda i: marks[i].record(stream)) if marks is not None else (lambda i: None)
+        rec(0)
+        plan.predict(Q, K, Wt, Wt, stream)
+        rec(1)
+        plan.select(stream)
+        rec(2)
+        plan.forward(Q, K, V, stream)
+        rec(3)
+        if backward:
+            dsa.sparse_attn_bwd_preprocess(p, Q, K, V, plan.O, dO, plan.LSE, plan.ws_bwd, stream)
+            rec(4)
+            dsa.sparse_attn_bwd_dkdv(p, kph, plan.rev_ptr, plan.rev_idx, plan.dK, plan.dV, plan.ws_bwd, stream)
+            rec(5)
+            dsa.sparse_attn_bwd_dq(p, plan.idx, kph, plan.dQ, plan.ws_bwd, stream)
+            rec(6)
 
     # first pass checked on the host: every kept-block id in range before the attention kernels read them
-    plan.predict(Q, K, Wt, Wt)
-    plan.select()
+    plan.predict(Q, K, Wt, Wt, stream)
+    plan.select(stream)
     torch.cuda.synchronize()
     idx_host = plan.idx[: int(plan.row_base[-1])].cpu().numpy()
     assert idx_host.min() >= 0 and idx_host.max() < p.n_blocks, "kept-block list out of range"
@@ -129,38 +196,17 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    end.record()
+    start.record(stream)
+    for i in range(args.steps):
+        step(marks[i])
+    end.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
-
-    # per-stage times (separate pass; the backward as its three single-launch stages)
-    names = ["predict", "select", "fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if backward else [])
-    ev = {n: [] for n in names}
-    for _ in range(max(3, args.steps // 2)):
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-        marks[0].record()
-        plan.predict(Q, K, Wt, Wt)
-        marks[1].record()
-        plan.select()
-        marks[2].record()
-        plan.forward(Q, K, V)
-        marks[3].record()
-        if backward:
-            dsa.sparse_attn_bwd_preprocess(p, Q, K, V, plan.O, dO, plan.LSE, plan.ws_bwd)
-            marks[4].record()
-            dsa.sparse_attn_bwd_dkdv(p, kph, plan.rev_ptr, plan.rev_idx, plan.dK, plan.dV, plan.ws_bwd)
-            marks[5].record()
-            dsa.sparse_attn_bwd_dq(p, plan.idx, kph, plan.dQ, plan.ws_bwd)
-            marks[6].record()
-        torch.cuda.synchronize()
-        for i, n in enumerate(names):
-            ev[n].append(marks[i].elapsed_time(marks[i + 1]))
-    stage_ms = {n: float(np.median(v)) for n, v in ev.items()}
+    # per-kernel durations from the events recorded between the launches of the timed steps
+    stage_ms = {n: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in marks])) for i, n in enumerate(names)}
 
     pairs = kept_pairs(w, kph)
     unit = 64 * w.group * w.head_dim            # G x Bk x d per kept (group, block) pair
@@ -170,6 +216,7 @@ def main():
     tflops = (f_fwd + f_bwd) / step_s / 1e12
     attn_ms = stage_ms["fwd"] + sum(stage_ms.get(n, 0.0) for n in ("bwd_pre", "bwd_dkdv", "bwd_dq"))
     kernel_flops = {"fwd": 4.0 * unit * pairs, "bwd_dkdv": 8.0 * unit * pairs, "bwd_dq": 6.0 * unit * pairs}
+    kernel_names = {"fwd": "attn_fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel"}
     cand = [n for n in ("fwd", "bwd_dkdv", "bwd_dq") if n in stage_ms]
     dom = max(cand, key=lambda n: stage_ms[n])
     dom_tflops = kernel_flops[dom] / (stage_ms[dom] / 1e3) / 1e12
@@ -177,6 +224,7 @@ def main():
     elt = 2 if w.dtype == "bf16" else 4
     pred_bytes = 2 * w.batch * w.heads * w.seq_len * w.head_dim * elt + \
         (w.batch * w.heads * w.n_groups * w.n_blocks * 4 if not w.streamed else 0)
+    traffic = stored_traffic(kernel_names[dom], w.name) if w.dtype == "bf16" else None
     rec = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -199,8 +247,9 @@ def main():
         "counted_tflop_per_step": round((f_fwd + f_bwd) / 1e12, 4),
         "stage_ms": {n: round(v, 4) for n, v in stage_ms.items()},
         "predict_hbm_gbs": round(pred_bytes / (stage_ms["predict"] / 1e3) / 1e9, 1),
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(dom_tflops, 2), "peak": peak / 1e12,
-                     "unit": "TFLOP/s", "frac": round(dom_tflops * 1e12 / peak, 4), "traffic": None},
+        "roofline": {"kernel": kernel_names[dom], "bound": "mfma", "achieved": round(dom_tflops, 2),
+                     "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(dom_tflops * 1e12 / peak, 4),
+                     "traffic": traffic},
     }
     if not args.no_cpu_baseline:
         cb = cpu_baseline(inp, args.cpu_seconds)

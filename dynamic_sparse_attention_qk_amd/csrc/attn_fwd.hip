@@ -33,12 +33,15 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
   constexpr int RB = 2 * D;                    // bytes per tile row
   constexpr int TILE = 64 * RB;                // one 64 x D 16-bit tile
   constexpr int OBUF = D * 128;                // one row tile's O partial: 64 lanes x D/2 floats
-  // two stages (K bf16 + V fp16 each), separate objects so the compiler can see
-  // that reads of one stage never alias the DMA filling the other
-  __shared__ __attribute__((aligned(1024))) char st0[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) char st1[2 * TILE];
+  static_assert(OBUF == TILE && NRT <= 4, "merge buffers reuse the four tiles");
+  // K ring and V ring of two tiles each, separate objects so the compiler can
+  // see that reading one never aliases the DMA filling another.  Block t's K
+  // sits in kb[t % 2], its V in vb[t % 2]; K runs one block ahead of V.
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILE];
   __shared__ float sml[NRT][2][64];            // m and l of the key-half-1 waves
-  static_assert(NRT * OBUF <= 4 * TILE, "merge buffers must fit in the stages");
 
   const int NG = N / G;
   const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NG * H * B));
@@ -49,7 +52,8 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
   const size_t bh = (size_t)b * H + h;
   const bf16_t* Kbh = K + bh * (size_t)N * D;
   const uint16_t* Vbh = V16 + bh * (size_t)N * D;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int rt = wave % NRT, kh = wave / NRT;  // rows 32*rt.., keys 32*kh.. of every block
   const int qrow = g * G + rt * 32 + l32;
@@ -75,29 +79,35 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
   for (int c = 0; c < D / 32; ++c)
 #pragma unroll
     for (int r = 0; r < 2; ++r)
-      vofs[c][r] = TILE + tile_off<D>(32 * kh + 8 * r + rl, 4 * c + 2 * (g16 & 1) + ((li & 3) >> 1)) + 8 * (li & 1);
+      vofs[c][r] = tile_off<D>(32 * kh + 8 * r + rl, 4 * c + 2 * (g16 & 1) + ((li & 3) >> 1)) + 8 * (li & 1);
 
   float m_used = -INFINITY, l_run = 0.f;
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) oacc[c] = f32x16{};
 
-  auto fetch = [&](int t, char* dst) {
-    const int j = block_id(t);
-    dma_tile<D, NW>(Kbh + (size_t)j * kBlock * D, dst, wave, lane);
-    dma_tile<D, NW>(Vbh + (size_t)j * kBlock * D, dst + TILE, wave, lane);
+  auto fetch_k = [&](int t, char* dst) { dma_tile<D, NW>(Kbh + (size_t)block_id(t) * kBlock * D, dst, wave, lane); };
+  auto fetch_v = [&](int t, char* dst) { dma_tile<D, NW>(Vbh + (size_t)block_id(t) * kBlock * D, dst, wave, lane); };
+  // S^T of one block: element e is key 32*kh + 8*(e/4) + 4*hh + e%4 of the block, query row l32
+  auto s_tile = [&](const char* kt) {
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) acc = mfma32(*reinterpret_cast<const bf16x8*>(kt + kofs[c]), qreg[c], acc);
+    return acc;
   };
-  auto step = [&](int t, const char* cur, char* nxt) {
+  // Block t: softmax of its scores sc and O += P V, with the next block's scores
+  // sn = K_{t+1} Q^T issued in between, so the matrix cores work on block t+1
+  // while the vector ALUs exponentiate block t.  At entry K_{t+1} and V_t are
+  // in flight into kn and vc; K_t's and V_{t-1}'s buffers (kfree, vfree) take
+  // K_{t+2} and V_{t+1}.
+  auto step = [&](int t, const f32x16& sc, f32x16& sn, const char* kn, const char* vc, char* kfree, char* vfree) {
     wait_vmem();
-    __syncthreads();  // block t is in LDS and every wave is done with block t-1
-    if (t + 1 < k) fetch(t + 1, nxt);
-    f32x16 sacc = f32x16{};  // element e: key 32*kh + 8*(e/4) + 4*hh + e%4, query row l32
+    __syncthreads();  // K_{t+1}, V_t in LDS; every wave is done with K_t and V_{t-1}
+    if (t + 2 < k) fetch_k(t + 2, kfree);
+    if (t + 1 < k) fetch_v(t + 1, vfree);
+    float bm = sc[0];
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c)
-      sacc = mfma32(*reinterpret_cast<const bf16x8*>(cur + kofs[c]), qreg[c], sacc);
-    float bm = sacc[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) bm = fmaxf(bm, sacc[e]);
+    for (int e = 1; e < 16; ++e) bm = fmaxf(bm, sc[e]);
     bm = wave_max_pair(bm) * scale_log2;
     // lazy rescale: keep the running max unless the block exceeds it by 2^8
     if (__ballot(bm > m_used + 8.0f)) {
@@ -108,31 +118,40 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
       for (int c = 0; c < D / 32; ++c) oacc[c] *= alpha;
       m_used = m_new;
     }
+    // the next block's scores (after the last block this reads a stale buffer; the result is unused)
+    sn = s_tile(kn);
+    f16x8 p[2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      sacc[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], scale_log2, -m_used));
-      l_run += sacc[e];
-    }
-    const f16x8 p0 = pack_f16(sacc, 0), p1 = pack_f16(sacc, 1);
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        p[hf][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * hf + e], scale_log2, -m_used));
+    // row sum of the rounded weights that enter P V
+    l_run = sum_f16x8(p[1], sum_f16x8(p[0], l_run));
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
-      const char* v0 = cur + vofs[c][0];
-      const char* v1 = cur + vofs[c][1];
-      oacc[c] = mfma32h(join_f16(lds_read_tr16(v0), lds_read_tr16(v1)), p0, oacc[c]);
-      oacc[c] = mfma32h(join_f16(lds_read_tr16(v0 + 16 * RB), lds_read_tr16(v1 + 16 * RB)), p1, oacc[c]);
+      const char* v0 = vc + vofs[c][0];
+      const char* v1 = vc + vofs[c][1];
+      oacc[c] = mfma32h(join_f16(lds_read_tr16(v0), lds_read_tr16(v1)), p[0], oacc[c]);
+      oacc[c] = mfma32h(join_f16(lds_read_tr16(v0 + 16 * RB), lds_read_tr16(v1 + 16 * RB)), p[1], oacc[c]);
     }
   };
 
-  fetch(0, st0);
+  fetch_k(0, kb0);
+  fetch_v(0, vb0);
+  if (k > 1) fetch_k(1, kb1);
+  wait_vmem();
+  __syncthreads();
+  f32x16 sa = s_tile(kb0), sb;
   for (int t = 0; t < k; t += 2) {
-    step(t, st0, st1);
-    if (t + 1 < k) step(t + 1, st1, st0);
+    step(t, sa, sb, kb1, vb0, kb0, vb1);
+    if (t + 1 < k) step(t + 1, sb, sa, kb0, vb1, kb1, vb0);
   }
 
-  // merge the two key halves of each row tile (O partials parked in the stage buffers)
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // merge the two key halves of each row tile (O partials parked in the ring buffers)
+  const float l_tot = wave_sum_pair(l_run);
   __syncthreads();
-  float* mb = reinterpret_cast<float*>((rt < 2 ? st0 : st1) + (rt & 1) * OBUF);
+  float* mb = reinterpret_cast<float*>(rt == 0 ? kb0 : rt == 1 ? kb1 : rt == 2 ? vb0 : vb1);
   if (kh == 1) {
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)

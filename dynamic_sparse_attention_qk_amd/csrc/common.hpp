@@ -283,10 +283,12 @@ template <int D, int NW>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, char* lds_base, int wave, int lane) {
   constexpr int RB = 2 * D;            // bytes per row
   constexpr int RPI = 1024 / RB;       // rows per 1 KB copy
+  static_assert((D / 8) % NW == 0, "each wave issues the same number of copies");
   const int rin = (lane * 16) / RB;    // row within the copy
   const int p = ((lane * 16) % RB) / 16;
 #pragma unroll
-  for (int j = wave; j < D / 8; j += NW) {
+  for (int i = 0; i < D / 8 / NW; ++i) {
+    const int j = wave + i * NW;
     const int r = j * RPI + rin;
     const uint16_t* g = src + (size_t)r * D + 8 * (p ^ tile_swz<D>(r));
     __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_base + j * 1024), 16, 0, 0);
@@ -387,8 +389,23 @@ inline hipError_t launch_cvt_f16(const void* src, void* dst, int64_t elems, hipS
   return hipGetLastError();
 }
 
-__device__ __forceinline__ float wave_max_pair(float v) {  // max with lane l^32
-  return fmaxf(v, __shfl_xor(v, 32));
+// Max / sum of v over the lane pair (l, l ^ 32), by v_permlane32_swap (no LDS
+// round trip): the two results of the swap hold v of both lanes of the pair.
+__device__ __forceinline__ float wave_max_pair(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_sum_pair(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum of the 8 fp16 values of x, accumulated in fp32 onto acc (v_dot2 with ones).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float sum_f16x8(const f16x8& x, float acc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(f16x2{x[2 * i], x[2 * i + 1]}, f16x2{1, 1}, acc, false);
+  return acc;
 }
 
 }  // namespace dsa

@@ -86,8 +86,14 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) oacc[c] = f32x16{};
 
-  auto fetch_k = [&](int t, char* dst) { dma_tile<D, NW>(Kbh + (size_t)block_id(t) * kBlock * D, dst, wave, lane); };
-  auto fetch_v = [&](int t, char* dst) { dma_tile<D, NW>(Vbh + (size_t)block_id(t) * kBlock * D, dst, wave, lane); };
+  // copies of block min(t, k-1): past the end the last block is fetched again into a free buffer
+  // (keeps the copies branch-free so they schedule among the MFMAs; the data is never used)
+  auto fetch_k = [&](int t, char* dst) {
+    dma_tile<D, NW>(Kbh + (size_t)block_id(min(t, k - 1)) * kBlock * D, dst, wave, lane);
+  };
+  auto fetch_v = [&](int t, char* dst) {
+    dma_tile<D, NW>(Vbh + (size_t)block_id(min(t, k - 1)) * kBlock * D, dst, wave, lane);
+  };
   // S^T of one block: element e is key 32*kh + 8*(e/4) + 4*hh + e%4 of the block, query row l32
   auto s_tile = [&](const char* kt) {
     f32x16 acc = f32x16{};
@@ -95,21 +101,25 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
     for (int c = 0; c < D / 16; ++c) acc = mfma32(*reinterpret_cast<const bf16x8*>(kt + kofs[c]), qreg[c], acc);
     return acc;
   };
-  // Block t: softmax of its scores sc and O += P V, with the next block's scores
-  // sn = K_{t+1} Q^T issued in between, so the matrix cores work on block t+1
-  // while the vector ALUs exponentiate block t.  At entry K_{t+1} and V_t are
-  // in flight into kn and vc; K_t's and V_{t-1}'s buffers (kfree, vfree) take
-  // K_{t+2} and V_{t+1}.
-  auto step = [&](int t, const f32x16& sc, f32x16& sn, const char* kn, const char* vc, char* kfree, char* vfree) {
-    wait_vmem();
-    __syncthreads();  // K_{t+1}, V_t in LDS; every wave is done with K_t and V_{t-1}
-    if (t + 2 < k) fetch_k(t + 2, kfree);
-    if (t + 1 < k) fetch_v(t + 1, vfree);
+  // row maximum of a score tile (log2 domain)
+  auto row_max = [&](const f32x16& sc) {
     float bm = sc[0];
 #pragma unroll
     for (int e = 1; e < 16; ++e) bm = fmaxf(bm, sc[e]);
-    bm = wave_max_pair(bm) * scale_log2;
-    // lazy rescale: keep the running max unless the block exceeds it by 2^8
+    return wave_max_pair(bm) * scale_log2;
+  };
+  // Block t, in two phases that each pair MFMAs with independent vector work of the same wave:
+  //   A: scores of block t+1 (K_{t+1} Q^T)  ||  exponentials of block t
+  //   B: O += P_t V_t                        ||  row max of block t+1, row sums of block t
+  // At entry K_{t+1} and V_t are in flight into kn and vc and bm holds block t's row max; K_t's and
+  // V_{t-1}'s buffers (kfree, vfree) take K_{t+2} and V_{t+1}.
+  float bm;
+  auto step = [&](int t, const f32x16& sc, f32x16& sn, const char* kn, const char* vc, char* kfree, char* vfree) {
+    wait_vmem();
+    __syncthreads();  // K_{t+1}, V_t in LDS; every wave is done with K_t and V_{t-1}
+    fetch_k(t + 2, kfree);
+    fetch_v(t + 1, vfree);
+    // lazy rescale: keep the running max unless block t exceeds it by 2^8
     if (__ballot(bm > m_used + 8.0f)) {
       const float m_new = fmaxf(m_used, bm);
       const float alpha = __builtin_amdgcn_exp2f(m_used - m_new);
@@ -118,16 +128,13 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
       for (int c = 0; c < D / 32; ++c) oacc[c] *= alpha;
       m_used = m_new;
     }
-    // the next block's scores (after the last block this reads a stale buffer; the result is unused)
-    sn = s_tile(kn);
+    sn = s_tile(kn);  // after the last block this reads a stale buffer; the result is unused
     f16x8 p[2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         p[hf][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[8 * hf + e], scale_log2, -m_used));
-    // row sum of the rounded weights that enter P V
-    l_run = sum_f16x8(p[1], sum_f16x8(p[0], l_run));
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
       const char* v0 = vc + vofs[c][0];
@@ -135,18 +142,23 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
       oacc[c] = mfma32h(join_f16(lds_read_tr16(v0), lds_read_tr16(v1)), p[0], oacc[c]);
       oacc[c] = mfma32h(join_f16(lds_read_tr16(v0 + 16 * RB), lds_read_tr16(v1 + 16 * RB)), p[1], oacc[c]);
     }
+    // row sum of the rounded weights that enter P V
+    l_run = sum_f16x8(p[1], sum_f16x8(p[0], l_run));
+    bm = row_max(sn);
   };
 
   fetch_k(0, kb0);
   fetch_v(0, vb0);
-  if (k > 1) fetch_k(1, kb1);
+  fetch_k(1, kb1);
   wait_vmem();
   __syncthreads();
   f32x16 sa = s_tile(kb0), sb;
+  bm = row_max(sa);
   for (int t = 0; t < k; t += 2) {
     step(t, sa, sb, kb1, vb0, kb0, vb1);
     if (t + 1 < k) step(t + 1, sb, sa, kb0, vb1, kb1, vb0);
   }
+  wait_vmem();  // the copies issued by the last blocks land before the buffers are reused
 
   // merge the two key halves of each row tile (O partials parked in the ring buffers)
   const float l_tot = wave_sum_pair(l_run);

@@ -131,6 +131,24 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
       s = mfma32h(*reinterpret_cast<const f16x8*>(cur + kofs[c]), qreg[c], s);
       dp = mfma32h(*reinterpret_cast<const f16x8*>(cur + TILE + kofs[c]), oreg[c], dp);
     }
+    // operand reads two MFMA pairs ahead of their use
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < D / 16 - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    // K^T operands of dQ^T, read before the exponentials so that those hide the LDS latency
+    f16x8 kt[D / 32][2];
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const char* t0 = cur + tofs[c][0];
+      const char* t1 = cur + tofs[c][1];
+      kt[c][0] = join_f16(lds_read_tr16(t0), lds_read_tr16(t1));
+      kt[c][1] = join_f16(lds_read_tr16(t0 + 16 * RB), lds_read_tr16(t1 + 16 * RB));
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, nl2));
@@ -140,10 +158,8 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
     // dQ^T[c][i] += K^T[c][m] dS^T[m][i]
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
-      const char* t0 = cur + tofs[c][0];
-      const char* t1 = cur + tofs[c][1];
-      acc[c] = mfma32h(join_f16(lds_read_tr16(t0), lds_read_tr16(t1)), d0, acc[c]);
-      acc[c] = mfma32h(join_f16(lds_read_tr16(t0 + 16 * RB), lds_read_tr16(t1 + 16 * RB)), d1, acc[c]);
+      acc[c] = mfma32h(kt[c][0], d0, acc[c]);
+      acc[c] = mfma32h(kt[c][1], d1, acc[c]);
     }
   };
 
@@ -299,6 +315,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
         dp[rb][e] = p * (dp[rb][e] - d4[e]);
       }
     }
+    // S/dP phase: operand reads two MFMA pairs ahead of their use
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * 4 * NS / 2 - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
     // A operands over 32-query chunks kc: element e' <-> query 32*kc + 16*(e'/4) + 4*q4 + e'%4
     const f16x8 pa0 = join4_f16(s[0], s[1]), pa1 = join4_f16(s[2], s[3]);
     f16x8 dh0, dl0, dh1, dl1;
@@ -317,6 +342,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
       dk[c] = mfma16h(dh1, qb1, dk[c]);
       dk[c] = mfma16h(dl1, qb1, dk[c]);
     }
+    // dV/dK phase: the transpose reads of column tile c+1 are issued before the MFMAs of tile c
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+#pragma unroll
+    for (int c = 0; c < NC - 1; ++c) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);
   };
 
   if (iters > 0) fetch(0, st0);

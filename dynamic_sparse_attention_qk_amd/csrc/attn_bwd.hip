@@ -64,7 +64,7 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ dO16,
                                                           const float* __restrict__ NL2, const float* __restrict__ Dvec,
                                                           const int32_t* __restrict__ idx, float* __restrict__ dQ,
-                                                          HeadTable ht, int N, int H, int B, float scale_log2,
+                                                          HeadTable ht, XcdSplit sp, int N, int H, int B, float scale_log2,
                                                           float tau) {
   constexpr int NRT = G / 32;
   constexpr int NW = 2 * NRT;
@@ -76,7 +76,9 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
   static_assert(NRT * OBUF <= 4 * TILE, "merge buffers must fit in the stages");
 
   const int NG = N / G;
-  const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NG * H * B));
+  const int64_t task = xcd_task(sp, blockIdx.x);
+  if (task < 0) return;
+  const uint32_t L = (uint32_t)task;
   const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
   const int k = ht.k[h];
   const int NB = N / kBlock;
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
                                                           const float* __restrict__ Dvec,
                                                           const int32_t* __restrict__ rev_ptr,
                                                           const int32_t* __restrict__ rev_idx, float* __restrict__ dK,
-                                                          float* __restrict__ dV, HeadTable ht, int N, int H, int NB,
+                                                          float* __restrict__ dV, HeadTable ht, XcdSplit sp, int N, int H, int NB,
                                                           int B, float tau) {
   constexpr int NW = 4;
   constexpr int RB = 2 * D;
@@ -242,7 +244,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
   const float scale_log2 = tau * kLog2e;
 
-  const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NB * H * B));
+  const int64_t task = xcd_task(sp, blockIdx.x);
+  if (task < 0) return;
+  const uint32_t L = (uint32_t)task;
   const int j = L % NB, h = (L / NB) % H, b = L / (NB * H);
   const int NG = N / G;
   const size_t bh = (size_t)b * H + h;
@@ -384,8 +388,11 @@ template <int D, int G>
 hipError_t dkdv_launch(const Shape& s, const BwdWork& w, const int32_t* rev_ptr, const int32_t* rev_idx, float* dK,
                        float* dV, const HeadTable& ht, hipStream_t st) {
   const float tau = 1.0f / sqrtf((float)D);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3((unsigned)(s.NB * s.H * s.B)), dim3(256), 0, st, w.Q16, w.K16,
-                     w.V16, w.dO16, w.nl2, w.Dvec, rev_ptr, rev_idx, dK, dV, ht, s.N, s.H, s.NB, s.B, tau);
+  // a KV block costs its reverse-list length, NG * k_h / NB on average, + 1
+  unsigned nwg = 0;
+  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NB, ht, (double)s.NG / s.NB, 1.0, &nwg);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3(nwg), dim3(256), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2,
+                     w.Dvec, rev_ptr, rev_idx, dK, dV, ht, sp, s.N, s.H, s.NB, s.B, tau);
   return hipGetLastError();
 }
 
@@ -393,8 +400,10 @@ template <int D, int G>
 hipError_t dq_launch(const Shape& s, const BwdWork& w, const int32_t* idx, float* dQ, const HeadTable& ht,
                      hipStream_t st) {
   const float tau = 1.0f / sqrtf((float)D);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3((unsigned)(s.NG * s.H * s.B)), dim3(G * 4), 0, st, w.Q16, w.K16,
-                     w.V16, w.dO16, w.nl2, w.Dvec, idx, dQ, ht, s.N, s.H, s.B, tau * kLog2e, tau);
+  unsigned nwg = 0;
+  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0, 1.0, &nwg);  // a group costs k_h blocks + 1
+  hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3(nwg), dim3(G * 4), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2,
+                     w.Dvec, idx, dQ, ht, sp, s.N, s.H, s.B, tau * kLog2e, tau);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
                                                                  const uint16_t* __restrict__ V16,
                                                                  const int32_t* __restrict__ idx,
                                                                  float* __restrict__ O, float* __restrict__ LSE,
-                                                                 HeadTable ht, int N, int H, int B,
+                                                                 HeadTable ht, XcdSplit sp, int N, int H, int B,
                                                                  float scale_log2) {
   constexpr int NRT = G / 32;                  // 32-row tiles of the group
   constexpr int NW = 2 * NRT;                  // waves: row tile x key half
@@ -44,7 +44,9 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
   __shared__ float sml[NRT][2][64];            // m and l of the key-half-1 waves
 
   const int NG = N / G;
-  const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NG * H * B));
+  const int64_t task = xcd_task(sp, blockIdx.x);
+  if (task < 0) return;
+  const uint32_t L = (uint32_t)task;
   const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
   const int k = ht.k[h];
   const int NB = N / kBlock;
@@ -199,7 +201,7 @@ template <int D, int G>
 __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                              const float* __restrict__ V,
                                                              const int32_t* __restrict__ idx, float* __restrict__ O,
-                                                             float* __restrict__ LSE, HeadTable ht, int N, int H,
+                                                             float* __restrict__ LSE, HeadTable ht, XcdSplit sp, int N, int H,
                                                              int B, float scale_log2) {
   constexpr int NT = G * 2;
   constexpr int LD = D + 1;
@@ -207,7 +209,9 @@ __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __rest
   __shared__ float sV[64 * LD];
 
   const int NG = N / G;
-  const uint32_t L = xcd_remap(blockIdx.x, (uint32_t)(NG * H * B));
+  const int64_t task = xcd_task(sp, blockIdx.x);
+  if (task < 0) return;
+  const uint32_t L = (uint32_t)task;
   const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
   const int k = ht.k[h];
   const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * k;
@@ -292,15 +296,17 @@ template <int D, int G>
 hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx, float* O,
                       float* LSE, uint16_t* V16, const HeadTable& ht, hipStream_t st) {
   const float scale_log2 = (1.0f / sqrtf((float)D)) * kLog2e;
-  dim3 grid((unsigned)(s.NG * s.H * s.B));
+  unsigned nwg = 0;
+  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0, 1.0, &nwg);  // a group costs k_h blocks + 1
+  dim3 grid(nwg);
   if (s.bf16) {
     const hipError_t e = launch_cvt_f16(V, V16, (int64_t)s.B * s.H * s.N * D, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, G>), grid, dim3(G * 4), 0, st, static_cast<const bf16_t*>(Q),
-                       static_cast<const bf16_t*>(K), V16, idx, O, LSE, ht, s.N, s.H, s.B, scale_log2);
+                       static_cast<const bf16_t*>(K), V16, idx, O, LSE, ht, sp, s.N, s.H, s.B, scale_log2);
   } else
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D, G>), grid, dim3(G * 2), 0, st, static_cast<const float*>(Q),
-                       static_cast<const float*>(K), static_cast<const float*>(V), idx, O, LSE, ht, s.N, s.H,
+                       static_cast<const float*>(K), static_cast<const float*>(V), idx, O, LSE, ht, sp, s.N, s.H,
                        s.B, scale_log2);
   return hipGetLastError();
 }

@@ -12,6 +12,9 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
 #include <stdint.h>
 
 namespace dsa {
@@ -366,6 +369,49 @@ __device__ __forceinline__ bf16x8 join_bf16(i16x4 a, i16x4 b) {
 // which share most kept blocks, then meet in the same L2.  (Interleaving
 // 64-item runs across the XCDs measured slower on the 57.6k-token workload.)
 constexpr uint32_t kXcds = 8;
+// Work-balanced variant for kernels whose tasks (ordered (b, h, item)) cost
+// different amounts per head: the host cuts the task list into kXcds
+// contiguous ranges of about equal work; workgroup w runs task start[x] + w / 8
+// of XCD x = w % 8, or exits at once when that is past the range.  The grid is
+// 8 x the longest range.  With equal work per task this is xcd_remap.
+struct XcdSplit {
+  int32_t start[kXcds + 1];
+};
+
+__device__ __forceinline__ int64_t xcd_task(const XcdSplit& sp, uint32_t w) {
+  const uint32_t x = w % kXcds, i = w / kXcds;
+  const int64_t t = (int64_t)sp.start[x] + i;
+  return t < sp.start[x + 1] ? t : -1;
+}
+
+// Host: split of the B*H*items tasks when a task of head h costs k_h * scale + overhead.
+inline XcdSplit make_xcd_split(int B, int H, int items, const HeadTable& ht, double scale, double overhead,
+                               unsigned* grid) {
+  double total = 0.0;
+  for (int h = 0; h < H; ++h) total += (double)B * items * (ht.k[h] * scale + overhead);
+  XcdSplit sp;
+  sp.start[0] = 0;
+  uint32_t x = 1;
+  double cum = 0.0;
+  int64_t t = 0;
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+      const double wt = ht.k[h] * scale + overhead;
+      while (x < kXcds && cum + items * wt >= total * x / kXcds) {
+        int64_t m = (int64_t)std::ceil((total * x / kXcds - cum) / wt);
+        m = m < 0 ? 0 : (m > items ? items : m);
+        sp.start[x++] = (int32_t)(t + m);
+      }
+      cum += items * wt;
+      t += items;
+    }
+  while (x <= kXcds) sp.start[x++] = (int32_t)t;
+  int32_t longest = 0;
+  for (uint32_t i = 0; i < kXcds; ++i) longest = std::max(longest, sp.start[i + 1] - sp.start[i]);
+  *grid = kXcds * (unsigned)longest;
+  return sp;
+}
+
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t n) {
   const uint32_t q = n / kXcds, r = n % kXcds;
   const uint32_t x = w % kXcds, i = w / kXcds;

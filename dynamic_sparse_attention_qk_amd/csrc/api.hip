@@ -66,7 +66,8 @@ size_t select_ws(const Shape& s, const HeadTable& ht) {
 
 size_t bwd_row_bytes(const Shape& s) { return align256((size_t)s.B * s.H * s.N * sizeof(float)); }
 size_t bwd_tensor_bytes(const Shape& s) { return align256((size_t)s.B * s.H * s.N * s.D * 2); }
-size_t bwd_ws(const Shape& s) { return 2 * bwd_row_bytes(s) + 4 * bwd_tensor_bytes(s); }
+size_t bwd_order_bytes(const Shape& s) { return align256((size_t)s.B * s.H * s.NB * sizeof(int32_t)); }
+size_t bwd_ws(const Shape& s) { return 2 * bwd_row_bytes(s) + 4 * bwd_tensor_bytes(s) + bwd_order_bytes(s); }
 
 dsa::BwdWork bwd_work(const Shape& s, void* ws) {
   char* p = static_cast<char*>(ws);
@@ -78,6 +79,7 @@ dsa::BwdWork bwd_work(const Shape& s, void* ws) {
   w.K16 = reinterpret_cast<uint16_t*>(t + bwd_tensor_bytes(s));
   w.V16 = reinterpret_cast<uint16_t*>(t + 2 * bwd_tensor_bytes(s));
   w.dO16 = reinterpret_cast<uint16_t*>(t + 3 * bwd_tensor_bytes(s));
+  w.order = reinterpret_cast<int32_t*>(t + 4 * bwd_tensor_bytes(s));
   return w;
 }
 

@@ -222,6 +222,64 @@ __device__ __forceinline__ void join4_f16_split(const f32x4& a, const f32x4& b, 
   }
 }
 
+// Order of the dK/dV tasks within each XCD range: the blocks whose reverse
+// list is longer than half the head's mean first, the rest after, each part in
+// task order (so neighbouring blocks still run together).  The workgroups that
+// start last then have short lists, which trims the tail of the launch.  One
+// workgroup per range; a stable partition by block-wide prefix counts.
+__global__ __launch_bounds__(256) void dkdv_order_kernel(const int32_t* __restrict__ rev_ptr,
+                                                         int32_t* __restrict__ order, HeadTable ht, XcdSplit sp,
+                                                         int NB, int NG, int H) {
+  __shared__ int wsum[4];
+  __shared__ int run[2];
+  const int x = blockIdx.x;
+  const int32_t t0 = sp.start[x], t1 = sp.start[x + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto is_long = [&](int32_t t) {
+    const int32_t bh = t / NB, j = t % NB, h = bh % H;
+    const int32_t* rp = rev_ptr + (int64_t)bh * (NB + 1);
+    const int32_t len = rp[j + 1] - rp[j];
+    return 2LL * len * NB > (long long)NG * ht.k[h];  // len > NG k_h / (2 NB)
+  };
+  // block-wide exclusive prefix of flag over the 256 threads; returns the block total
+  auto block_scan = [&](int flag, int& prefix) {
+    const uint64_t m = __ballot(flag);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+    if (lane == 0) wsum[wave] = __popcll(m);
+    __syncthreads();
+    int base = 0, total = 0;
+    for (int w = 0; w < 4; ++w) {
+      base += w < wave ? wsum[w] : 0;
+      total += wsum[w];
+    }
+    __syncthreads();
+    prefix = base + below;
+    return total;
+  };
+  // pass 1: number of long tasks in the range
+  int nlong = 0;
+  for (int32_t c = t0; c < t1; c += 256) {
+    const int32_t t = c + (int32_t)threadIdx.x;
+    int pre;
+    nlong += block_scan(t < t1 && is_long(t), pre);
+  }
+  // pass 2: stable partition
+  if (threadIdx.x == 0) { run[0] = 0; run[1] = 0; }
+  __syncthreads();
+  for (int32_t c = t0; c < t1; c += 256) {
+    const int32_t t = c + (int32_t)threadIdx.x;
+    const bool valid = t < t1;
+    const bool lg = valid && is_long(t);
+    int pl, ps;
+    const int nl = block_scan(lg, pl);
+    const int ns = block_scan(valid && !lg, ps);
+    if (valid) order[lg ? t0 + run[0] + pl : t0 + nlong + run[1] + ps] = t;
+    __syncthreads();
+    if (threadIdx.x == 0) { run[0] += nl; run[1] += ns; }
+    __syncthreads();
+  }
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q16,
                                                           const uint16_t* __restrict__ K16,
@@ -230,7 +288,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
                                                           const float* __restrict__ NL2,
                                                           const float* __restrict__ Dvec,
                                                           const int32_t* __restrict__ rev_ptr,
-                                                          const int32_t* __restrict__ rev_idx, float* __restrict__ dK,
+                                                          const int32_t* __restrict__ rev_idx,
+                                                          const int32_t* __restrict__ order, float* __restrict__ dK,
                                                           float* __restrict__ dV, HeadTable ht, XcdSplit sp, int N, int H, int NB,
                                                           int B, float tau) {
   constexpr int NW = 4;
@@ -244,9 +303,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
   const float scale_log2 = tau * kLog2e;
 
-  const int64_t task = xcd_task(sp, blockIdx.x);
-  if (task < 0) return;
-  const uint32_t L = (uint32_t)task;
+  const int64_t slot = xcd_task(sp, blockIdx.x);
+  if (slot < 0) return;
+  const int32_t n_tasks = NB * H * B;
+  const uint32_t L = (uint32_t)min(max(order[slot], 0), n_tasks - 1);  // a permutation of the range; clamped
   const int j = L % NB, h = (L / NB) % H, b = L / (NB * H);
   const int NG = N / G;
   const size_t bh = (size_t)b * H + h;
@@ -391,8 +451,9 @@ hipError_t dkdv_launch(const Shape& s, const BwdWork& w, const int32_t* rev_ptr,
   // a KV block costs its reverse-list length, NG * k_h / NB on average, + 1
   unsigned nwg = 0;
   const XcdSplit sp = make_xcd_split(s.B, s.H, s.NB, ht, (double)s.NG / s.NB, 1.0, &nwg);
+  hipLaunchKernelGGL(dkdv_order_kernel, dim3(kXcds), dim3(256), 0, st, rev_ptr, w.order, ht, sp, s.NB, s.NG, s.H);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3(nwg), dim3(256), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2,
-                     w.Dvec, rev_ptr, rev_idx, dK, dV, ht, sp, s.N, s.H, s.NB, s.B, tau);
+                     w.Dvec, rev_ptr, rev_idx, w.order, dK, dV, ht, sp, s.N, s.H, s.NB, s.B, tau);
   return hipGetLastError();
 }
 

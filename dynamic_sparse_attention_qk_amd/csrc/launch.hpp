@@ -34,6 +34,7 @@ struct BwdWork {
   uint16_t* K16;
   uint16_t* V16;
   uint16_t* dO16;
+  int32_t* order;  // dK/dV task order: per XCD range, long reverse lists first
 };
 
 hipError_t launch_bwd_pre(const Shape& s, const void* Q, const void* K, const void* V, const float* O,

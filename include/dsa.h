@@ -157,7 +157,10 @@ int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, cons
  * fp16 copies of Q, K, V, dO, written by the preprocess stage):
  *   dsa_sparse_attn_bwd_preprocess  fills the workspace from Q, K, V, O, dO, LSE;
  *   dsa_sparse_attn_bwd_dkdv        dK, dV from the reverse index (every key
- *                                   row of every block is written);
+ *                                   row of every block is written); it also
+ *                                   writes its own task order (blocks with
+ *                                   long reverse lists first) into the
+ *                                   workspace before the dK/dV launch;
  *   dsa_sparse_attn_bwd_dq          dQ from the kept-block lists.
  */
 int dsa_sparse_attn_bwd_preprocess(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,

@@ -87,19 +87,23 @@ __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(const T* __r
   }
 }
 
-constexpr int kScoreRows = 8;
-constexpr int kScoreCols = 256;
+constexpr int kScoreRows = 32;   // query groups per workgroup
+constexpr int kScoreCols = 256;  // KV blocks per workgroup, one per thread
 
+// scores[b,h,g,j] for a 32 x 256 tile: the 32 q-hat rows sit in LDS (read as
+// broadcasts), each thread keeps its k-hat row in registers and writes one
+// coalesced column of the tile.  score_dot's fixed fma chain makes the values
+// bit-identical to the ones the streamed selection recomputes.
 template <int R>
 __global__ __launch_bounds__(kScoreCols) void block_scores_kernel(const float* __restrict__ qhat,
                                                                    const float* __restrict__ khat,
                                                                    float* __restrict__ scores, int NG, int NB,
-                                                                   int H, float tau) {
+                                                                   float tau) {
   __shared__ float sq[kScoreRows][R];
-  __shared__ float sk[kScoreCols][R + 1];
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int g0 = blockIdx.x * kScoreRows;
-  const size_t bh = (size_t)b * H + h;
+  const int ncx = (NB + kScoreCols - 1) / kScoreCols;
+  const size_t bh = (size_t)blockIdx.z * gridDim.y + blockIdx.y;
+  const int g0 = (blockIdx.x / ncx) * kScoreRows;
+  const int j = (blockIdx.x % ncx) * kScoreCols + threadIdx.x;
   const float* qbh = qhat + bh * (size_t)NG * R;
   const float* kbh = khat + bh * (size_t)NB * R;
   float* sbh = scores + bh * (size_t)NG * NB;
@@ -107,24 +111,21 @@ __global__ __launch_bounds__(kScoreCols) void block_scores_kernel(const float* _
     const int row = t / R, r = t % R;
     sq[row][r] = (g0 + row < NG) ? qbh[(size_t)(g0 + row) * R + r] : 0.f;
   }
-  for (int j0 = 0; j0 < NB; j0 += kScoreCols) {
-    __syncthreads();
-    for (int e = threadIdx.x; e < kScoreCols * R; e += kScoreCols) {
-      const int jr = e / R, r = e % R;
-      const int j = j0 + jr;
-      sk[jr][r] = (j < NB) ? kbh[(size_t)j * R + r] : 0.f;
-    }
-    __syncthreads();
-    const int j = j0 + threadIdx.x;
-    if (j < NB) {
-      float kr[R];
+  float kr[R];
+  if (j < NB) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) kr[r] = sk[threadIdx.x][r];
-#pragma unroll
-      for (int row = 0; row < kScoreRows; ++row)
-        if (g0 + row < NG) sbh[(size_t)(g0 + row) * NB + j] = score_dot<R>(sq[row], kr, tau);
+    for (int r = 0; r < R; r += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(kbh + (size_t)j * R + r);
+      kr[r] = v.x;
+      kr[r + 1] = v.y;
+      kr[r + 2] = v.z;
+      kr[r + 3] = v.w;
     }
   }
+  __syncthreads();
+  if (j >= NB) return;
+  const int rows = min(kScoreRows, NG - g0);
+  for (int row = 0; row < rows; ++row) sbh[(size_t)(g0 + row) * NB + j] = score_dot<R>(sq[row], kr, tau);
 }
 
 template <typename T, int D>
@@ -155,12 +156,12 @@ hipError_t launch_pool_project(const Shape& s, const void* X, const float* W, fl
 
 hipError_t launch_block_scores(const Shape& s, const float* qhat, const float* khat, float* scores, float tau,
                                hipStream_t st) {
-  dim3 grid((s.NG + kScoreRows - 1) / kScoreRows, s.H, s.B);
+  dim3 grid((unsigned)(((s.NB + kScoreCols - 1) / kScoreCols) * ((s.NG + kScoreRows - 1) / kScoreRows)), s.H, s.B);
   switch (s.R) {
-    case 8: hipLaunchKernelGGL(block_scores_kernel<8>, grid, dim3(kScoreCols), 0, st, qhat, khat, scores, s.NG, s.NB, s.H, tau); break;
-    case 16: hipLaunchKernelGGL(block_scores_kernel<16>, grid, dim3(kScoreCols), 0, st, qhat, khat, scores, s.NG, s.NB, s.H, tau); break;
-    case 32: hipLaunchKernelGGL(block_scores_kernel<32>, grid, dim3(kScoreCols), 0, st, qhat, khat, scores, s.NG, s.NB, s.H, tau); break;
-    case 64: hipLaunchKernelGGL(block_scores_kernel<64>, grid, dim3(kScoreCols), 0, st, qhat, khat, scores, s.NG, s.NB, s.H, tau); break;
+    case 8: hipLaunchKernelGGL(block_scores_kernel<8>, grid, dim3(kScoreCols), 0, st, qhat, khat, scores, s.NG, s.NB, tau); break;
+    case 16: hipLaunchKernelGGL(block_scores_kernel<16>, grid, dim3(kScoreCols), 0, st, qhat, khat, scores, s.NG, s.NB, tau); break;
+    case 32: hipLaunchKernelGGL(block_scores_kernel<32>, grid, dim3(kScoreCols), 0, st, qhat, khat, scores, s.NG, s.NB, tau); break;
+    case 64: hipLaunchKernelGGL(block_scores_kernel<64>, grid, dim3(kScoreCols), 0, st, qhat, khat, scores, s.NG, s.NB, tau); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

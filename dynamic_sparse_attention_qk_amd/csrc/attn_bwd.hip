@@ -24,17 +24,26 @@ namespace dsa {
 
 namespace {
 
-// D_i = sum_c dO_ic O_ic, nl2_i = -LSE_i * log2(e), and the fp16 copy of dO;
-// one 16-lane slice per row (D = 128) or 8 (D = 64), 8 columns per lane.
+// D_i = sum_c dO_ic O_ic, nl2_i = -LSE_i * log2(e), and the exact fp16 copies
+// of Q, K, V, dO, in one pass over the rows; one 16-lane slice per row
+// (D = 128) or 8 (D = 64), 8 columns per lane.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__ dO, const float* __restrict__ O,
-                                                      const float* __restrict__ LSE, float* __restrict__ Dvec,
-                                                      float* __restrict__ nl2, uint16_t* __restrict__ dO16,
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
+                                                      const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
+                                                      const float* __restrict__ O, const float* __restrict__ LSE,
+                                                      float* __restrict__ Dvec, float* __restrict__ nl2,
+                                                      uint16_t* __restrict__ Q16, uint16_t* __restrict__ K16,
+                                                      uint16_t* __restrict__ V16, uint16_t* __restrict__ dO16,
                                                       int64_t rows) {
   constexpr int LPR = D / 8;           // lanes per row
   constexpr int RPB = 256 / LPR;       // rows per workgroup pass
   const int sub = threadIdx.x % LPR;
   for (int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR; row < rows; row += (int64_t)gridDim.x * RPB) {
+    const int64_t at = row * D + 8 * sub;
+    const uint4 q = ldg16(Q + at), k = ldg16(K + at), v = ldg16(V + at);
+    *reinterpret_cast<uint4*>(Q16 + at) = bf16x8_to_f16x8(q);
+    *reinterpret_cast<uint4*>(K16 + at) = bf16x8_to_f16x8(k);
+    *reinterpret_cast<uint4*>(V16 + at) = bf16x8_to_f16x8(v);
     const uint4 d = ldg16(dO + row * D + 8 * sub);
     const float4 o0 = *reinterpret_cast<const float4*>(O + row * D + 8 * sub);
     const float4 o1 = *reinterpret_cast<const float4*>(O + row * D + 8 * sub + 4);
@@ -434,13 +443,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
 }
 
 template <int D>
-hipError_t pre_launch(const Shape& s, const float* O, const bf16_t* dO, const float* LSE, const BwdWork& w,
-                      hipStream_t st) {
+hipError_t pre_launch(const Shape& s, const bf16_t* Q, const bf16_t* K, const bf16_t* V, const float* O,
+                      const bf16_t* dO, const float* LSE, const BwdWork& w, hipStream_t st) {
   const int64_t rows = (int64_t)s.B * s.H * s.N;
   constexpr int RPB = 256 / (D / 8);
   const int64_t nwg = (rows + RPB - 1) / RPB;
-  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(nwg < 65536 ? nwg : 65536)), dim3(256), 0, st, dO, O, LSE,
-                     w.Dvec, w.nl2, w.dO16, rows);
+  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(nwg < 65536 ? nwg : 65536)), dim3(256), 0, st, Q, K, V, dO,
+                     O, LSE, w.Dvec, w.nl2, w.Q16, w.K16, w.V16, w.dO16, rows);
   return hipGetLastError();
 }
 
@@ -472,13 +481,11 @@ hipError_t dq_launch(const Shape& s, const BwdWork& w, const int32_t* idx, float
 
 hipError_t launch_bwd_pre(const Shape& s, const void* Q, const void* K, const void* V, const float* O,
                           const void* dO, const float* LSE, const BwdWork& w, hipStream_t st) {
-  const int64_t elems = (int64_t)s.B * s.H * s.N * s.D;
-  hipError_t e = launch_cvt_f16(Q, w.Q16, elems, st);
-  if (e == hipSuccess) e = launch_cvt_f16(K, w.K16, elems, st);
-  if (e == hipSuccess) e = launch_cvt_f16(V, w.V16, elems, st);
-  if (e != hipSuccess) return e;
+  const bf16_t* q = static_cast<const bf16_t*>(Q);
+  const bf16_t* k = static_cast<const bf16_t*>(K);
+  const bf16_t* v = static_cast<const bf16_t*>(V);
   const bf16_t* o = static_cast<const bf16_t*>(dO);
-  return s.D == 64 ? pre_launch<64>(s, O, o, LSE, w, st) : pre_launch<128>(s, O, o, LSE, w, st);
+  return s.D == 64 ? pre_launch<64>(s, q, k, v, O, o, LSE, w, st) : pre_launch<128>(s, q, k, v, O, o, LSE, w, st);
 }
 
 hipError_t launch_bwd_dkdv(const Shape& s, const BwdWork& w, const int32_t* rev_ptr, const int32_t* rev_idx,

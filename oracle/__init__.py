@@ -11,12 +11,14 @@ unpinned".
 """
 from . import dsv_oracle
 from .dsv_oracle import (
-    BLOCK, backward, backward_head, dkdv_blocks, dq_groups, forward, forward_head, group_backward,
-    group_forward, kept_keys, pool_mean, predict, predict_head, reverse_index, reverse_list, select, select_row,
+    BLOCK, backward, backward_head, dkdv_blocks, dq_groups, forward, forward_head, forward_split_head,
+    group_backward, group_forward, kept_keys, merge_states, partial_state, pool_mean, predict, predict_head,
+    reverse_index, reverse_list, select, select_row, split_bounds,
 )
 
 __all__ = [
     "dsv_oracle", "BLOCK", "backward", "backward_head", "dkdv_blocks", "dq_groups", "forward",
-    "forward_head", "group_backward", "group_forward", "kept_keys", "pool_mean", "predict",
-    "predict_head", "reverse_index", "reverse_list", "select", "select_row",
+    "forward_head", "forward_split_head", "group_backward", "group_forward", "kept_keys", "merge_states",
+    "partial_state", "pool_mean", "predict", "predict_head", "reverse_index", "reverse_list", "select",
+    "select_row", "split_bounds",
 ]

@@ -22,6 +22,9 @@ groups of consecutive tokens):
 5. exact softmax attention of every query of the group over the keys of its
    kept blocks only (no mask beyond the selection; bidirectional)
                                                     [hi §2.A stage 2, nl §2.A fase 2]
+   and split-KV partial states over parts of the kept list with their merge
+   (LSE = logsumexp of the parts' LSE, O their exp-weighted sum)
+                                                    [DiTango nl Methodologie; hi §2.C]
 6. the gradient of L = sum(dO * O) with the selection held fixed: dQ, dK, dV
    (keys in no kept block get exactly zero).  The pages call the method a
    training system but never write the backward out; this is the standard
@@ -163,6 +166,53 @@ def forward(q, k, v, idx, group, block=BLOCK):
     for b in range(B):
         for h in range(H):
             o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], idx[b][h], group, block)
+    return o, lse
+
+
+# ----------------------------------------------------------------------------
+# Split-KV: partial attention states over parts of a row's kept blocks, merged
+# (DiTango explainer, nl edition, technical summary, Methodologie: attention
+# states -- output and log-sum-exp -- compose associatively and commutatively;
+# DSV hi §2.C sparse sequence-wise CP: a device attends to the critical KV it
+# holds)
+# ----------------------------------------------------------------------------
+
+def split_bounds(k: int, n_split: int) -> List[Tuple[int, int]]:
+    """Positions [floor(s k / n), floor((s + 1) k / n)) of part s of a k-entry kept list."""
+    return [(s * k // n_split, (s + 1) * k // n_split) for s in range(n_split)]
+
+
+def partial_state(qg: np.ndarray, k: np.ndarray, v: np.ndarray, keys: np.ndarray):
+    """(O_p, LSE_p) of the rows of one group over a subset ``keys`` of its kept keys: the softmax
+    normalised within the subset.  An empty subset gives O_p = 0 and LSE_p = -inf."""
+    if len(keys) == 0:
+        return np.zeros((qg.shape[0], v.shape[1])), np.full(qg.shape[0], -np.inf)
+    o, lse, _ = group_forward(qg, k, v, keys)
+    return o, lse
+
+
+def merge_states(o_parts: Sequence[np.ndarray], lse_parts: Sequence[np.ndarray]):
+    """LSE = ln sum_p exp(LSE_p); O = sum_p exp(LSE_p - LSE) O_p (a part with LSE_p = -inf adds nothing)."""
+    lse_parts = np.stack([np.asarray(x, dtype=np.float64) for x in lse_parts])
+    m = lse_parts.max(axis=0)
+    lse = m + np.log(np.exp(lse_parts - m).sum(axis=0))
+    o = np.zeros_like(np.asarray(o_parts[0], dtype=np.float64))
+    for op, lp in zip(o_parts, lse_parts):
+        o = o + np.exp(lp - lse)[..., None] * op
+    return o, lse
+
+
+def forward_split_head(q, k, v, idx_bh, group, n_split, block=BLOCK, groups=None):
+    """Per part s: O_s [N, d], LSE_s [N] of one (b, h) over part s of every group's kept list
+    (only ``groups`` filled when given, the rest NaN)."""
+    n, d = q.shape
+    o = np.full((n_split, n, d), np.nan)
+    lse = np.full((n_split, n), np.nan)
+    for g in (range(n // group) if groups is None else groups):
+        rows = slice(g * group, (g + 1) * group)
+        row = np.asarray(idx_bh[g])
+        for s, (a, e) in enumerate(split_bounds(len(row), n_split)):
+            o[s, rows], lse[s, rows] = partial_state(q[rows], k, v, kept_keys(row[a:e], block))
     return o, lse
 
 

@@ -229,11 +229,83 @@ def check_batched_api(seed=13):
         np.testing.assert_allclose(lse[0, h], lse_ref, rtol=1e-12, atol=1e-12)
 
 
+def _tiny_selection(seed, n=512, d=16, r=8, group=64, kk=5):
+    q, k, v, do, wq, wk = _tiny(seed, n=n, d=d, r=r)
+    _, _, s = O.predict_head(q, k, wq, wk, group)
+    idx = np.stack([O.select_row(s[g], kk) for g in range(n // group)])
+    return q, k, v, idx
+
+
+def check_split_bounds():
+    for k in (1, 2, 5, 13, 90):
+        for n in (1, 2, 3, 4, 7, 16, 100):
+            b = O.split_bounds(k, n)
+            assert len(b) == n and b[0][0] == 0 and b[-1][1] == k
+            assert all(b[i][1] == b[i + 1][0] for i in range(n - 1))   # contiguous
+            sizes = [e - a for a, e in b]
+            assert max(sizes) - min(sizes) <= 1 and sum(sizes) == k
+
+
+def check_split_merge_equals_unsplit(seed=31, group=64, kk=5):
+    """Any partition of the kept lists, merged, is the unsplit attention (brute-force masked softmax)."""
+    q, k, v, idx = _tiny_selection(seed, group=group, kk=kk)
+    n = q.shape[0]
+    o_ref, lse_ref, _ = brute.masked_attention(q, k, v, brute.mask_from_idx(idx, n, group))
+    for n_split in (1, 2, 3, kk, kk + 3):     # kk + 3 leaves some parts empty
+        o_p, lse_p = O.forward_split_head(q, k, v, idx, group, n_split)
+        o, lse = O.merge_states(list(o_p), list(lse_p))
+        np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+
+
+def check_partial_states_brute(seed=32, group=64, kk=5, n_split=3):
+    """Each part's state is the masked softmax over that part's blocks alone."""
+    q, k, v, idx = _tiny_selection(seed, group=group, kk=kk)
+    n = q.shape[0]
+    o_p, lse_p = O.forward_split_head(q, k, v, idx, group, n_split)
+    for s, (a, e) in enumerate(O.split_bounds(kk, n_split)):
+        mask = brute.mask_from_idx(idx[:, a:e], n, group)
+        o_ref, lse_ref, _ = brute.masked_attention(q, k, v, mask)
+        np.testing.assert_allclose(o_p[s], o_ref, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(lse_p[s], lse_ref, rtol=1e-12, atol=1e-12)
+    # an empty part: O = 0, LSE = -inf
+    o_e, lse_e = O.partial_state(q[:group], k, v, np.zeros(0, dtype=np.int64))
+    assert (o_e == 0).all() and np.isneginf(lse_e).all()
+
+
+def check_merge_algebra(seed=33):
+    """Associative, commutative, identity on one part, and a -inf part contributes nothing."""
+    rng = _rng(seed)
+    parts = [(rng.standard_normal((7, 5)), rng.standard_normal(7) * 3.0) for _ in range(4)]
+    os_, ls_ = [p[0] for p in parts], [p[1] for p in parts]
+    o_all, l_all = O.merge_states(os_, ls_)
+    o12, l12 = O.merge_states(os_[:2], ls_[:2])
+    o34, l34 = O.merge_states(os_[2:], ls_[2:])
+    o_t, l_t = O.merge_states([o12, o34], [l12, l34])
+    np.testing.assert_allclose(o_t, o_all, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(l_t, l_all, rtol=1e-13, atol=1e-13)
+    perm = [2, 0, 3, 1]
+    o_p, l_p = O.merge_states([os_[i] for i in perm], [ls_[i] for i in perm])
+    np.testing.assert_allclose(o_p, o_all, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(l_p, l_all, rtol=1e-13, atol=1e-13)
+    o1, l1 = O.merge_states(os_[:1], ls_[:1])
+    np.testing.assert_allclose(o1, os_[0], rtol=1e-15, atol=0)
+    np.testing.assert_allclose(l1, ls_[0], rtol=1e-15, atol=0)
+    o_n, l_n = O.merge_states(os_[:2] + [np.full((7, 5), 9.0)], ls_[:2] + [np.full(7, -np.inf)])
+    np.testing.assert_allclose(o_n, o12, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(l_n, l12, rtol=1e-14, atol=1e-14)
+    # closed form for two parts with equal LSE: the plain mean of the outputs, LSE + ln 2
+    o_eq, l_eq = O.merge_states([os_[0], os_[1]], [ls_[0], ls_[0]])
+    np.testing.assert_allclose(o_eq, 0.5 * (os_[0] + os_[1]), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(l_eq, ls_[0] + math.log(2.0), rtol=1e-14, atol=1e-14)
+
+
 ALL_CHECKS = [
     check_scores_brute, check_identity_predictor, check_select_brute, check_select_special,
     check_duplicate_blocks_tie, check_linearity, check_forward_brute, check_dense_equals_sdpa,
     check_sparse_equals_masked_sdpa, check_finite_differences, check_gradient_invariants,
-    check_sampled_match_full, check_reverse_index, check_batched_api,
+    check_sampled_match_full, check_reverse_index, check_batched_api, check_split_bounds,
+    check_split_merge_equals_unsplit, check_partial_states_brute, check_merge_algebra,
 ]
 
 
@@ -337,3 +409,18 @@ def test_mutation_backward_transposed_dv(monkeypatch):
         ds = p * (dog @ v[keys].T - dvec[:, None])
         return tau * (ds @ k[keys]), tau * (ds.T @ qg), (p / p.sum(axis=0, keepdims=True)).T @ dog, og, lse
     assert _fails_some_pin(monkeypatch, "group_backward", bad, [check_finite_differences, check_sparse_equals_masked_sdpa])
+
+
+def test_mutation_merge_unweighted(monkeypatch):
+    def bad(o_parts, lse_parts):   # averages the parts' outputs instead of weighting them by exp(LSE_p - LSE)
+        lse = np.logaddexp.reduce(np.stack(lse_parts), axis=0)
+        return sum(o_parts) / len(o_parts), lse
+    assert _fails_some_pin(monkeypatch, "merge_states", bad,
+                           [check_split_merge_equals_unsplit, check_merge_algebra]) > 0
+
+
+def test_mutation_split_bounds_overlap(monkeypatch):
+    def bad(k, n_split):           # parts overlap by one entry
+        return [(max(0, s * k // n_split - 1), (s + 1) * k // n_split) for s in range(n_split)]
+    assert _fails_some_pin(monkeypatch, "split_bounds", bad,
+                           [check_split_bounds, check_split_merge_equals_unsplit]) > 0

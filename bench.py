@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=3, help="workload id 1..5 (3 is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--split-kv", type=int, default=0,
+                    help="also time the split-KV forward in this many parts plus the (O, LSE) merge")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -121,6 +123,37 @@ def stored_traffic(kernel: str, workload: str):
         if kv.get("kernel") == kernel and kv.get("workload") == workload and kv.get("source_sha256") == cur:
             return int(float(kv["fetch_bytes"]) + float(kv["write_bytes"]))
     return None
+
+
+def time_split_kv(args, p, plan, Q, K, V, stream, fwd_ms, f_fwd, w):
+    """Split-KV forward over args.split_kv parts of every kept list, then the (O, LSE) merge, timed with
+    HIP events on the bench stream (same inputs and lists as the step)."""
+    import torch
+    import dynamic_sparse_attention_qk_amd as dsa
+    n = args.split_kv
+    O_part = torch.empty((n,) + tuple(plan.O.shape), dtype=torch.float32, device=plan.O.device)
+    L_part = torch.empty((n,) + tuple(plan.LSE.shape), dtype=torch.float32, device=plan.O.device)
+    O = torch.empty_like(plan.O)
+    L = torch.empty_like(plan.LSE)
+    split_ms, merge_ms = [], []
+    for i in range(args.warmup + args.steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        dsa.sparse_attn_fwd_split(p, Q, K, V, plan.idx, plan.k_per_head, n, O_part, L_part, plan.ws_fwd, stream)
+        e[1].record(stream)
+        dsa.attn_merge(p, n, O_part, L_part, O, L, stream)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            split_ms.append(e[0].elapsed_time(e[1]))
+            merge_ms.append(e[1].elapsed_time(e[2]))
+    rows = w.batch * w.heads * w.seq_len
+    merge_bytes = (n + 1) * rows * (w.head_dim + 1) * 4        # read every part's O and LSE, write O and LSE
+    sm, mm = float(np.mean(split_ms)), float(np.mean(merge_ms))
+    return {"parts": n, "fwd_split_ms": round(sm, 4), "merge_ms": round(mm, 4),
+            "fwd_split_tflops": round(f_fwd / (sm / 1e3) / 1e12, 2), "unsplit_fwd_ms": round(fwd_ms, 4),
+            "merge_hbm_gbs": round(merge_bytes / (mm / 1e3) / 1e9, 1), "merge_hbm_frac": round(
+                merge_bytes / (mm / 1e3) / PEAK_HBM, 4)}
 
 
 def main():
@@ -251,6 +284,8 @@ def main():
                      "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(dom_tflops * 1e12 / peak, 4),
                      "traffic": traffic},
     }
+    if args.split_kv:
+        rec["split_kv"] = time_split_kv(args, p, plan, Q, K, V, stream, stage_ms["fwd"], f_fwd, w)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(inp, args.cpu_seconds)
         rec["cpu_baseline"] = cb

@@ -72,9 +72,12 @@ def library() -> ctypes.CDLL:
         lib.dsa_sparse_attn_bwd_preprocess.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, vp, sz, vp]
         lib.dsa_sparse_attn_bwd_dkdv.argtypes = [pp, kph, i32p, i32p, f32p, f32p, vp, sz, vp]
         lib.dsa_sparse_attn_bwd_dq.argtypes = [pp, i32p, kph, f32p, vp, sz, vp]
+        lib.dsa_sparse_attn_fwd_split.argtypes = [pp, vp, vp, vp, i32p, kph, ctypes.c_int, f32p, f32p, vp, sz, vp]
+        lib.dsa_attn_merge.argtypes = [pp, ctypes.c_int, f32p, f32p, f32p, f32p, vp]
         for name in ("dsa_index_layout", "dsa_predict_block_scores", "dsa_select_topk_blocks",
                      "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_preprocess",
-                     "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq"):
+                     "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_fwd_split",
+                     "dsa_attn_merge"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -82,7 +85,9 @@ def library() -> ctypes.CDLL:
 
 EXPORTED = ("dsa_version", "dsa_status_string", "dsa_index_layout", "dsa_workspace_bytes",
             "dsa_predict_block_scores", "dsa_select_topk_blocks", "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd",
-            "dsa_sparse_attn_bwd_preprocess", "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq")
+            "dsa_sparse_attn_bwd_preprocess", "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq",
+            "dsa_sparse_attn_fwd_split", "dsa_attn_merge")
+MAX_SPLIT = 64  # DSA_MAX_SPLIT
 
 
 @dataclass(frozen=True)
@@ -172,6 +177,22 @@ def sparse_attn_fwd(p: Problem, Q, K, V, idx, k_per_head, O, LSE, workspace=None
     _check("dsa_sparse_attn_fwd", library().dsa_sparse_attn_fwd(
         ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _kph(k_per_head), _ptr(O), _ptr(LSE),
         _ptr(workspace), nbytes, _stream(stream)))
+
+
+def sparse_attn_fwd_split(p: Problem, Q, K, V, idx, k_per_head, n_split: int, O_part, LSE_part, workspace=None,
+                          stream=None) -> None:
+    """Partial states over n_split contiguous parts of every row's kept list: O_part [n_split, B, H, N, d],
+    LSE_part [n_split, B, H, N] (fp32)."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("dsa_sparse_attn_fwd_split", library().dsa_sparse_attn_fwd_split(
+        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _kph(k_per_head), int(n_split), _ptr(O_part),
+        _ptr(LSE_part), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def attn_merge(p: Problem, n_parts: int, O_part, LSE_part, O, LSE, stream=None) -> None:
+    """O, LSE from n_parts partial states (log-sum-exp weighted)."""
+    _check("dsa_attn_merge", library().dsa_attn_merge(
+        ctypes.byref(p.c()), int(n_parts), _ptr(O_part), _ptr(LSE_part), _ptr(O), _ptr(LSE), _stream(stream)))
 
 
 def sparse_attn_bwd(p: Problem, Q, K, V, O, dO, LSE, idx, k_per_head, rev_ptr, rev_idx, dQ, dK, dV, workspace,

@@ -189,8 +189,39 @@ int dsa_sparse_attn_fwd(const dsa_problem* p, const void* Q, const void* K, cons
   const size_t need = fwd_ws(s);
   if (need && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
   if (need && !aligned16(workspace)) return DSA_ERR_ALIGN;
-  return hip_status(dsa::launch_attn_fwd(s, Q, K, V, idx, O, LSE, static_cast<uint16_t*>(workspace), ht,
+  return hip_status(dsa::launch_attn_fwd(s, Q, K, V, idx, O, LSE, static_cast<uint16_t*>(workspace), ht, 1,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int dsa_sparse_attn_fwd_split(const dsa_problem* p, const void* Q, const void* K, const void* V, const int32_t* idx,
+                              const int32_t* k_per_head, int n_split, float* O_part, float* LSE_part,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  HeadTable ht;
+  int st = check_problem(p, &s);
+  if (st) return st;
+  if ((st = check_heads(s, k_per_head, &ht, nullptr))) return st;
+  if (n_split < 1 || n_split > DSA_MAX_SPLIT) return DSA_ERR_INVALID_ARG;
+  if (!Q || !K || !V || !idx || !O_part || !LSE_part) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(idx) || !aligned16(O_part) ||
+      !aligned16(LSE_part))
+    return DSA_ERR_ALIGN;
+  const size_t need = fwd_ws(s);
+  if (need && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return DSA_ERR_ALIGN;
+  return hip_status(dsa::launch_attn_fwd(s, Q, K, V, idx, O_part, LSE_part, static_cast<uint16_t*>(workspace), ht,
+                                         n_split, static_cast<hipStream_t>(stream)));
+}
+
+int dsa_attn_merge(const dsa_problem* p, int n_parts, const float* O_part, const float* LSE_part, float* O,
+                   float* LSE, void* stream) {
+  Shape s;
+  int st = check_problem(p, &s);
+  if (st) return st;
+  if (n_parts < 1 || n_parts > DSA_MAX_SPLIT) return DSA_ERR_INVALID_ARG;
+  if (!O_part || !LSE_part || !O || !LSE) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(O_part) || !aligned16(LSE_part) || !aligned16(O) || !aligned16(LSE)) return DSA_ERR_ALIGN;
+  return hip_status(dsa::launch_attn_merge(s, n_parts, O_part, LSE_part, O, LSE, static_cast<hipStream_t>(stream)));
 }
 
 static int check_bwd_common(const dsa_problem* p, const int32_t* k_per_head, Shape* s, HeadTable* ht) {

@@ -20,6 +20,42 @@ namespace dsa {
 
 namespace {
 
+// Split-KV (partial states over parts of each row's kept list, merged by
+// log-sum-exp; DiTango explainer, nl edition, Methodologie: attention states
+// compose associatively and commutatively; DSV hi §2.C sparse sequence-wise
+// CP): task L of a forward launch with n_split parts is part L % n_split of
+// query group L / n_split (ordered b, h, g); the part covers list positions
+// [part k_h / n_split, (part + 1) k_h / n_split).  n_split = 1 is the plain
+// forward.
+struct FwdTask {
+  int g, h, b, part, kbeg, klen;
+};
+
+__device__ __forceinline__ FwdTask fwd_task(uint32_t L, int NG, int H, int n_split, const HeadTable& ht) {
+  FwdTask t;
+  t.part = (int)(L % (uint32_t)n_split);
+  const uint32_t r = L / (uint32_t)n_split;
+  t.g = r % NG;
+  t.h = (r / NG) % H;
+  t.b = r / (NG * H);
+  const int k = ht.k[t.h];
+  t.kbeg = t.part * k / n_split;
+  t.klen = (t.part + 1) * k / n_split - t.kbeg;
+  return t;
+}
+
+// An empty part: O = 0, LSE = -inf for the 32 rows starting at qrow0 (one wave; lane pair l32, l32+32 per row).
+template <int D>
+__device__ __forceinline__ void write_empty_part(float* O, float* LSE, size_t row, int hh) {
+  float* orow = O + row * D;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *reinterpret_cast<float4*>(orow + 32 * c + 8 * q4 + 4 * hh) = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (hh == 0) LSE[row] = -INFINITY;
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* __restrict__ Q,
                                                                  const bf16_t* __restrict__ K,
@@ -27,7 +63,7 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
                                                                  const int32_t* __restrict__ idx,
                                                                  float* __restrict__ O, float* __restrict__ LSE,
                                                                  HeadTable ht, XcdSplit sp, int N, int H, int B,
-                                                                 float scale_log2) {
+                                                                 int n_split, float scale_log2) {
   constexpr int NRT = G / 32;                  // 32-row tiles of the group
   constexpr int NW = 2 * NRT;                  // waves: row tile x key half
   constexpr int RB = 2 * D;                    // bytes per tile row
@@ -46,19 +82,25 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
   const int NG = N / G;
   const int64_t task = xcd_task(sp, blockIdx.x);
   if (task < 0) return;
-  const uint32_t L = (uint32_t)task;
-  const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
-  const int k = ht.k[h];
+  const FwdTask tk = fwd_task((uint32_t)task, NG, H, n_split, ht);
+  const int g = tk.g, h = tk.h, b = tk.b;
+  const int k = tk.klen;  // blocks of this part
   const int NB = N / kBlock;
-  const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * k;
+  const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * ht.k[h] + tk.kbeg;
   const size_t bh = (size_t)b * H + h;
   const bf16_t* Kbh = K + bh * (size_t)N * D;
   const uint16_t* Vbh = V16 + bh * (size_t)N * D;
+  O += (size_t)tk.part * B * H * N * D;  // this part's output slice
+  LSE += (size_t)tk.part * B * H * N;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int rt = wave % NRT, kh = wave / NRT;  // rows 32*rt.., keys 32*kh.. of every block
   const int qrow = g * G + rt * 32 + l32;
+  if (k == 0) {  // uniform over the workgroup, before any barrier
+    if (kh == 0) write_empty_part<D>(O, LSE, bh * N + qrow, hh);
+    return;
+  }
   // block ids are valid by contract; clamping keeps a bad list from reading out of bounds
   auto block_id = [&](int t) { return min(max(irow[t], 0), NB - 1); };
 
@@ -202,7 +244,7 @@ __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __rest
                                                              const float* __restrict__ V,
                                                              const int32_t* __restrict__ idx, float* __restrict__ O,
                                                              float* __restrict__ LSE, HeadTable ht, XcdSplit sp, int N, int H,
-                                                             int B, float scale_log2) {
+                                                             int B, int n_split, float scale_log2) {
   constexpr int NT = G * 2;
   constexpr int LD = D + 1;
   __shared__ float sK[64 * LD];
@@ -211,16 +253,22 @@ __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __rest
   const int NG = N / G;
   const int64_t task = xcd_task(sp, blockIdx.x);
   if (task < 0) return;
-  const uint32_t L = (uint32_t)task;
-  const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
-  const int k = ht.k[h];
-  const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * k;
+  const FwdTask tk = fwd_task((uint32_t)task, NG, H, n_split, ht);
+  const int g = tk.g, h = tk.h, b = tk.b;
+  const int k = tk.klen;  // blocks of this part
+  const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * ht.k[h] + tk.kbeg;
   const size_t bh = (size_t)b * H + h;
   const float* Kbh = K + bh * (size_t)N * D;
   const float* Vbh = V + bh * (size_t)N * D;
+  O += (size_t)tk.part * B * H * N * D;  // this part's output slice
+  LSE += (size_t)tk.part * B * H * N;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int qrow = g * G + wave * 32 + l32;
+  if (k == 0) {  // uniform over the workgroup, before any barrier
+    write_empty_part<D>(O, LSE, bh * N + qrow, hh);
+    return;
+  }
 
   float qreg[D / 2];
   {
@@ -292,36 +340,85 @@ __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __rest
   if (hh == 0) LSE[bh * N + qrow] = (m_run + __log2f(l_tot)) * kLn2;
 }
 
+// O = sum_s exp(LSE_s - LSE) O_s with LSE = ln sum_s exp(LSE_s), per row; a
+// part with LSE_s = -inf adds nothing (all parts empty: O = 0, LSE = -inf).
+// D/4 lanes per row, four columns each.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ O_part,
+                                                         const float* __restrict__ LSE_part, float* __restrict__ O,
+                                                         float* __restrict__ LSE, int n_parts, int64_t rows) {
+  constexpr int LPR = D / 4;
+  constexpr int RPB = 256 / LPR;
+  const int sub = threadIdx.x % LPR;
+  for (int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR; row < rows; row += (int64_t)gridDim.x * RPB) {
+    float m = -INFINITY;
+    for (int p = 0; p < n_parts; ++p) m = fmaxf(m, LSE_part[p * rows + row]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f;
+    if (m > -INFINITY) {
+      for (int p = 0; p < n_parts; ++p) {
+        const float w = expf(LSE_part[p * rows + row] - m);
+        const float4 o = *reinterpret_cast<const float4*>(O_part + (p * rows + row) * D + 4 * sub);
+        l += w;
+        acc.x += w * o.x;
+        acc.y += w * o.y;
+        acc.z += w * o.z;
+        acc.w += w * o.w;
+      }
+      const float inv = 1.0f / l;
+      acc = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
+    *reinterpret_cast<float4*>(O + row * D + 4 * sub) = acc;
+    if (sub == 0) LSE[row] = m > -INFINITY ? m + logf(l) : -INFINITY;
+  }
+}
+
 template <int D, int G>
 hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx, float* O,
-                      float* LSE, uint16_t* V16, const HeadTable& ht, hipStream_t st) {
+                      float* LSE, uint16_t* V16, const HeadTable& ht, int n_split, hipStream_t st) {
   const float scale_log2 = (1.0f / sqrtf((float)D)) * kLog2e;
   unsigned nwg = 0;
-  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0, 1.0, &nwg);  // a group costs k_h blocks + 1
+  // a (group, part) task costs k_h / n_split blocks + 1
+  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG * n_split, ht, 1.0 / n_split, 1.0, &nwg);
   dim3 grid(nwg);
   if (s.bf16) {
     const hipError_t e = launch_cvt_f16(V, V16, (int64_t)s.B * s.H * s.N * D, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, G>), grid, dim3(G * 4), 0, st, static_cast<const bf16_t*>(Q),
-                       static_cast<const bf16_t*>(K), V16, idx, O, LSE, ht, sp, s.N, s.H, s.B, scale_log2);
+                       static_cast<const bf16_t*>(K), V16, idx, O, LSE, ht, sp, s.N, s.H, s.B, n_split, scale_log2);
   } else
     hipLaunchKernelGGL((attn_fwd_f32_kernel<D, G>), grid, dim3(G * 2), 0, st, static_cast<const float*>(Q),
                        static_cast<const float*>(K), static_cast<const float*>(V), idx, O, LSE, ht, sp, s.N, s.H,
-                       s.B, scale_log2);
+                       s.B, n_split, scale_log2);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx, float* O,
-                           float* LSE, uint16_t* V16, const HeadTable& ht, hipStream_t st) {
+                           float* LSE, uint16_t* V16, const HeadTable& ht, int n_split, hipStream_t st) {
   if (s.D == 64)
-    return s.G == 64 ? fwd_launch<64, 64>(s, Q, K, V, idx, O, LSE, V16, ht, st)
-                     : fwd_launch<64, 128>(s, Q, K, V, idx, O, LSE, V16, ht, st);
+    return s.G == 64 ? fwd_launch<64, 64>(s, Q, K, V, idx, O, LSE, V16, ht, n_split, st)
+                     : fwd_launch<64, 128>(s, Q, K, V, idx, O, LSE, V16, ht, n_split, st);
   if (s.D == 128)
-    return s.G == 64 ? fwd_launch<128, 64>(s, Q, K, V, idx, O, LSE, V16, ht, st)
-                     : fwd_launch<128, 128>(s, Q, K, V, idx, O, LSE, V16, ht, st);
+    return s.G == 64 ? fwd_launch<128, 64>(s, Q, K, V, idx, O, LSE, V16, ht, n_split, st)
+                     : fwd_launch<128, 128>(s, Q, K, V, idx, O, LSE, V16, ht, n_split, st);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_merge(const Shape& s, int n_parts, const float* O_part, const float* LSE_part, float* O,
+                             float* LSE, hipStream_t st) {
+  const int64_t rows = (int64_t)s.B * s.H * s.N;
+  const int rpb = 256 / (s.D / 4);
+  const int64_t nwg = (rows + rpb - 1) / rpb;
+  const dim3 grid((unsigned)(nwg < 65536 ? nwg : 65536));
+  if (s.D == 64)
+    hipLaunchKernelGGL(attn_merge_kernel<64>, grid, dim3(256), 0, st, O_part, LSE_part, O, LSE, n_parts, rows);
+  else if (s.D == 128)
+    hipLaunchKernelGGL(attn_merge_kernel<128>, grid, dim3(256), 0, st, O_part, LSE_part, O, LSE, n_parts, rows);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace dsa

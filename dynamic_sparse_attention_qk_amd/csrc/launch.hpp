@@ -25,7 +25,9 @@ hipError_t launch_reverse_index(const Shape& s, const int32_t* idx, int32_t* rev
                                 int32_t* counters, int32_t* scratch, const HeadTable& ht, int kmax,
                                 hipStream_t st);
 hipError_t launch_attn_fwd(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx,
-                           float* O, float* LSE, uint16_t* V16, const HeadTable& ht, hipStream_t st);
+                           float* O, float* LSE, uint16_t* V16, const HeadTable& ht, int n_split, hipStream_t st);
+hipError_t launch_attn_merge(const Shape& s, int n_parts, const float* O_part, const float* LSE_part, float* O,
+                             float* LSE, hipStream_t st);
 // Backward workspace: D, -LSE*log2(e) and exact fp16 copies of Q, K, V, dO.
 struct BwdWork {
   float* Dvec;

@@ -151,6 +151,45 @@ int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, cons
                         float* dQ, float* dK, float* dV, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* Most parts a split-KV forward or a merge takes. */
+#define DSA_MAX_SPLIT 64
+
+/*
+ * dsa_sparse_attn_fwd_split -- split-KV forward: attention of every query over
+ * one part of its group's kept blocks, as a partial state (DSV hi §2.C sparse
+ * sequence-wise CP: a device attends to the critical KV it holds; DiTango
+ * explainer, nl edition, Methodologie: attention states, output and
+ * log-sum-exp, compose associatively and commutatively).
+ * The kept list of row (b,h,g) (k_h ascending ids) is cut into n_split
+ * contiguous parts; part s holds list positions [s k_h / n_split,
+ * (s+1) k_h / n_split) (integer division).  For every part s and query i of the
+ * group, over the keys m of the part's blocks:
+ *   LSE_part[s][b,h,i] = ln sum_m exp(tau Q_i.K_m),
+ *   O_part[s][b,h,i,:] = sum_m exp(tau Q_i.K_m - LSE_part[s][b,h,i]) V_m;
+ * an empty part (n_split > k_h) gives O = 0 and LSE = -inf.  Merging the parts
+ * with dsa_attn_merge gives dsa_sparse_attn_fwd's O and LSE.
+ * O_part: [n_split, B, H, N, d] fp32; LSE_part: [n_split, B, H, N] fp32;
+ * 1 <= n_split <= DSA_MAX_SPLIT (else DSA_ERR_INVALID_ARG).  Workspace, other
+ * arguments and errors as dsa_sparse_attn_fwd (DSA_WS_FWD).
+ */
+int dsa_sparse_attn_fwd_split(const dsa_problem* p, const void* Q, const void* K, const void* V,
+                              const int32_t* idx, const int32_t* k_per_head, int n_split, float* O_part,
+                              float* LSE_part, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_attn_merge -- combine n_parts partial attention states per query row
+ * (DiTango explainer, nl edition, Methodologie: state composition):
+ *   LSE = ln sum_s exp(LSE_part[s]),  O = sum_s exp(LSE_part[s] - LSE) O_part[s];
+ * a part with LSE = -inf adds nothing; if every part has -inf, O = 0 and
+ * LSE = -inf.  O_part [n_parts, B, H, N, d] and LSE_part [n_parts, B, H, N]
+ * fp32 as written by dsa_sparse_attn_fwd_split (or by other devices'
+ * partial forwards over other blocks); O [B, H, N, d], LSE [B, H, N] fp32.
+ * Only batch, heads, seq_len and head_dim of p are read beyond validation.
+ * 1 <= n_parts <= DSA_MAX_SPLIT; all pointers 16-byte aligned device memory.
+ */
+int dsa_attn_merge(const dsa_problem* p, int n_parts, const float* O_part, const float* LSE_part, float* O,
+                   float* LSE, void* stream);
+
 /*
  * The three stages dsa_sparse_attn_bwd runs, exposed one launch group each,
  * sharing the DSA_WS_BWD workspace (D_i = dO_i . O_i, -LSE*log2(e) and exact

@@ -128,3 +128,23 @@ def test_status_strings():
     for s in range(0, -8, -1):
         assert dsa.status_string(s) != "unknown status"
     assert dsa.status_string(5) == "unknown status"
+
+
+def test_split_and_merge_validation():
+    lib = dsa.library()
+    p = _p()
+    kph = dsa._kph([4, 4])
+    big = 1 << 40
+    pc = ctypes.byref(p.c())
+    for n in (0, -1, dsa.MAX_SPLIT + 1):
+        assert lib.dsa_sparse_attn_fwd_split(pc, FAKE, FAKE, FAKE, FAKE, kph, n, FAKE, FAKE, FAKE, big, None) == -1
+        assert lib.dsa_attn_merge(pc, n, FAKE, FAKE, FAKE, FAKE, None) == -1
+    bad = ctypes.c_void_p(0x100004)
+    assert lib.dsa_sparse_attn_fwd_split(pc, FAKE, FAKE, FAKE, FAKE, kph, 2, None, FAKE, FAKE, big, None) == -1
+    assert lib.dsa_sparse_attn_fwd_split(pc, FAKE, FAKE, FAKE, FAKE, kph, 2, FAKE, bad, FAKE, big, None) == -4
+    assert lib.dsa_sparse_attn_fwd_split(pc, FAKE, FAKE, FAKE, FAKE, kph, 2, FAKE, FAKE, None, 0, None) == -6
+    assert lib.dsa_sparse_attn_fwd_split(pc, FAKE, FAKE, FAKE, FAKE, dsa._kph([0, 4]), 2, FAKE, FAKE, FAKE, big,
+                                         None) == -2
+    assert lib.dsa_attn_merge(pc, 2, FAKE, FAKE, None, FAKE, None) == -1
+    assert lib.dsa_attn_merge(pc, 2, FAKE, FAKE, FAKE, bad, None) == -4
+    assert lib.dsa_attn_merge(ctypes.byref(_p(head_dim=96).c()), 2, FAKE, FAKE, FAKE, FAKE, None) == -5

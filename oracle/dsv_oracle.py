@@ -25,6 +25,9 @@ groups of consecutive tokens):
    and split-KV partial states over parts of the kept list with their merge
    (LSE = logsumexp of the parts' LSE, O their exp-weighted sum)
                                                     [DiTango nl Methodologie; hi §2.C]
+   and, for the OP dispatcher's other branch, full (dense) attention over all
+   keys, with the dispatcher's rule: sparse iff the skipped fraction of
+   (head, group, block) tiles exceeds a threshold   [hi §2.A, nl §2.A stage 2]
 6. the gradient of L = sum(dO * O) with the selection held fixed: dQ, dK, dV
    (keys in no kept block get exactly zero).  The pages call the method a
    training system but never write the backward out; this is the standard
@@ -290,3 +293,94 @@ def dkdv_blocks(q, k, v, do, idx_bh, group, blocks, block=BLOCK) -> Dict[int, Tu
             dv += dv_p[pos:pos + block]
         out[j] = (dk, dv)
     return out
+
+
+# ----------------------------------------------------------------------------
+# Dense attention and the OP dispatcher (hi and nl §2.A, stage 2: per
+# transformer block, sparse attention is switched on only when the block's
+# sparsity exceeds a threshold found by offline profiling; below it the block
+# keeps full attention, as in stage 1)
+# ----------------------------------------------------------------------------
+
+def dense_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray):
+    """O [r, d] and LSE [r] of the given query rows over ALL keys: O = softmax(tau q K^T) V,
+    LSE = ln sum_m exp(tau q . k_m).  Every row is independent of the others."""
+    tau = 1.0 / np.sqrt(q_rows.shape[1])
+    logits = tau * (q_rows @ k.T)
+    m = logits.max(axis=1, keepdims=True)
+    w = np.exp(logits - m)
+    l = w.sum(axis=1)
+    return (w @ v) / l[:, None], m[:, 0] + np.log(l)
+
+
+def dense_forward_head(q, k, v):
+    """O [N, d], LSE [N] of full attention for one (b, h)."""
+    return dense_rows(q, k, v)
+
+
+def dense_backward_head(q, k, v, do):
+    """dQ, dK, dV [N, d] of L = sum(dO * O) for full attention of one (b, h):
+    P = exp(tau Q K^T - LSE), D_i = dO_i . O_i, dS = P (dO V^T - D),
+    dQ = tau dS K, dK = tau dS^T Q, dV = P^T dO."""
+    tau = 1.0 / np.sqrt(q.shape[1])
+    o, lse = dense_rows(q, k, v)
+    p = np.exp(tau * (q @ k.T) - lse[:, None])
+    ds = p * (do @ v.T - (do * o).sum(axis=1)[:, None])
+    return tau * (ds @ k), tau * (ds.T @ q), p.T @ do
+
+
+def dense_forward(q, k, v):
+    """O [B, H, N, d] and LSE [B, H, N] of full attention."""
+    o = np.empty(q.shape[:3] + (v.shape[3],))
+    lse = np.empty(q.shape[:3])
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            o[b, h], lse[b, h] = dense_forward_head(q[b, h], k[b, h], v[b, h])
+    return o, lse
+
+
+def dense_backward(q, k, v, do):
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            dq[b, h], dk[b, h], dv[b, h] = dense_backward_head(q[b, h], k[b, h], v[b, h], do[b, h])
+    return dq, dk, dv
+
+
+def dense_dq_rows(q, k, v, do, rows) -> np.ndarray:
+    """dQ of the listed query rows of one (b, h) under full attention (one row needs only its own P)."""
+    tau = 1.0 / np.sqrt(q.shape[1])
+    qr, dor = q[rows], do[rows]
+    o, lse = dense_rows(qr, k, v)
+    p = np.exp(tau * (qr @ k.T) - lse[:, None])
+    ds = p * (dor @ v.T - (dor * o).sum(axis=1)[:, None])
+    return tau * (ds @ k)
+
+
+def dense_dkdv_blocks(q, k, v, do, blocks, block=BLOCK, chunk=2048) -> Dict[int, Tuple[np.ndarray, np.ndarray]]:
+    """dK, dV rows of the listed 64-key blocks of one (b, h) under full attention: the sums over
+    every query i of tau dS_im q_i and P_im dO_i, taken over query rows ``chunk`` at a time
+    (each row's O, LSE and D over all keys first)."""
+    tau = 1.0 / np.sqrt(q.shape[1])
+    out = {j: (np.zeros((block, k.shape[1])), np.zeros((block, v.shape[1]))) for j in blocks}
+    for r0 in range(0, q.shape[0], chunk):
+        qr, dor = q[r0:r0 + chunk], do[r0:r0 + chunk]
+        o, lse = dense_rows(qr, k, v)
+        dvec = (dor * o).sum(axis=1)
+        for j in blocks:
+            keys = slice(j * block, (j + 1) * block)
+            p = np.exp(tau * (qr @ k[keys].T) - lse[:, None])
+            ds = p * (dor @ v[keys].T - dvec[:, None])
+            out[j][0][:] += tau * (ds.T @ qr)
+            out[j][1][:] += p.T @ dor
+    return out
+
+
+def sparsity(k_per_head: Sequence[int], n_blocks: int) -> float:
+    """Fraction of (head, group, block) attention tiles that the selection skips: 1 - sum_h k_h / (H NB)."""
+    return 1.0 - float(sum(int(x) for x in k_per_head)) / (len(k_per_head) * n_blocks)
+
+
+def use_sparse(k_per_head: Sequence[int], n_blocks: int, threshold: float) -> bool:
+    """The dispatcher's rule: sparse attention iff the sparsity exceeds the threshold."""
+    return sparsity(k_per_head, n_blocks) > threshold

@@ -300,12 +300,86 @@ def check_merge_algebra(seed=33):
     np.testing.assert_allclose(l_eq, ls_[0] + math.log(2.0), rtol=1e-14, atol=1e-14)
 
 
+def check_dense_sdpa(seed=31, n=320, d=16):
+    # full attention against torch's scaled_dot_product_attention and autograd in float64
+    q, k, v, do, _, _ = _tiny(seed, n=n, d=d)
+    o, lse = O.dense_forward_head(q, k, v)
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None])[0]
+    np.testing.assert_allclose(o, ref.detach().numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, torch.logsumexp(tq @ tk.T / math.sqrt(d), dim=1).detach().numpy(),
+                               rtol=1e-12, atol=1e-12)
+    (ref * torch.tensor(do)).sum().backward()
+    for mine, theirs in zip(O.dense_backward_head(q, k, v, do), (tq, tk, tv)):
+        np.testing.assert_allclose(mine, theirs.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def check_dense_brute(seed=32, n=64, d=4):
+    # an all-true mask in the brute-force attention, and central differences of sum(dO * O)
+    q, k, v, do, _, _ = _tiny(seed, n=n, d=d, r=2)
+    mask = np.ones((n, n), dtype=bool)
+    o_ref, lse_ref, _ = brute.masked_attention(q, k, v, mask)
+    o, lse = O.dense_forward_head(q, k, v)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+    for mine, fd in zip(O.dense_backward_head(q, k, v, do), brute.finite_diff_grads(q, k, v, do, mask)):
+        np.testing.assert_allclose(mine, fd, rtol=1e-5, atol=1e-7)
+
+
+def check_dense_closed_forms(seed=33, n=192, d=8):
+    q, _, v, do, _, _ = _tiny(seed, n=n, d=d)
+    k0 = np.zeros((n, d))                                       # equal logits: uniform attention
+    o, lse = O.dense_forward_head(q, k0, v)
+    np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=0), o.shape), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, math.log(n), rtol=1e-14, atol=1e-14)
+    _, _, dv = O.dense_backward_head(q, k0, v, do)
+    np.testing.assert_allclose(dv, np.broadcast_to(do.mean(axis=0), dv.shape), rtol=1e-12, atol=1e-13)
+    # any inputs: rows of P sum to 1, so the dV rows add up to the dO rows; dS rows sum to 0, so dK sums to 0
+    q, k, v, do, _, _ = _tiny(seed + 1, n=n, d=d)
+    _, dk, dv = O.dense_backward_head(q, k, v, do)
+    np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, atol=1e-11)
+    # a key that is a copy of another gets the same gradient rows
+    k2 = k.copy()
+    k2[5] = k2[70]
+    _, dk2, dv2 = O.dense_backward_head(q, k2, np.where(np.arange(n)[:, None] == 5, v[70], v), do)
+    np.testing.assert_allclose(dk2[5], dk2[70], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv2[5], dv2[70], rtol=1e-11, atol=1e-12)
+
+
+def check_dense_sampled(seed=34, n=448, d=8):
+    # the row- and block-sampled evaluators against the full gradient (chunk 96: a ragged last chunk)
+    q, k, v, do, _, _ = _tiny(seed, n=n, d=d)
+    dq, dk, dv = O.dense_backward_head(q, k, v, do)
+    rows = np.array([0, 1, 63, 64, 200, n - 1])
+    np.testing.assert_allclose(O.dense_dq_rows(q, k, v, do, rows), dq[rows], rtol=1e-12, atol=1e-13)
+    got = O.dense_dkdv_blocks(q, k, v, do, [0, 3, n // 64 - 1], chunk=96)
+    for j, (a, b) in got.items():
+        np.testing.assert_allclose(a, dk[j * 64:(j + 1) * 64], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(b, dv[j * 64:(j + 1) * 64], rtol=1e-11, atol=1e-12)
+    o, lse = O.dense_forward_head(q, k, v)
+    o_r, lse_r = O.dense_rows(q[rows], k, v)
+    np.testing.assert_allclose(o_r, o[rows], rtol=1e-12, atol=1e-14)   # BLAS blocking varies with the row count
+    np.testing.assert_allclose(lse_r, lse[rows], rtol=1e-14, atol=0)
+
+
+def check_dispatch_rule():
+    assert O.sparsity([16, 16], 16) == 0.0
+    assert abs(O.sparsity([1, 3], 10) - 0.8) < 1e-15
+    assert abs(O.sparsity([90] * 24, 900) - 0.9) < 1e-15
+    assert not O.use_sparse([16, 16], 16, 0.0)          # nothing skipped: dense even at threshold 0
+    assert not O.use_sparse([8, 8], 16, 0.5)            # exactly at the threshold: dense
+    assert O.use_sparse([7, 8], 16, 0.5)
+    assert O.use_sparse([1], 2, 0.0) and not O.use_sparse([1], 2, 0.5)
+
+
 ALL_CHECKS = [
     check_scores_brute, check_identity_predictor, check_select_brute, check_select_special,
     check_duplicate_blocks_tie, check_linearity, check_forward_brute, check_dense_equals_sdpa,
     check_sparse_equals_masked_sdpa, check_finite_differences, check_gradient_invariants,
     check_sampled_match_full, check_reverse_index, check_batched_api, check_split_bounds,
-    check_split_merge_equals_unsplit, check_partial_states_brute, check_merge_algebra,
+    check_split_merge_equals_unsplit, check_partial_states_brute, check_merge_algebra, check_dense_sdpa,
+    check_dense_brute, check_dense_closed_forms, check_dense_sampled, check_dispatch_rule,
 ]
 
 
@@ -424,3 +498,54 @@ def test_mutation_split_bounds_overlap(monkeypatch):
         return [(max(0, s * k // n_split - 1), (s + 1) * k // n_split) for s in range(n_split)]
     assert _fails_some_pin(monkeypatch, "split_bounds", bad,
                            [check_split_bounds, check_split_merge_equals_unsplit]) > 0
+
+
+def test_mutation_dense_missing_scale(monkeypatch):
+    def bad(q_rows, k, v):
+        logits = q_rows @ k.T
+        m = logits.max(axis=1, keepdims=True)
+        w = np.exp(logits - m)
+        return (w @ v) / w.sum(axis=1)[:, None], m[:, 0] + np.log(w.sum(axis=1))
+    assert _fails_some_pin(monkeypatch, "dense_rows", bad, [check_dense_sdpa, check_dense_brute])
+
+
+def test_mutation_dense_backward_missing_D(monkeypatch):
+    def bad(q, k, v, do):
+        tau = 1.0 / np.sqrt(q.shape[1])
+        o, lse = O.dense_rows(q, k, v)
+        p = np.exp(tau * (q @ k.T) - lse[:, None])
+        ds = p * (do @ v.T)
+        return tau * (ds @ k), tau * (ds.T @ q), p.T @ do
+    assert _fails_some_pin(monkeypatch, "dense_backward_head", bad,
+                           [check_dense_sdpa, check_dense_brute, check_dense_closed_forms])
+
+
+def test_mutation_dense_backward_swapped_dq_dk(monkeypatch):
+    def bad(q, k, v, do):
+        tau = 1.0 / np.sqrt(q.shape[1])
+        o, lse = O.dense_rows(q, k, v)
+        p = np.exp(tau * (q @ k.T) - lse[:, None])
+        ds = p * (do @ v.T - (do * o).sum(axis=1)[:, None])
+        return tau * (ds.T @ q), tau * (ds @ k), p.T @ do
+    assert _fails_some_pin(monkeypatch, "dense_backward_head", bad, [check_dense_sdpa, check_dense_brute])
+
+
+def test_mutation_dense_blocks_chunk_local_lse(monkeypatch):
+    # normalising P within the block instead of over all keys
+    def bad(q, k, v, do, blocks, block=64, chunk=2048):
+        tau = 1.0 / np.sqrt(q.shape[1])
+        out = {}
+        for j in blocks:
+            keys = slice(j * block, (j + 1) * block)
+            o, lse = O.dense_rows(q, k[keys], v[keys])
+            p = np.exp(tau * (q @ k[keys].T) - lse[:, None])
+            ds = p * (do @ v[keys].T - (do * o).sum(axis=1)[:, None])
+            out[j] = (tau * (ds.T @ q), p.T @ do)
+        return out
+    assert _fails_some_pin(monkeypatch, "dense_dkdv_blocks", bad, [check_dense_sampled])
+
+
+def test_mutation_dispatch_at_threshold(monkeypatch):
+    def bad(k_per_head, n_blocks, threshold):
+        return O.sparsity(k_per_head, n_blocks) >= threshold
+    assert _fails_some_pin(monkeypatch, "use_sparse", bad, [check_dispatch_rule])

@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--split-kv", type=int, default=0,
                     help="also time the split-KV forward in this many parts plus the (O, LSE) merge")
+    ap.add_argument("--dispatch-sweep", action="store_true",
+                    help="also time dense attention against the sparse step over a sweep of keep fractions "
+                         "(the dispatcher's break-even sparsity)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -154,6 +157,91 @@ def time_split_kv(args, p, plan, Q, K, V, stream, fwd_ms, f_fwd, w):
             "fwd_split_tflops": round(f_fwd / (sm / 1e3) / 1e12, 2), "unsplit_fwd_ms": round(fwd_ms, 4),
             "merge_hbm_gbs": round(merge_bytes / (mm / 1e3) / 1e9, 1), "merge_hbm_frac": round(
                 merge_bytes / (mm / 1e3) / PEAK_HBM, 4)}
+
+
+SWEEP_KEEP = (0.02, 0.05, 0.1, 0.2, 0.3, 0.5, 0.7, 0.8, 0.9, 0.95, 1.0)
+
+
+def _crossing(xs, ys, level):
+    """Largest x at which the piecewise-linear curve through (xs, ys) (xs ascending) is still below level."""
+    best = None
+    for (x0, y0), (x1, y1) in zip(zip(xs, ys), zip(xs[1:], ys[1:])):
+        if y0 < level <= y1:
+            best = x0 + (x1 - x0) * (level - y0) / (y1 - y0)
+    if best is None:
+        best = xs[-1] if ys[-1] < level else (xs[0] if ys[0] >= level else None)
+    return best
+
+
+def dispatch_sweep(args, w, stream):
+    """Dense forward+backward against the sparse step (predict, select, forward, backward) at uniform keep
+    fractions of the same layer shape, each timed with HIP events on the bench stream.  The break-even keep
+    fraction f* is where the sparse step's time reaches the dense one's; the dispatcher's threshold on the
+    sparsity is 1 - f*.  The same is reported for the forward alone."""
+    import torch
+    import synth
+    import dynamic_sparse_attention_qk_amd as dsa
+    from tests.parity import problem_of, to_device
+
+    wb = w.with_(backward=True)
+    inp = synth.generate(wb)
+    p = problem_of(wb)
+    Q, K, V, dO = (to_device(getattr(inp, n)) for n in ("q", "k", "v", "do"))
+    Wt = to_device(inp.w)
+    reps = max(args.steps // 4, 3)
+
+    def timed(fns):
+        """Mean ms of each of the callables in fns, run back to back, over reps passes after one warm-up."""
+        out = [[] for _ in fns]
+        for i in range(reps + 1):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+            ev[0].record(stream)
+            for j, f in enumerate(fns):
+                f()
+                ev[j + 1].record(stream)
+            torch.cuda.synchronize()
+            if i:
+                for j in range(len(fns)):
+                    out[j].append(ev[j].elapsed_time(ev[j + 1]))
+        return [float(np.mean(x)) for x in out]
+
+    dense = dsa.DenseAttentionPlan(p)
+    d_fwd, d_bwd = timed([lambda: dense.forward(Q, K, V, stream), lambda: dense.backward(Q, K, V, dO, stream)])
+    del dense
+    torch.cuda.empty_cache()
+    unit = 64 * wb.group * wb.head_dim
+    dense_flops = 14.0 * unit * wb.batch * wb.heads * wb.n_groups * wb.n_blocks
+    rows = []
+    for f in SWEEP_KEEP:
+        k = synth.keep_to_k(f, wb.n_blocks)
+        plan = dsa.SparseAttentionPlan(p, [k] * wb.heads, materialise_scores=not wb.streamed)
+        plan.idx.zero_()
+        plan.rev_idx.zero_()
+        plan.predict(Q, K, Wt, Wt, stream)
+        plan.select(stream)
+        torch.cuda.synchronize()
+        ids = plan.idx[: int(plan.row_base[-1])].cpu().numpy()
+        assert ids.min() >= 0 and ids.max() < p.n_blocks, "kept-block list out of range"
+        s_pred, s_fwd, s_bwd = timed([lambda: (plan.predict(Q, K, Wt, Wt, stream), plan.select(stream)),
+                                      lambda: plan.forward(Q, K, V, stream),
+                                      lambda: plan.backward(Q, K, V, dO, stream)])
+        rows.append({"keep": f, "k": k, "predict_select_ms": round(s_pred, 4), "fwd_ms": round(s_fwd, 4),
+                     "bwd_ms": round(s_bwd, 4), "step_ms": round(s_pred + s_fwd + s_bwd, 4),
+                     "fwd_only_ms": round(s_pred + s_fwd, 4)})
+        del plan
+        torch.cuda.empty_cache()
+    keeps = [r["k"] / wb.n_blocks for r in rows]
+    f_step = _crossing(keeps, [r["step_ms"] for r in rows], d_fwd + d_bwd)
+    f_fwd = _crossing(keeps, [r["fwd_only_ms"] for r in rows], d_fwd)
+    return {"workload": wb.name, "seq_len": wb.seq_len, "heads": wb.heads, "head_dim": wb.head_dim,
+            "group": wb.group, "dense_fwd_ms": round(d_fwd, 4), "dense_bwd_ms": round(d_bwd, 4),
+            "dense_fwd_bwd_tflops": round(dense_flops / ((d_fwd + d_bwd) / 1e3) / 1e12, 2),
+            "dense_fwd_tflops": round(dense_flops * 4 / 14 / (d_fwd / 1e3) / 1e12, 2),
+            "sparse": rows,
+            "break_even_keep_step": None if f_step is None else round(f_step, 4),
+            "min_sparsity_step": None if f_step is None else round(1 - f_step, 4),
+            "break_even_keep_fwd": None if f_fwd is None else round(f_fwd, 4),
+            "min_sparsity_fwd": None if f_fwd is None else round(1 - f_fwd, 4)}
 
 
 def main():
@@ -286,6 +374,10 @@ def main():
     }
     if args.split_kv:
         rec["split_kv"] = time_split_kv(args, p, plan, Q, K, V, stream, stage_ms["fwd"], f_fwd, w)
+    if args.dispatch_sweep:
+        del plan
+        torch.cuda.empty_cache()
+        rec["dispatch_sweep"] = dispatch_sweep(args, w, stream)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(inp, args.cpu_seconds)
         rec["cpu_baseline"] = cb

@@ -74,10 +74,13 @@ def library() -> ctypes.CDLL:
         lib.dsa_sparse_attn_bwd_dq.argtypes = [pp, i32p, kph, f32p, vp, sz, vp]
         lib.dsa_sparse_attn_fwd_split.argtypes = [pp, vp, vp, vp, i32p, kph, ctypes.c_int, f32p, f32p, vp, sz, vp]
         lib.dsa_attn_merge.argtypes = [pp, ctypes.c_int, f32p, f32p, f32p, f32p, vp]
+        lib.dsa_dense_attn_fwd.argtypes = [pp, vp, vp, vp, f32p, f32p, vp, sz, vp]
+        lib.dsa_dense_attn_bwd.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, f32p, f32p, f32p, vp, sz, vp]
+        lib.dsa_choose_path.argtypes = [pp, kph, ctypes.c_double, sz]
         for name in ("dsa_index_layout", "dsa_predict_block_scores", "dsa_select_topk_blocks",
                      "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_preprocess",
                      "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_fwd_split",
-                     "dsa_attn_merge"):
+                     "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd", "dsa_choose_path"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -86,8 +89,11 @@ def library() -> ctypes.CDLL:
 EXPORTED = ("dsa_version", "dsa_status_string", "dsa_index_layout", "dsa_workspace_bytes",
             "dsa_predict_block_scores", "dsa_select_topk_blocks", "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd",
             "dsa_sparse_attn_bwd_preprocess", "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq",
-            "dsa_sparse_attn_fwd_split", "dsa_attn_merge")
+            "dsa_sparse_attn_fwd_split", "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd",
+            "dsa_choose_path")
 MAX_SPLIT = 64  # DSA_MAX_SPLIT
+PATH_DENSE, PATH_SPARSE = 0, 1  # dsa_path
+DEFAULT_MIN_SPARSITY = 0.06     # DSA_DEFAULT_MIN_SPARSITY
 
 
 @dataclass(frozen=True)
@@ -154,8 +160,10 @@ def index_layout(p: Problem, k_per_head: Sequence[int]) -> np.ndarray:
     return out
 
 
-def workspace_bytes(p: Problem, k_per_head: Sequence[int], which: int) -> int:
-    return int(library().dsa_workspace_bytes(ctypes.byref(p.c()), _kph(k_per_head), which))
+def workspace_bytes(p: Problem, k_per_head: Optional[Sequence[int]], which: int) -> int:
+    """Workspace bytes of a call; k_per_head may be None for DSA_WS_FWD / DSA_WS_BWD."""
+    kph = None if k_per_head is None else _kph(k_per_head)
+    return int(library().dsa_workspace_bytes(ctypes.byref(p.c()), kph, which))
 
 
 def predict_block_scores(p: Problem, Q, K, Wq, Wk, qhat, khat, scores=None, stream=None) -> None:
@@ -193,6 +201,28 @@ def attn_merge(p: Problem, n_parts: int, O_part, LSE_part, O, LSE, stream=None) 
     """O, LSE from n_parts partial states (log-sum-exp weighted)."""
     _check("dsa_attn_merge", library().dsa_attn_merge(
         ctypes.byref(p.c()), int(n_parts), _ptr(O_part), _ptr(LSE_part), _ptr(O), _ptr(LSE), _stream(stream)))
+
+
+def dense_attn_fwd(p: Problem, Q, K, V, O, LSE, workspace=None, stream=None) -> None:
+    """Full attention over every key (the dispatcher's dense branch)."""
+    nbytes = 0 if workspace is None else _nbytes(workspace)
+    _check("dsa_dense_attn_fwd", library().dsa_dense_attn_fwd(
+        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), _ptr(workspace), nbytes,
+        _stream(stream)))
+
+
+def dense_attn_bwd(p: Problem, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, stream=None) -> None:
+    _check("dsa_dense_attn_bwd", library().dsa_dense_attn_bwd(
+        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV),
+        _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def choose_path(p: Problem, k_per_head: Sequence[int], min_sparsity: float = -1.0, max_sparse_bytes: int = 0) -> int:
+    """PATH_SPARSE or PATH_DENSE for one layer (min_sparsity < 0: the library's measured default)."""
+    st = library().dsa_choose_path(ctypes.byref(p.c()), _kph(k_per_head), float(min_sparsity), int(max_sparse_bytes))
+    if st < 0:
+        _check("dsa_choose_path", st)
+    return st
 
 
 def sparse_attn_bwd(p: Problem, Q, K, V, O, dO, LSE, idx, k_per_head, rev_ptr, rev_idx, dQ, dK, dV, workspace,
@@ -289,3 +319,26 @@ class SparseAttentionPlan:
         """View of the kept-block list of (b, h) as [NG, k_h]."""
         s = int(self.row_base[b * self.p.heads + h])
         return self.idx[s:s + self.p.n_groups * self.k_per_head[h]].view(self.p.n_groups, self.k_per_head[h])
+
+
+class DenseAttentionPlan:
+    """Outputs and workspaces of full attention for one problem (the dispatcher's dense branch)."""
+
+    def __init__(self, p: Problem, device="cuda", backward: bool = True):
+        self.p = p
+        B, H, N, D = p.batch, p.heads, p.seq_len, p.head_dim
+        f32 = dict(dtype=torch.float32, device=device)
+        self.ws_fwd = torch.empty(max(workspace_bytes(p, None, DSA_WS_FWD), 16), dtype=torch.uint8, device=device)
+        self.O = torch.empty(B, H, N, D, **f32)
+        self.LSE = torch.empty(B, H, N, **f32)
+        if backward:
+            self.dQ = torch.empty(B, H, N, D, **f32)
+            self.dK = torch.empty(B, H, N, D, **f32)
+            self.dV = torch.empty(B, H, N, D, **f32)
+            self.ws_bwd = torch.empty(workspace_bytes(p, None, DSA_WS_BWD), dtype=torch.uint8, device=device)
+
+    def forward(self, Q, K, V, stream=None):
+        dense_attn_fwd(self.p, Q, K, V, self.O, self.LSE, self.ws_fwd, stream)
+
+    def backward(self, Q, K, V, dO, stream=None):
+        dense_attn_bwd(self.p, Q, K, V, self.O, dO, self.LSE, self.dQ, self.dK, self.dV, self.ws_bwd, stream)

@@ -88,6 +88,24 @@ size_t fwd_ws(const Shape& s) { return s.bf16 ? align256((size_t)s.B * s.H * s.N
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
+// Dense attention: every head keeps all NB blocks and the kernels take block t at list position t.
+HeadTable dense_heads(const Shape& s) {
+  HeadTable ht;
+  memset(&ht, 0, sizeof(ht));
+  for (int h = 0; h <= s.H; ++h) ht.kofs[h] = h * s.NB;
+  for (int h = 0; h < s.H; ++h) ht.k[h] = s.NB;
+  ht.ksum = s.H * s.NB;
+  return ht;
+}
+
+// Device bytes the sparse path needs beyond the dense one: qhat, khat, idx, rev_ptr, rev_idx and the
+// selection workspace (block scores streamed, not materialised).
+size_t sparse_extra_bytes(const Shape& s, const HeadTable& ht) {
+  const size_t list = (size_t)s.B * s.NG * ht.ksum * sizeof(int32_t);
+  return (size_t)s.B * s.H * ((size_t)s.NG + s.NB) * s.R * sizeof(float) + 2 * list +
+         (size_t)s.B * s.H * (s.NB + 1) * sizeof(int32_t) + select_ws(s, ht);
+}
+
 }  // namespace
 
 extern "C" {
@@ -124,7 +142,11 @@ int dsa_index_layout(const dsa_problem* p, const int32_t* k_per_head, int64_t* r
 size_t dsa_workspace_bytes(const dsa_problem* p, const int32_t* k_per_head, int which_call) {
   Shape s;
   HeadTable ht;
-  if (check_problem(p, &s) || check_heads(s, k_per_head, &ht, nullptr)) return 0;
+  if (check_problem(p, &s)) return 0;
+  // the forward and backward workspaces do not depend on the kept counts (dense calls pass none)
+  if (!k_per_head && which_call == DSA_WS_FWD) return fwd_ws(s);
+  if (!k_per_head && which_call == DSA_WS_BWD) return bwd_ws(s);
+  if (check_heads(s, k_per_head, &ht, nullptr)) return 0;
   if (which_call == DSA_WS_SELECT) return select_ws(s, ht);
   if (which_call == DSA_WS_BWD) return bwd_ws(s);
   if (which_call == DSA_WS_FWD) return fwd_ws(s);
@@ -298,6 +320,61 @@ int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, cons
   if (e == hipSuccess) e = dsa::launch_bwd_dkdv(s, w, rev_ptr, rev_idx, dK, dV, ht, hs);
   if (e == hipSuccess) e = dsa::launch_bwd_dq(s, w, idx, dQ, ht, hs);
   return hip_status(e);
+}
+
+int dsa_dense_attn_fwd(const dsa_problem* p, const void* Q, const void* K, const void* V, float* O, float* LSE,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  Shape s;
+  int st = check_problem(p, &s);
+  if (st) return st;
+  if (!Q || !K || !V || !O || !LSE) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(LSE)) return DSA_ERR_ALIGN;
+  const size_t need = fwd_ws(s);
+  if (need && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (need && !aligned16(workspace)) return DSA_ERR_ALIGN;
+  return hip_status(dsa::launch_attn_fwd(s, Q, K, V, nullptr, O, LSE, static_cast<uint16_t*>(workspace),
+                                         dense_heads(s), 1, static_cast<hipStream_t>(stream)));
+}
+
+int dsa_dense_attn_bwd(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
+                       const void* dO, const float* LSE, float* dQ, float* dK, float* dV, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  Shape s;
+  int st = check_problem(p, &s);
+  if (st) return st;
+  if (!s.bf16) return DSA_ERR_DTYPE;
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(LSE) ||
+      !aligned16(dQ) || !aligned16(dK) || !aligned16(dV))
+    return DSA_ERR_ALIGN;
+  if ((st = check_ws(s, workspace, workspace_bytes))) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const dsa::BwdWork w = bwd_work(s, workspace);
+  const HeadTable ht = dense_heads(s);
+  hipError_t e = dsa::launch_bwd_pre(s, Q, K, V, O, dO, LSE, w, hs);
+  if (e == hipSuccess) e = dsa::launch_bwd_dkdv(s, w, nullptr, nullptr, dK, dV, ht, hs);
+  if (e == hipSuccess) e = dsa::launch_bwd_dq(s, w, nullptr, dQ, ht, hs);
+  return hip_status(e);
+}
+
+int dsa_choose_path(const dsa_problem* p, const int32_t* k_per_head, double min_sparsity, size_t max_sparse_bytes) {
+  Shape s;
+  HeadTable ht;
+  int st = check_problem(p, &s);
+  if (st) return st;
+  if (!k_per_head) return DSA_ERR_INVALID_ARG;
+  memset(&ht, 0, sizeof(ht));
+  int64_t kept = 0;
+  for (int h = 0; h < s.H; ++h) {
+    if (k_per_head[h] < 1 || k_per_head[h] > s.NB) return DSA_ERR_SHAPE;
+    kept += k_per_head[h];
+  }
+  if (!(min_sparsity >= 0.0)) min_sparsity = DSA_DEFAULT_MIN_SPARSITY;  // negative or NaN: the default
+  const double sparsity = 1.0 - (double)kept / ((double)s.H * s.NB);
+  if (!(sparsity > min_sparsity)) return DSA_PATH_DENSE;
+  if (check_heads(s, k_per_head, &ht, nullptr)) return DSA_PATH_DENSE;  // lists beyond the sparse limits
+  if (max_sparse_bytes && sparse_extra_bytes(s, ht) > max_sparse_bytes) return DSA_PATH_DENSE;
+  return DSA_PATH_SPARSE;
 }
 
 }  // extern "C"

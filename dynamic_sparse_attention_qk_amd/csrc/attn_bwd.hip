@@ -66,7 +66,8 @@ __device__ __forceinline__ f16x8 ldg_f16x8(const uint16_t* p) { return __builtin
 
 // ---------------------------------------------------------------- dQ
 
-template <int D, int G>
+// kLists false: dense attention (no lists; list position t is block t).
+template <int D, int G, bool kLists>
 __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __restrict__ Q16,
                                                           const uint16_t* __restrict__ K16,
                                                           const uint16_t* __restrict__ V16,
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
   const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
   const int k = ht.k[h];
   const int NB = N / kBlock;
-  const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * k;
+  const int32_t* irow = kLists ? idx + row_base(ht, b, h, NG) + (int64_t)g * k : nullptr;
   const size_t bh = (size_t)b * H + h;
   const uint16_t* Kbh = K16 + bh * (size_t)N * D;
   const uint16_t* Vbh = V16 + bh * (size_t)N * D;
@@ -99,7 +100,11 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
   const int l32 = lane & 31, hh = lane >> 5;
   const int rt = wave % NRT, kh = wave / NRT;
   const size_t qrow = bh * N + (size_t)g * G + rt * 32 + l32;
-  auto block_id = [&](int t) { return min(max(irow[t], 0), NB - 1); };
+  // block of list position min(t, k-1); ids are valid by contract, clamped so a bad list cannot read out of bounds
+  auto block_id = [&](int t) {
+    if constexpr (kLists) return min(max(irow[min(t, k - 1)], 0), NB - 1);
+    else return min(t, k - 1);
+  };
 
   f16x8 qreg[D / 16], oreg[D / 16];
 #pragma unroll
@@ -126,15 +131,18 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) acc[c] = f32x16{};
 
-  auto fetch = [&](int t, char* dst) {
-    const int j = block_id(t);
+  auto fetch = [&](int j, char* dst) {
     dma_tile<D, NW>(Kbh + (size_t)j * kBlock * D, dst, wave, lane);
     dma_tile<D, NW>(Vbh + (size_t)j * kBlock * D, dst + TILE, wave, lane);
   };
+  // block ids read ahead: at step t, id_n = block of t+1 and id_pf = block of t+2 are in registers
+  int id_n, id_pf;
   auto step = [&](int t, const char* cur, char* nxt) {
     wait_vmem();
     __syncthreads();
-    if (t + 1 < k) fetch(t + 1, nxt);
+    if (t + 1 < k) fetch(id_n, nxt);
+    id_n = id_pf;
+    id_pf = block_id(t + 3);
     // S^T and dP^T: rows = this half's 32 keys, columns = the wave's 32 queries
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -174,7 +182,9 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
     }
   };
 
-  fetch(0, st0);
+  fetch(block_id(0), st0);
+  id_n = block_id(1);
+  id_pf = block_id(2);
   for (int t = 0; t < k; t += 2) {
     step(t, st0, st1);
     if (t + 1 < k) step(t + 1, st1, st0);
@@ -289,7 +299,8 @@ __global__ __launch_bounds__(256) void dkdv_order_kernel(const int32_t* __restri
   }
 }
 
-template <int D, int G>
+// kLists false: dense attention (no reverse lists or order; every block has all NG groups).
+template <int D, int G, bool kLists>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q16,
                                                           const uint16_t* __restrict__ K16,
                                                           const uint16_t* __restrict__ V16,
@@ -315,16 +326,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
   const int64_t slot = xcd_task(sp, blockIdx.x);
   if (slot < 0) return;
   const int32_t n_tasks = NB * H * B;
-  const uint32_t L = (uint32_t)min(max(order[slot], 0), n_tasks - 1);  // a permutation of the range; clamped
+  // a permutation of the range (the identity for dense attention); clamped
+  const uint32_t L = kLists ? (uint32_t)min(max(order[slot], 0), n_tasks - 1) : (uint32_t)slot;
   const int j = L % NB, h = (L / NB) % H, b = L / (NB * H);
   const int NG = N / G;
   const size_t bh = (size_t)b * H + h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
-  const int32_t* rp = rev_ptr + bh * (NB + 1);
   const int32_t total = NG * ht.k[h];  // size of the (b, h) region of the reverse list
-  const int32_t s0 = min(max(rp[j], 0), total), s1 = min(max(rp[j + 1], s0), total);
-  const int32_t* rlist = rev_idx + row_base(ht, b, h, NG) + s0;
+  int32_t s0 = 0, s1 = NG;
+  const int32_t* rlist = nullptr;
+  if constexpr (kLists) {
+    const int32_t* rp = rev_ptr + bh * (NB + 1);
+    s0 = min(max(rp[j], 0), total);
+    s1 = min(max(rp[j + 1], s0), total);
+    rlist = rev_idx + row_base(ht, b, h, NG) + s0;
+  }
   const int iters = (s1 - s0) * SUB;
 
   // this wave's 16 keys as B operands: K for S = Q K^T, V for dP = dO V^T
@@ -350,8 +367,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
 #pragma unroll
   for (int c = 0; c < NC; ++c) { dk[c] = f32x4{}; dv[c] = f32x4{}; }
 
-  auto fetch = [&](int it, char* dst) {
-    const int g = min(max(rlist[it / SUB], 0), NG - 1);  // valid by contract; never read out of bounds
+  // group of query tile min(it, iters-1) (needs iters > 0); clamped: never out of bounds
+  auto group_of = [&](int it) {
+    if constexpr (kLists) return min(max(rlist[min(it, iters - 1) / SUB], 0), NG - 1);
+    else return min(it, iters - 1) / SUB;
+  };
+  // groups read ahead: at step it, g_n = group of tile it+1 and g_pf = group of tile it+2 are in registers
+  int g_n = 0, g_pf = 0;
+  auto fetch = [&](int it, int g, char* dst) {
     const size_t row0 = bh * N + (size_t)g * G + (size_t)(it % SUB) * 64;
     dma_tile<D, NW>(Q16 + row0 * D, dst, wave, lane);
     dma_tile<D, NW>(dO16 + row0 * D, dst + TILE, wave, lane);
@@ -361,7 +384,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
   auto step = [&](int it, const char* cur, char* nxt) {
     wait_vmem();
     __syncthreads();  // tile it is in LDS and every wave is done with tile it-1
-    if (it + 1 < iters) fetch(it + 1, nxt);
+    if (it + 1 < iters) fetch(it + 1, g_n, nxt);
+    g_n = g_pf;
+    g_pf = group_of(it + 3);
     // S[i][m], dP[i][m] for the 64 queries (4 row blocks) x this wave's 16 keys;
     // element e of row block rb: query 16*rb + 4*q4 + e
     f32x4 s[4], dp[4];
@@ -425,7 +450,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);
   };
 
-  if (iters > 0) fetch(0, st0);
+  if (iters > 0) {
+    fetch(0, group_of(0), st0);
+    g_n = group_of(1);
+    g_pf = group_of(2);
+  }
   for (int it = 0; it < iters; it += 2) {
     step(it, st0, st1);
     if (it + 1 < iters) step(it + 1, st1, st0);
@@ -460,9 +489,13 @@ hipError_t dkdv_launch(const Shape& s, const BwdWork& w, const int32_t* rev_ptr,
   // a KV block costs its reverse-list length, NG * k_h / NB on average, + 1
   unsigned nwg = 0;
   const XcdSplit sp = make_xcd_split(s.B, s.H, s.NB, ht, (double)s.NG / s.NB, 1.0, &nwg);
-  hipLaunchKernelGGL(dkdv_order_kernel, dim3(kXcds), dim3(256), 0, st, rev_ptr, w.order, ht, sp, s.NB, s.NG, s.H);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, G>), dim3(nwg), dim3(256), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2,
-                     w.Dvec, rev_ptr, rev_idx, w.order, dK, dV, ht, sp, s.N, s.H, s.NB, s.B, tau);
+  // dense (no reverse lists): every block has all NG groups and the order is the identity
+  if (rev_ptr)
+    hipLaunchKernelGGL(dkdv_order_kernel, dim3(kXcds), dim3(256), 0, st, rev_ptr, w.order, ht, sp, s.NB, s.NG,
+                       s.H);
+  auto kern = rev_ptr ? bwd_dkdv_kernel<D, G, true> : bwd_dkdv_kernel<D, G, false>;
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(256), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, rev_ptr, rev_idx,
+                     w.order, dK, dV, ht, sp, s.N, s.H, s.NB, s.B, tau);
   return hipGetLastError();
 }
 
@@ -472,8 +505,9 @@ hipError_t dq_launch(const Shape& s, const BwdWork& w, const int32_t* idx, float
   const float tau = 1.0f / sqrtf((float)D);
   unsigned nwg = 0;
   const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0, 1.0, &nwg);  // a group costs k_h blocks + 1
-  hipLaunchKernelGGL((bwd_dq_kernel<D, G>), dim3(nwg), dim3(G * 4), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2,
-                     w.Dvec, idx, dQ, ht, sp, s.N, s.H, s.B, tau * kLog2e, tau);
+  auto kern = idx ? bwd_dq_kernel<D, G, true> : bwd_dq_kernel<D, G, false>;
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(G * 4), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, idx, dQ, ht, sp,
+                     s.N, s.H, s.B, tau * kLog2e, tau);
   return hipGetLastError();
 }
 

@@ -56,7 +56,8 @@ __device__ __forceinline__ void write_empty_part(float* O, float* LSE, size_t ro
   if (hh == 0) LSE[row] = -INFINITY;
 }
 
-template <int D, int G>
+// kLists false: dense attention (no lists; list position t of the part is block kbeg + t).
+template <int D, int G, bool kLists>
 __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* __restrict__ Q,
                                                                  const bf16_t* __restrict__ K,
                                                                  const uint16_t* __restrict__ V16,
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
   const int g = tk.g, h = tk.h, b = tk.b;
   const int k = tk.klen;  // blocks of this part
   const int NB = N / kBlock;
-  const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * ht.k[h] + tk.kbeg;
+  const int32_t* irow = kLists ? idx + row_base(ht, b, h, NG) + (int64_t)g * ht.k[h] + tk.kbeg : nullptr;
   const size_t bh = (size_t)b * H + h;
   const bf16_t* Kbh = K + bh * (size_t)N * D;
   const uint16_t* Vbh = V16 + bh * (size_t)N * D;
@@ -101,8 +102,13 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
     if (kh == 0) write_empty_part<D>(O, LSE, bh * N + qrow, hh);
     return;
   }
-  // block ids are valid by contract; clamping keeps a bad list from reading out of bounds
-  auto block_id = [&](int t) { return min(max(irow[t], 0), NB - 1); };
+  // block of list position min(t, k-1): past the end the last block is fetched again into a free
+  // buffer (keeps the copies branch-free; the data is never used).  Ids are valid by contract;
+  // clamping keeps a bad list from reading out of bounds.
+  auto block_id = [&](int t) {
+    if constexpr (kLists) return min(max(irow[min(t, k - 1)], 0), NB - 1);
+    else return tk.kbeg + min(t, k - 1);
+  };
 
   bf16x8 qreg[D / 16];
   {
@@ -130,14 +136,12 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) oacc[c] = f32x16{};
 
-  // copies of block min(t, k-1): past the end the last block is fetched again into a free buffer
-  // (keeps the copies branch-free so they schedule among the MFMAs; the data is never used)
-  auto fetch_k = [&](int t, char* dst) {
-    dma_tile<D, NW>(Kbh + (size_t)block_id(min(t, k - 1)) * kBlock * D, dst, wave, lane);
-  };
-  auto fetch_v = [&](int t, char* dst) {
-    dma_tile<D, NW>(Vbh + (size_t)block_id(min(t, k - 1)) * kBlock * D, dst, wave, lane);
-  };
+  auto fetch_k = [&](int j, char* dst) { dma_tile<D, NW>(Kbh + (size_t)j * kBlock * D, dst, wave, lane); };
+  auto fetch_v = [&](int j, char* dst) { dma_tile<D, NW>(Vbh + (size_t)j * kBlock * D, dst, wave, lane); };
+  // Block ids of the copies, read ahead: at step t, id_v = block of t+1, id_k = block of t+2 and
+  // id_pf = block of t+3 are in registers and the id of t+4 is being read, so no list read stands
+  // between a barrier and the copies it releases.
+  int id_v, id_k, id_pf;
   // S^T of one block: element e is key 32*kh + 8*(e/4) + 4*hh + e%4 of the block, query row l32
   auto s_tile = [&](const char* kt) {
     f32x16 acc = f32x16{};
@@ -161,8 +165,11 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
   auto step = [&](int t, const f32x16& sc, f32x16& sn, const char* kn, const char* vc, char* kfree, char* vfree) {
     wait_vmem();
     __syncthreads();  // K_{t+1}, V_t in LDS; every wave is done with K_t and V_{t-1}
-    fetch_k(t + 2, kfree);
-    fetch_v(t + 1, vfree);
+    fetch_k(id_k, kfree);
+    fetch_v(id_v, vfree);
+    id_v = id_k;
+    id_k = id_pf;
+    id_pf = block_id(t + 4);
     // lazy rescale: keep the running max unless block t exceeds it by 2^8
     if (__ballot(bm > m_used + 8.0f)) {
       const float m_new = fmaxf(m_used, bm);
@@ -191,9 +198,15 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
     bm = row_max(sn);
   };
 
-  fetch_k(0, kb0);
-  fetch_v(0, vb0);
-  fetch_k(1, kb1);
+  {
+    const int id0 = block_id(0);
+    id_v = block_id(1);
+    id_k = block_id(2);
+    id_pf = block_id(3);
+    fetch_k(id0, kb0);
+    fetch_v(id0, vb0);
+    fetch_k(id_v, kb1);
+  }
   wait_vmem();
   __syncthreads();
   f32x16 sa = s_tile(kb0), sb;
@@ -238,8 +251,8 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
   }
 }
 
-// fp32 operands: v_mfma_f32_32x32x2_f32, K and V row-major in LDS.
-template <int D, int G>
+// fp32 operands: v_mfma_f32_32x32x2_f32, K and V row-major in LDS.  kLists as for the bf16 kernel.
+template <int D, int G, bool kLists>
 __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                              const float* __restrict__ V,
                                                              const int32_t* __restrict__ idx, float* __restrict__ O,
@@ -256,7 +269,7 @@ __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __rest
   const FwdTask tk = fwd_task((uint32_t)task, NG, H, n_split, ht);
   const int g = tk.g, h = tk.h, b = tk.b;
   const int k = tk.klen;  // blocks of this part
-  const int32_t* irow = idx + row_base(ht, b, h, NG) + (int64_t)g * ht.k[h] + tk.kbeg;
+  const int32_t* irow = kLists ? idx + row_base(ht, b, h, NG) + (int64_t)g * ht.k[h] + tk.kbeg : nullptr;
   const size_t bh = (size_t)b * H + h;
   const float* Kbh = K + bh * (size_t)N * D;
   const float* Vbh = V + bh * (size_t)N * D;
@@ -284,7 +297,7 @@ __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __rest
 
   const int NB = N / kBlock;
   for (int t = 0; t < k; ++t) {
-    const int j = min(max(irow[t], 0), NB - 1);
+    const int j = kLists ? min(max(irow[t], 0), NB - 1) : tk.kbeg + t;
     __syncthreads();
     for (int e = threadIdx.x; e < 64 * D; e += NT) {
       const int m = e / D, c = e % D;
@@ -384,12 +397,14 @@ hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* 
   if (s.bf16) {
     const hipError_t e = launch_cvt_f16(V, V16, (int64_t)s.B * s.H * s.N * D, st);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, G>), grid, dim3(G * 4), 0, st, static_cast<const bf16_t*>(Q),
-                       static_cast<const bf16_t*>(K), V16, idx, O, LSE, ht, sp, s.N, s.H, s.B, n_split, scale_log2);
-  } else
-    hipLaunchKernelGGL((attn_fwd_f32_kernel<D, G>), grid, dim3(G * 2), 0, st, static_cast<const float*>(Q),
-                       static_cast<const float*>(K), static_cast<const float*>(V), idx, O, LSE, ht, sp, s.N, s.H,
-                       s.B, n_split, scale_log2);
+    auto kern = idx ? attn_fwd_bf16_kernel<D, G, true> : attn_fwd_bf16_kernel<D, G, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(G * 4), 0, st, static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K),
+                       V16, idx, O, LSE, ht, sp, s.N, s.H, s.B, n_split, scale_log2);
+  } else {
+    auto kern = idx ? attn_fwd_f32_kernel<D, G, true> : attn_fwd_f32_kernel<D, G, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(G * 2), 0, st, static_cast<const float*>(Q), static_cast<const float*>(K),
+                       static_cast<const float*>(V), idx, O, LSE, ht, sp, s.N, s.H, s.B, n_split, scale_log2);
+  }
   return hipGetLastError();
 }
 

@@ -84,7 +84,11 @@ const char* dsa_status_string(int status);
  */
 int dsa_index_layout(const dsa_problem* p, const int32_t* k_per_head, int64_t* row_base);
 
-/* Bytes of workspace the given call needs (0 if the arguments are invalid). */
+/*
+ * Bytes of workspace the given call needs (0 if the arguments are invalid).
+ * k_per_head may be NULL for DSA_WS_FWD and DSA_WS_BWD, whose sizes do not
+ * depend on it (the dense calls below take no kept counts).
+ */
 size_t dsa_workspace_bytes(const dsa_problem* p, const int32_t* k_per_head, int which_call);
 
 /*
@@ -210,6 +214,59 @@ int dsa_sparse_attn_bwd_dkdv(const dsa_problem* p, const int32_t* k_per_head, co
                              void* stream);
 int dsa_sparse_attn_bwd_dq(const dsa_problem* p, const int32_t* idx, const int32_t* k_per_head, float* dQ,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The OP dispatcher's branches (hi and nl §2.A, stage 2: per transformer
+ * block, sparse attention is switched on only when the block's sparsity
+ * exceeds a threshold set by offline profiling of speedup against memory
+ * overhead; otherwise the block keeps the full attention of stage 1).
+ *
+ * dsa_dense_attn_fwd -- full attention, every query over every key:
+ *   LSE_i = ln sum_m exp(tau Q_i.K_m),  O_i = sum_m exp(tau Q_i.K_m - LSE_i) V_m,
+ * i.e. dsa_sparse_attn_fwd with k_h = NB and every block kept, without index
+ * lists.  Same dtypes, layouts, workspace (DSA_WS_FWD, k_per_head NULL) and
+ * errors as dsa_sparse_attn_fwd.
+ */
+int dsa_dense_attn_fwd(const dsa_problem* p, const void* Q, const void* K, const void* V, float* O,
+                       float* LSE, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_dense_attn_bwd -- gradient of sum(dO * O) for dsa_dense_attn_fwd (the
+ * formulas of dsa_sparse_attn_bwd over all keys).  bf16 inputs only;
+ * workspace DSA_WS_BWD (k_per_head NULL); deterministic.
+ */
+int dsa_dense_attn_bwd(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
+                       const void* dO, const float* LSE, float* dQ, float* dK, float* dV, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+typedef enum { DSA_PATH_DENSE = 0, DSA_PATH_SPARSE = 1 } dsa_path;
+
+/*
+ * Sparsity above which the sparse training step (predict, select, forward,
+ * backward) beats the dense one (forward, backward) on these kernels: a
+ * sweep of the kept fraction on MI355X put the break-even at a sparsity of
+ * 0.06 for a 57,600-token, 24-head, d = 128 layer and at 0 for an
+ * 8,192-token, 16-head, d = 64 one (the larger is taken).  Forward-only
+ * callers (break-even 0.03 and 0.09 there), or callers with their own
+ * profile, pass their own threshold.
+ */
+#define DSA_DEFAULT_MIN_SPARSITY 0.06
+
+/*
+ * dsa_choose_path -- the dispatcher's decision for one attention layer (host
+ * only; reads k_per_head, launches nothing).  With the sparsity
+ *   s = 1 - sum_h k_h / (H * NB)   (the fraction of (head, group, block)
+ *                                   tiles the selection skips),
+ * returns DSA_PATH_SPARSE iff s > min_sparsity, the kept lists fit the sparse
+ * calls' limits, and (when max_sparse_bytes > 0) the device memory the sparse
+ * path needs beyond the dense one -- qhat, khat, idx, rev_ptr, rev_idx and the
+ * DSA_WS_SELECT workspace, block scores streamed -- is at most
+ * max_sparse_bytes; otherwise DSA_PATH_DENSE.  min_sparsity < 0 (or NaN)
+ * selects DSA_DEFAULT_MIN_SPARSITY.  Negative status on invalid arguments
+ * (k_h outside [1, NB]: DSA_ERR_SHAPE).
+ */
+int dsa_choose_path(const dsa_problem* p, const int32_t* k_per_head, double min_sparsity,
+                    size_t max_sparse_bytes);
 
 #ifdef __cplusplus
 }

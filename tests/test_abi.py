@@ -148,3 +148,83 @@ def test_split_and_merge_validation():
     assert lib.dsa_attn_merge(pc, 2, FAKE, FAKE, None, FAKE, None) == -1
     assert lib.dsa_attn_merge(pc, 2, FAKE, FAKE, FAKE, bad, None) == -4
     assert lib.dsa_attn_merge(ctypes.byref(_p(head_dim=96).c()), 2, FAKE, FAKE, FAKE, FAKE, None) == -5
+
+
+def test_dense_calls_validation():
+    lib = dsa.library()
+    big = 1 << 40
+    p = _p()
+    pc = ctypes.byref(p.c())
+    # forward: null, misaligned, missing workspace (bf16 needs one), bad problem
+    assert lib.dsa_dense_attn_fwd(pc, None, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    assert lib.dsa_dense_attn_fwd(pc, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == -1
+    assert lib.dsa_dense_attn_fwd(pc, FAKE, ctypes.c_void_p(0x100004), FAKE, FAKE, FAKE, FAKE, big, None) == -4
+    assert lib.dsa_dense_attn_fwd(pc, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -6
+    need = dsa.workspace_bytes(p, None, dsa.DSA_WS_FWD)
+    assert need == dsa.workspace_bytes(p, [3, 5], dsa.DSA_WS_FWD) > 0
+    assert lib.dsa_dense_attn_fwd(pc, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == -6
+    assert lib.dsa_dense_attn_fwd(ctypes.byref(_p(head_dim=96).c()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big,
+                                  None) == -5
+    assert lib.dsa_dense_attn_fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, big, None) == -1
+    # backward: bf16 only, nine tensors, DSA_WS_BWD
+    args = [FAKE] * 9
+    f32 = ctypes.byref(_p(dtype=dsa.DSA_F32).c())
+    assert lib.dsa_dense_attn_bwd(f32, *args, FAKE, big, None) == -3
+    for i in range(9):
+        bad = list(args)
+        bad[i] = None
+        assert lib.dsa_dense_attn_bwd(pc, *bad, FAKE, big, None) == -1, i
+        bad[i] = ctypes.c_void_p(0x100008)
+        assert lib.dsa_dense_attn_bwd(pc, *bad, FAKE, big, None) == -4, i
+    need = dsa.workspace_bytes(p, None, dsa.DSA_WS_BWD)
+    assert need == dsa.workspace_bytes(p, [16, 16], dsa.DSA_WS_BWD) > 0
+    assert lib.dsa_dense_attn_bwd(pc, *args, FAKE, need - 1, None) == -6
+    assert lib.dsa_dense_attn_bwd(pc, *args, None, big, None) == -6
+    # the selection workspace still needs the kept counts
+    assert dsa.workspace_bytes(p, None, dsa.DSA_WS_SELECT) == 0
+
+
+def _sparsity(kph, nb):
+    return 1.0 - sum(kph) / (len(kph) * nb)
+
+
+def test_default_threshold_matches_header():
+    text = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    assert float(re.search(r"#define DSA_DEFAULT_MIN_SPARSITY ([0-9.]+)", text).group(1)) == dsa.DEFAULT_MIN_SPARSITY
+
+
+def test_choose_path_rule():
+    p = _p(heads=3)                    # NB = 16
+    for kph in ([16, 16, 16], [15, 16, 16], [8, 8, 8], [1, 1, 1], [2, 16, 9], [14, 14, 14]):
+        for thr in (0.0, 0.01, 0.1, 0.5, 0.9):
+            want = dsa.PATH_SPARSE if _sparsity(kph, 16) > thr else dsa.PATH_DENSE
+            assert dsa.choose_path(p, kph, thr) == want, (kph, thr)
+    assert dsa.choose_path(p, [8, 8, 8], 0.5) == dsa.PATH_DENSE       # exactly at the threshold
+    # the default threshold (any negative value, or NaN)
+    lib = dsa.library()
+    for kph in ([16, 16, 16], [15, 16, 16], [15, 15, 15], [14, 15, 15], [1, 1, 1]):   # sparsity 0 .. 0.94
+        for thr in (-1.0, float("nan")):
+            got = lib.dsa_choose_path(ctypes.byref(p.c()), dsa._kph(kph), thr, 0)
+            assert got == (dsa.PATH_SPARSE if _sparsity(kph, 16) > dsa.DEFAULT_MIN_SPARSITY else dsa.PATH_DENSE)
+    # invalid arguments
+    assert lib.dsa_choose_path(ctypes.byref(p.c()), None, 0.1, 0) == -1
+    assert lib.dsa_choose_path(None, dsa._kph([1, 1, 1]), 0.1, 0) == -1
+    assert lib.dsa_choose_path(ctypes.byref(p.c()), dsa._kph([0, 1, 1]), 0.1, 0) == -2
+    assert lib.dsa_choose_path(ctypes.byref(p.c()), dsa._kph([1, 17, 1]), 0.1, 0) == -2
+    with pytest.raises(dsa.DsaError):
+        dsa.choose_path(_p(head_dim=96), [1, 1], 0.1)
+
+
+def test_choose_path_memory_cap():
+    # sparse extras: qhat + khat, idx + rev_idx, rev_ptr, the selection workspace
+    p = _p(heads=2)                    # NG = NB = 16, r = 16
+    kph = [4, 4]
+    ws = dsa.workspace_bytes(p, kph, dsa.DSA_WS_SELECT)
+    extra = 2 * (16 + 16) * 16 * 4 + 2 * 16 * 8 * 4 + 2 * 17 * 4 + ws
+    assert dsa.choose_path(p, kph, 0.1, extra) == dsa.PATH_SPARSE
+    assert dsa.choose_path(p, kph, 0.1, extra - 1) == dsa.PATH_DENSE
+    assert dsa.choose_path(p, kph, 0.1, 0) == dsa.PATH_SPARSE         # 0: no cap
+    # kept lists beyond the sparse calls' index range: dense
+    big = _p(heads=128, seq_len=64 * 8192, group=64)
+    assert dsa.choose_path(big, [4096] * 128, 0.1) == dsa.PATH_DENSE
+    assert dsa.choose_path(big, [8] * 128, 0.1) == dsa.PATH_SPARSE

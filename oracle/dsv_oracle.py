@@ -28,6 +28,9 @@ groups of consecutive tokens):
    and, for the OP dispatcher's other branch, full (dense) attention over all
    keys, with the dispatcher's rule: sparse iff the skipped fraction of
    (head, group, block) tiles exceeds a threshold   [hi §2.A, nl §2.A stage 2]
+7. stage-1 predictor training: a loss on the row-centred difference between
+   the block scores and the true pooled logits, and its gradient with respect
+   to W_q and W_k                                    [hi §2.A, nl §2.A stage 1]
 6. the gradient of L = sum(dO * O) with the selection held fixed: dQ, dK, dV
    (keys in no kept block get exactly zero).  The pages call the method a
    training system but never write the backward out; this is the standard
@@ -384,3 +387,49 @@ def sparsity(k_per_head: Sequence[int], n_blocks: int) -> float:
 def use_sparse(k_per_head: Sequence[int], n_blocks: int, threshold: float) -> bool:
     """The dispatcher's rule: sparse attention iff the sparsity exceeds the threshold."""
     return sparsity(k_per_head, n_blocks) > threshold
+
+
+# ----------------------------------------------------------------------------
+# Stage 1: training the predictor (hi §2.A stage 1, nl §2.A fase 1: the
+# low-rank predictors are trained for every head in parallel with the normal,
+# full-attention training, through a loss that keeps the relative magnitude of
+# the estimated scores)
+# ----------------------------------------------------------------------------
+
+def predictor_loss_head(q, k, wq, wk, group, block=BLOCK):
+    """Loss of one (b, h).  With the predictor's block scores S = tau qhat khat^T and the true pooled
+    logits T = tau qbar kbar^T (qbar, kbar the group and block means: T is the mean of tau Q K^T over each
+    G x 64 tile), E = (S - T) minus each row's mean, and L = mean over the NG x NB entries of E^2.  Removing
+    the row mean keeps only the relative magnitudes within a row, the part a softmax and a top-k see.
+    Returns (L, E, qbar, kbar, qhat, khat)."""
+    tau = 1.0 / np.sqrt(q.shape[1])
+    qbar, kbar = pool_mean(q, group), pool_mean(k, block)
+    qhat, khat = qbar @ wq, kbar @ wk
+    diff = tau * (qhat @ khat.T) - tau * (qbar @ kbar.T)
+    e = diff - diff.mean(axis=1, keepdims=True)
+    return float((e * e).mean()), e, qbar, kbar, qhat, khat
+
+
+def predictor_loss_grad_head(q, k, wq, wk, group, block=BLOCK):
+    """(L, dL/dW_q, dL/dW_k) of one (b, h).  dL/dS = 2 E / (NG NB) (E already has zero row means, so the
+    mean removal adds nothing), S = tau (qbar W_q)(kbar W_k)^T: dW_q = tau qbar^T dS khat,
+    dW_k = tau kbar^T dS^T qhat."""
+    tau = 1.0 / np.sqrt(q.shape[1])
+    loss, e, qbar, kbar, qhat, khat = predictor_loss_head(q, k, wq, wk, group, block)
+    ds = 2.0 * e / e.size
+    return loss, tau * (qbar.T @ (ds @ khat)), tau * (kbar.T @ (ds.T @ qhat))
+
+
+def predictor_loss_grad(q, k, wq, wk, group, block=BLOCK):
+    """Per head h, averaged over the batch: loss [H], dW_q [H, d, r], dW_k [H, d, r] for inputs
+    [B, H, N, d] and weights [H, d, r]."""
+    B, H = q.shape[:2]
+    loss = np.zeros(H)
+    dwq, dwk = np.zeros(wq.shape), np.zeros(wk.shape)
+    for h in range(H):
+        for b in range(B):
+            l, gq, gk = predictor_loss_grad_head(q[b, h], k[b, h], wq[h], wk[h], group, block)
+            loss[h] += l / B
+            dwq[h] += gq / B
+            dwk[h] += gk / B
+    return loss, dwq, dwk

@@ -373,6 +373,59 @@ def check_dispatch_rule():
     assert O.use_sparse([1], 2, 0.0) and not O.use_sparse([1], 2, 0.5)
 
 
+def _brute_pred_loss(q, k, wq, wk, group):
+    # from the full N x N predicted and true logit matrices, averaged per tile (tests/brute.py)
+    diff = brute.tile_mean_scores(q, k, wq, wk, group) - brute.true_tile_mean(q, k, group)
+    e = diff - diff.mean(axis=1, keepdims=True)
+    return float((e * e).mean())
+
+
+def check_pred_loss_brute(seed=41, n=256, d=8, r=4, group=64):
+    q, k, _, _, wq, wk = _tiny(seed, n=n, d=d, r=r)
+    loss, gq, gk = O.predictor_loss_grad_head(q, k, wq, wk, group)
+    assert abs(loss - _brute_pred_loss(q, k, wq, wk, group)) <= 1e-12 * max(1.0, loss)
+    # central differences of the brute-force loss, entry by entry
+    h = 1e-6
+    for w, g, which in ((wq, gq, 0), (wk, gk, 1)):
+        fd = np.zeros_like(w)
+        for ix in np.ndindex(*w.shape):
+            wp, wm = w.copy(), w.copy()
+            wp[ix] += h
+            wm[ix] -= h
+            args_p = (wp, wk) if which == 0 else (wq, wp)
+            args_m = (wm, wk) if which == 0 else (wq, wm)
+            fd[ix] = (_brute_pred_loss(q, k, *args_p, group) - _brute_pred_loss(q, k, *args_m, group)) / (2 * h)
+        np.testing.assert_allclose(g, fd, rtol=1e-5, atol=1e-9)
+
+
+def check_pred_loss_closed_forms(seed=42, n=384, d=8, group=128):
+    q, k, _, _, _, _ = _tiny(seed, n=n, d=d, r=d)
+    eye = np.eye(d)
+    loss, gq, gk = O.predictor_loss_grad_head(q, k, eye, eye, group)   # full-rank identity: S = T
+    assert loss < 1e-28 and np.abs(gq).max() < 1e-14 and np.abs(gk).max() < 1e-14
+    # a zero predictor: L is the mean square of the row-centred true pooled logits
+    z = np.zeros((d, 3))
+    t = brute.true_tile_mean(q, k, group)
+    tc = t - t.mean(axis=1, keepdims=True)
+    loss0, _, _ = O.predictor_loss_grad_head(q, k, z, z, group)
+    assert abs(loss0 - float((tc * tc).mean())) <= 1e-12 * loss0
+    # shifting every key by one vector moves each row of S and T by a constant: L is unchanged
+    rng = _rng(seed)
+    wq, wk = rng.standard_normal((d, 3)), rng.standard_normal((d, 3))
+    c = rng.standard_normal(d) * 3.0
+    l1, g1q, g1k = O.predictor_loss_grad_head(q, k, wq, wk, group)
+    l2, g2q, _ = O.predictor_loss_grad_head(q, k + c, wq, wk, group)
+    assert abs(l1 - l2) <= 1e-11 * l1
+    np.testing.assert_allclose(g2q, g1q, rtol=1e-9, atol=1e-12)
+    # batched form: the mean over the batch of the per-(b, h) values
+    qb, kb = np.stack([q, q[::-1]])[:, None], np.stack([k, k[::-1]])[:, None]
+    lb, gbq, gbk = O.predictor_loss_grad(qb, kb, wq[None], wk[None], group)
+    l_r, gq_r, gk_r = O.predictor_loss_grad_head(q[::-1], k[::-1], wq, wk, group)
+    np.testing.assert_allclose(lb[0], 0.5 * (l1 + l_r), rtol=1e-13)
+    np.testing.assert_allclose(gbq[0], 0.5 * (g1q + gq_r), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(gbk[0], 0.5 * (g1k + gk_r), rtol=1e-12, atol=1e-15)
+
+
 ALL_CHECKS = [
     check_scores_brute, check_identity_predictor, check_select_brute, check_select_special,
     check_duplicate_blocks_tie, check_linearity, check_forward_brute, check_dense_equals_sdpa,
@@ -380,6 +433,7 @@ ALL_CHECKS = [
     check_sampled_match_full, check_reverse_index, check_batched_api, check_split_bounds,
     check_split_merge_equals_unsplit, check_partial_states_brute, check_merge_algebra, check_dense_sdpa,
     check_dense_brute, check_dense_closed_forms, check_dense_sampled, check_dispatch_rule,
+    check_pred_loss_brute, check_pred_loss_closed_forms,
 ]
 
 
@@ -549,3 +603,44 @@ def test_mutation_dispatch_at_threshold(monkeypatch):
     def bad(k_per_head, n_blocks, threshold):
         return O.sparsity(k_per_head, n_blocks) >= threshold
     assert _fails_some_pin(monkeypatch, "use_sparse", bad, [check_dispatch_rule])
+
+
+def test_mutation_pred_loss_no_centring(monkeypatch):
+    def bad(q, k, wq, wk, group, block=64):
+        tau = 1.0 / np.sqrt(q.shape[1])
+        qbar, kbar = O.pool_mean(q, group), O.pool_mean(k, block)
+        qhat, khat = qbar @ wq, kbar @ wk
+        e = tau * (qhat @ khat.T) - tau * (qbar @ kbar.T)
+        return float((e * e).mean()), e, qbar, kbar, qhat, khat
+    assert _fails_some_pin(monkeypatch, "predictor_loss_head", bad,
+                           [check_pred_loss_brute, check_pred_loss_closed_forms])
+
+
+def test_mutation_pred_loss_centres_columns(monkeypatch):
+    def bad(q, k, wq, wk, group, block=64):
+        tau = 1.0 / np.sqrt(q.shape[1])
+        qbar, kbar = O.pool_mean(q, group), O.pool_mean(k, block)
+        qhat, khat = qbar @ wq, kbar @ wk
+        diff = tau * (qhat @ khat.T) - tau * (qbar @ kbar.T)
+        e = diff - diff.mean(axis=0, keepdims=True)
+        return float((e * e).mean()), e, qbar, kbar, qhat, khat
+    assert _fails_some_pin(monkeypatch, "predictor_loss_head", bad,
+                           [check_pred_loss_brute, check_pred_loss_closed_forms])
+
+
+def test_mutation_pred_grad_swapped(monkeypatch):
+    def bad(q, k, wq, wk, group, block=64):
+        tau = 1.0 / np.sqrt(q.shape[1])
+        loss, e, qbar, kbar, qhat, khat = O.predictor_loss_head(q, k, wq, wk, group, block)
+        ds = 2.0 * e / e.size
+        return loss, tau * (kbar.T @ (ds.T @ qhat)), tau * (qbar.T @ (ds @ khat))
+    assert _fails_some_pin(monkeypatch, "predictor_loss_grad_head", bad, [check_pred_loss_brute])
+
+
+def test_mutation_pred_grad_half(monkeypatch):
+    def bad(q, k, wq, wk, group, block=64):
+        tau = 1.0 / np.sqrt(q.shape[1])
+        loss, e, qbar, kbar, qhat, khat = O.predictor_loss_head(q, k, wq, wk, group, block)
+        ds = e / e.size                       # the factor 2 of d(e^2) dropped
+        return loss, tau * (qbar.T @ (ds @ khat)), tau * (kbar.T @ (ds.T @ qhat))
+    assert _fails_some_pin(monkeypatch, "predictor_loss_grad_head", bad, [check_pred_loss_brute])

@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--dispatch-sweep", action="store_true",
                     help="also time dense attention against the sparse step over a sweep of keep fractions "
                          "(the dispatcher's break-even sparsity)")
+    ap.add_argument("--predictor-grad", action="store_true",
+                    help="also time the stage-1 predictor loss + gradient call on the same inputs")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -157,6 +159,34 @@ def time_split_kv(args, p, plan, Q, K, V, stream, fwd_ms, f_fwd, w):
             "fwd_split_tflops": round(f_fwd / (sm / 1e3) / 1e12, 2), "unsplit_fwd_ms": round(fwd_ms, 4),
             "merge_hbm_gbs": round(merge_bytes / (mm / 1e3) / 1e9, 1), "merge_hbm_frac": round(
                 merge_bytes / (mm / 1e3) / PEAK_HBM, 4)}
+
+
+def time_predictor_grad(args, p, Q, K, Wt, stream, w):
+    """dsa_predictor_loss_grad on the step's Q, K and predictor weights, timed with HIP events on the bench
+    stream.  Algorithmic HBM bytes: Q and K read once (everything else is B H (NG + NB) (d + r) floats plus
+    the NG x NB difference matrix, which the call writes once and reads three times)."""
+    import torch
+    import dynamic_sparse_attention_qk_amd as dsa
+    loss = torch.empty(w.heads, dtype=torch.float32, device=Q.device)
+    dWq, dWk = torch.empty_like(Wt), torch.empty_like(Wt)
+    ws = torch.empty(dsa.workspace_bytes(p, None, dsa.DSA_WS_PRED_GRAD), dtype=torch.uint8, device=Q.device)
+    ms = []
+    for i in range(args.warmup + args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dsa.predictor_loss_grad(p, Q, K, Wt, Wt, loss, dWq, dWk, ws, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            ms.append(e0.elapsed_time(e1))
+    elt = 2 if w.dtype == "bf16" else 4
+    qk_bytes = 2 * w.batch * w.heads * w.seq_len * w.head_dim * elt
+    e_bytes = 4 * w.batch * w.heads * w.n_groups * w.n_blocks * 4
+    t = float(np.mean(ms))
+    return {"ms": round(t, 4), "qk_read_gb": round(qk_bytes / 1e9, 4),
+            "hbm_gbs_algorithmic": round(qk_bytes / (t / 1e3) / 1e9, 1),
+            "hbm_frac_algorithmic": round(qk_bytes / (t / 1e3) / PEAK_HBM, 4),
+            "hbm_gbs_with_diff_matrix": round((qk_bytes + e_bytes) / (t / 1e3) / 1e9, 1)}
 
 
 SWEEP_KEEP = (0.02, 0.05, 0.1, 0.2, 0.3, 0.5, 0.7, 0.8, 0.9, 0.95, 1.0)
@@ -374,6 +404,8 @@ def main():
     }
     if args.split_kv:
         rec["split_kv"] = time_split_kv(args, p, plan, Q, K, V, stream, stage_ms["fwd"], f_fwd, w)
+    if args.predictor_grad:
+        rec["predictor_grad"] = time_predictor_grad(args, p, Q, K, Wt, stream, w)
     if args.dispatch_sweep:
         del plan
         torch.cuda.empty_cache()

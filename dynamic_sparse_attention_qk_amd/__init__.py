@@ -28,7 +28,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdsa.so")
 
 DSA_F32, DSA_BF16 = 0, 1
-DSA_WS_SELECT, DSA_WS_BWD, DSA_WS_FWD = 0, 1, 2
+DSA_WS_SELECT, DSA_WS_BWD, DSA_WS_FWD, DSA_WS_PRED_GRAD = 0, 1, 2, 3
 
 
 class DsaError(RuntimeError):
@@ -77,10 +77,12 @@ def library() -> ctypes.CDLL:
         lib.dsa_dense_attn_fwd.argtypes = [pp, vp, vp, vp, f32p, f32p, vp, sz, vp]
         lib.dsa_dense_attn_bwd.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, f32p, f32p, f32p, vp, sz, vp]
         lib.dsa_choose_path.argtypes = [pp, kph, ctypes.c_double, sz]
+        lib.dsa_predictor_loss_grad.argtypes = [pp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp, sz, vp]
         for name in ("dsa_index_layout", "dsa_predict_block_scores", "dsa_select_topk_blocks",
                      "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_preprocess",
                      "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_fwd_split",
-                     "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd", "dsa_choose_path"):
+                     "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd", "dsa_choose_path",
+                     "dsa_predictor_loss_grad"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -90,7 +92,7 @@ EXPORTED = ("dsa_version", "dsa_status_string", "dsa_index_layout", "dsa_workspa
             "dsa_predict_block_scores", "dsa_select_topk_blocks", "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd",
             "dsa_sparse_attn_bwd_preprocess", "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq",
             "dsa_sparse_attn_fwd_split", "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd",
-            "dsa_choose_path")
+            "dsa_choose_path", "dsa_predictor_loss_grad")
 MAX_SPLIT = 64  # DSA_MAX_SPLIT
 PATH_DENSE, PATH_SPARSE = 0, 1  # dsa_path
 DEFAULT_MIN_SPARSITY = 0.06     # DSA_DEFAULT_MIN_SPARSITY
@@ -161,7 +163,7 @@ def index_layout(p: Problem, k_per_head: Sequence[int]) -> np.ndarray:
 
 
 def workspace_bytes(p: Problem, k_per_head: Optional[Sequence[int]], which: int) -> int:
-    """Workspace bytes of a call; k_per_head may be None for DSA_WS_FWD / DSA_WS_BWD."""
+    """Workspace bytes of a call; k_per_head may be None for DSA_WS_FWD / DSA_WS_BWD / DSA_WS_PRED_GRAD."""
     kph = None if k_per_head is None else _kph(k_per_head)
     return int(library().dsa_workspace_bytes(ctypes.byref(p.c()), kph, which))
 
@@ -215,6 +217,13 @@ def dense_attn_bwd(p: Problem, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, strea
     _check("dsa_dense_attn_bwd", library().dsa_dense_attn_bwd(
         ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV),
         _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def predictor_loss_grad(p: Problem, Q, K, Wq, Wk, loss, dWq, dWk, workspace, stream=None) -> None:
+    """Stage-1 predictor training: loss [H] and its gradients dWq, dWk [H, d, r] (all fp32)."""
+    _check("dsa_predictor_loss_grad", library().dsa_predictor_loss_grad(
+        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(loss), _ptr(dWq), _ptr(dWk), _ptr(workspace),
+        _nbytes(workspace), _stream(stream)))
 
 
 def choose_path(p: Problem, k_per_head: Sequence[int], min_sparsity: float = -1.0, max_sparse_bytes: int = 0) -> int:

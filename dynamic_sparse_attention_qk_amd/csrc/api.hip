@@ -83,6 +83,36 @@ dsa::BwdWork bwd_work(const Shape& s, void* ws) {
   return w;
 }
 
+// stage-1 predictor training: the means, projections, E and the partial sums of PredWork
+size_t pred_ws(const Shape& s) {
+  const size_t BH = (size_t)s.B * s.H;
+  return align256(BH * s.NG * s.D * 4) + align256(BH * s.NB * s.D * 4) + align256(BH * s.NG * s.R * 4) +
+         align256(BH * s.NB * s.R * 4) + align256(BH * s.NG * s.NB * 4) + align256(BH * s.NG * s.R * 4) +
+         align256(BH * s.NB * s.R * 4) + align256(BH * s.NG * 4) +
+         align256((size_t)s.H * 2 * dsa::kPredWgParts * s.D * s.R * 4);
+}
+
+dsa::PredWork pred_work(const Shape& s, void* ws) {
+  const size_t BH = (size_t)s.B * s.H;
+  char* p = static_cast<char*>(ws);
+  auto take = [&](size_t bytes) {
+    float* f = reinterpret_cast<float*>(p);
+    p += align256(bytes);
+    return f;
+  };
+  dsa::PredWork w;
+  w.qbar = take(BH * s.NG * s.D * 4);
+  w.kbar = take(BH * s.NB * s.D * 4);
+  w.qhat = take(BH * s.NG * s.R * 4);
+  w.khat = take(BH * s.NB * s.R * 4);
+  w.E = take(BH * s.NG * s.NB * 4);
+  w.Y = take(BH * s.NG * s.R * 4);
+  w.Z = take(BH * s.NB * s.R * 4);
+  w.lrow = take(BH * s.NG * 4);
+  w.part = take((size_t)s.H * 2 * dsa::kPredWgParts * s.D * s.R * 4);
+  return w;
+}
+
 // forward: an fp16 copy of V (bf16 inputs only)
 size_t fwd_ws(const Shape& s) { return s.bf16 ? align256((size_t)s.B * s.H * s.N * s.D * 2) : 0; }
 
@@ -146,6 +176,7 @@ size_t dsa_workspace_bytes(const dsa_problem* p, const int32_t* k_per_head, int 
   // the forward and backward workspaces do not depend on the kept counts (dense calls pass none)
   if (!k_per_head && which_call == DSA_WS_FWD) return fwd_ws(s);
   if (!k_per_head && which_call == DSA_WS_BWD) return bwd_ws(s);
+  if (which_call == DSA_WS_PRED_GRAD) return pred_ws(s);
   if (check_heads(s, k_per_head, &ht, nullptr)) return 0;
   if (which_call == DSA_WS_SELECT) return select_ws(s, ht);
   if (which_call == DSA_WS_BWD) return bwd_ws(s);
@@ -355,6 +386,23 @@ int dsa_dense_attn_bwd(const dsa_problem* p, const void* Q, const void* K, const
   if (e == hipSuccess) e = dsa::launch_bwd_dkdv(s, w, nullptr, nullptr, dK, dV, ht, hs);
   if (e == hipSuccess) e = dsa::launch_bwd_dq(s, w, nullptr, dQ, ht, hs);
   return hip_status(e);
+}
+
+int dsa_predictor_loss_grad(const dsa_problem* p, const void* Q, const void* K, const float* Wq, const float* Wk,
+                            float* loss, float* dWq, float* dWk, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  Shape s;
+  int st = check_problem(p, &s);
+  if (st) return st;
+  if (!Q || !K || !Wq || !Wk || !loss || !dWq || !dWk) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(loss) || !aligned16(dWq) ||
+      !aligned16(dWk))
+    return DSA_ERR_ALIGN;
+  if ((size_t)s.B * s.H * s.NG * s.NB >= ((size_t)1 << 31)) return DSA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < pred_ws(s)) return DSA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DSA_ERR_ALIGN;
+  return hip_status(dsa::launch_predictor_loss_grad(s, Q, K, Wq, Wk, pred_work(s, workspace), loss, dWq, dWk,
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 int dsa_choose_path(const dsa_problem* p, const int32_t* k_per_head, double min_sparsity, size_t max_sparse_bytes) {

@@ -14,8 +14,9 @@ struct Shape {
   bool bf16;
 };
 
+// out = pooled means projected by W; mean_out (if not null) also receives the means [B, H, N / pool, d]
 hipError_t launch_pool_project(const Shape& s, const void* X, const float* W, float* out, int pool,
-                               hipStream_t st);
+                               hipStream_t st, float* mean_out = nullptr);
 hipError_t launch_block_scores(const Shape& s, const float* qhat, const float* khat, float* scores,
                                float tau, hipStream_t st);
 hipError_t launch_topk_select(const Shape& s, const float* scores, const float* qhat, const float* khat,
@@ -45,5 +46,23 @@ hipError_t launch_bwd_dkdv(const Shape& s, const BwdWork& w, const int32_t* rev_
                            float* dK, float* dV, const HeadTable& ht, hipStream_t st);
 hipError_t launch_bwd_dq(const Shape& s, const BwdWork& w, const int32_t* idx, float* dQ, const HeadTable& ht,
                          hipStream_t st);
+
+// Stage-1 predictor training workspace (fp32): qbar [B,H,NG,d], kbar [B,H,NB,d], qhat [B,H,NG,r],
+// khat [B,H,NB,r], E [B,H,NG,NB], Y [B,H,NG,r], Z [B,H,NB,r], lrow [B,H,NG], part [H,2,16,d,r].
+constexpr int kPredWgParts = 16;
+struct PredWork {
+  float* qbar;
+  float* kbar;
+  float* qhat;
+  float* khat;
+  float* E;
+  float* Y;
+  float* Z;
+  float* lrow;
+  float* part;
+};
+
+hipError_t launch_predictor_loss_grad(const Shape& s, const void* Q, const void* K, const float* Wq, const float* Wk,
+                                      const PredWork& w, float* loss, float* dWq, float* dWk, hipStream_t st);
 
 }  // namespace dsa

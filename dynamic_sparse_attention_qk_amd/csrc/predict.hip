@@ -18,7 +18,8 @@ constexpr int kPoolGroupsPerWG = 8;  // 2 rounds of 4 waves
 template <typename T, int D, int R>
 __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(const T* __restrict__ X,
                                                                      const float* __restrict__ W,
-                                                                     float* __restrict__ out, int N, int P,
+                                                                     float* __restrict__ out,
+                                                                     float* __restrict__ mean_out, int N, int P,
                                                                      int H) {
   constexpr int VE = 16 / sizeof(T);  // elements per 16-byte vector
   constexpr int VR = D / VE;          // vectors per row
@@ -68,9 +69,17 @@ __global__ __launch_bounds__(kPoolThreads) void pool_project_kernel(const T* __r
       for (int off = VR; off < 64; off <<= 1)
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[e] += __shfl_xor(acc[e], off);
-      if (r0 == 0)
+      if (r0 == 0) {
 #pragma unroll
         for (int e = 0; e < VE; ++e) smean[wave][cv * VE + e] = acc[e] * inv;
+        if (mean_out) {
+          float* mo = mean_out + (bh * npool + g) * D + cv * VE;
+#pragma unroll
+          for (int e = 0; e < VE; e += 4)
+            *reinterpret_cast<float4*>(mo + e) = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv,
+                                                             acc[e + 3] * inv);
+        }
+      }
     }
     __syncthreads();
     if (valid) {
@@ -129,14 +138,16 @@ __global__ __launch_bounds__(kScoreCols) void block_scores_kernel(const float* _
 }
 
 template <typename T, int D>
-hipError_t pool_dispatch_r(const Shape& s, const T* X, const float* W, float* out, int pool, hipStream_t st) {
+hipError_t pool_dispatch_r(const Shape& s, const T* X, const float* W, float* out, float* mean_out, int pool,
+                           hipStream_t st) {
   const int npool = s.N / pool;
   dim3 grid((npool + kPoolGroupsPerWG - 1) / kPoolGroupsPerWG, s.H, s.B);
+  dim3 blk(kPoolThreads);
   switch (s.R) {
-    case 8: hipLaunchKernelGGL((pool_project_kernel<T, D, 8>), grid, dim3(kPoolThreads), 0, st, X, W, out, s.N, pool, s.H); break;
-    case 16: hipLaunchKernelGGL((pool_project_kernel<T, D, 16>), grid, dim3(kPoolThreads), 0, st, X, W, out, s.N, pool, s.H); break;
-    case 32: hipLaunchKernelGGL((pool_project_kernel<T, D, 32>), grid, dim3(kPoolThreads), 0, st, X, W, out, s.N, pool, s.H); break;
-    case 64: hipLaunchKernelGGL((pool_project_kernel<T, D, 64>), grid, dim3(kPoolThreads), 0, st, X, W, out, s.N, pool, s.H); break;
+    case 8: hipLaunchKernelGGL((pool_project_kernel<T, D, 8>), grid, blk, 0, st, X, W, out, mean_out, s.N, pool, s.H); break;
+    case 16: hipLaunchKernelGGL((pool_project_kernel<T, D, 16>), grid, blk, 0, st, X, W, out, mean_out, s.N, pool, s.H); break;
+    case 32: hipLaunchKernelGGL((pool_project_kernel<T, D, 32>), grid, blk, 0, st, X, W, out, mean_out, s.N, pool, s.H); break;
+    case 64: hipLaunchKernelGGL((pool_project_kernel<T, D, 64>), grid, blk, 0, st, X, W, out, mean_out, s.N, pool, s.H); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -145,13 +156,15 @@ hipError_t pool_dispatch_r(const Shape& s, const T* X, const float* W, float* ou
 }  // namespace
 
 hipError_t launch_pool_project(const Shape& s, const void* X, const float* W, float* out, int pool,
-                               hipStream_t st) {
+                               hipStream_t st, float* mean_out) {
   if (s.bf16) {
     const bf16_t* x = static_cast<const bf16_t*>(X);
-    return s.D == 64 ? pool_dispatch_r<bf16_t, 64>(s, x, W, out, pool, st) : pool_dispatch_r<bf16_t, 128>(s, x, W, out, pool, st);
+    return s.D == 64 ? pool_dispatch_r<bf16_t, 64>(s, x, W, out, mean_out, pool, st)
+                     : pool_dispatch_r<bf16_t, 128>(s, x, W, out, mean_out, pool, st);
   }
   const float* x = static_cast<const float*>(X);
-  return s.D == 64 ? pool_dispatch_r<float, 64>(s, x, W, out, pool, st) : pool_dispatch_r<float, 128>(s, x, W, out, pool, st);
+  return s.D == 64 ? pool_dispatch_r<float, 64>(s, x, W, out, mean_out, pool, st)
+                   : pool_dispatch_r<float, 128>(s, x, W, out, mean_out, pool, st);
 }
 
 hipError_t launch_block_scores(const Shape& s, const float* qhat, const float* khat, float* scores, float tau,

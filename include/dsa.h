@@ -69,7 +69,7 @@ typedef struct {
 } dsa_problem;
 
 /* Which call a workspace is sized for. */
-typedef enum { DSA_WS_SELECT = 0, DSA_WS_BWD = 1, DSA_WS_FWD = 2 } dsa_ws_call;
+typedef enum { DSA_WS_SELECT = 0, DSA_WS_BWD = 1, DSA_WS_FWD = 2, DSA_WS_PRED_GRAD = 3 } dsa_ws_call;
 
 /* Library version string. */
 const char* dsa_version(void);
@@ -86,8 +86,9 @@ int dsa_index_layout(const dsa_problem* p, const int32_t* k_per_head, int64_t* r
 
 /*
  * Bytes of workspace the given call needs (0 if the arguments are invalid).
- * k_per_head may be NULL for DSA_WS_FWD and DSA_WS_BWD, whose sizes do not
- * depend on it (the dense calls below take no kept counts).
+ * k_per_head may be NULL for DSA_WS_FWD, DSA_WS_BWD and DSA_WS_PRED_GRAD,
+ * whose sizes do not depend on it (the dense calls and the predictor training
+ * call take no kept counts).
  */
 size_t dsa_workspace_bytes(const dsa_problem* p, const int32_t* k_per_head, int which_call);
 
@@ -238,6 +239,27 @@ int dsa_dense_attn_fwd(const dsa_problem* p, const void* Q, const void* K, const
 int dsa_dense_attn_bwd(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
                        const void* dO, const float* LSE, float* dQ, float* dK, float* dV, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_predictor_loss_grad -- stage-1 training of the low-rank predictor (hi
+ * and nl §2.A, stage 1: the per-head predictors are trained beside the full
+ * attention of normal training, by a loss that keeps the relative magnitude of
+ * the estimated scores).  Per (b, h), with qbar/kbar the group/block means of
+ * Q/K (qhat = qbar Wq[h], khat = kbar Wk[h] as in dsa_predict_block_scores):
+ *   diff[g,j] = tau (qhat_g.khat_j - qbar_g.kbar_j)  (the block score minus
+ *               the mean of tau Q K^T over the G x 64 tile),
+ *   E[g,j]    = diff[g,j] - mean_j diff[g,j]          (each row centred),
+ *   loss[h]   = mean over b, g, j of E^2,
+ *   dWq[h]    = 2 tau / (B NG NB) sum_b qbar^T E khat,
+ *   dWk[h]    = 2 tau / (B NG NB) sum_b kbar^T E^T qhat   (the gradients of loss[h]).
+ * Q, K: [B,H,N,d] bf16 or fp32; Wq, Wk: [H,d,r] fp32; loss [H], dWq, dWk
+ * [H,d,r] fp32 (overwritten).  Workspace: dsa_workspace_bytes(p, NULL,
+ * DSA_WS_PRED_GRAD) (means, projections, E and partial sums, all fp32).
+ * Deterministic.  B*H*NG*NB >= 2^31: DSA_ERR_UNSUPPORTED.
+ */
+int dsa_predictor_loss_grad(const dsa_problem* p, const void* Q, const void* K, const float* Wq, const float* Wk,
+                            float* loss, float* dWq, float* dWk, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 typedef enum { DSA_PATH_DENSE = 0, DSA_PATH_SPARSE = 1 } dsa_path;
 

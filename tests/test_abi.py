@@ -228,3 +228,28 @@ def test_choose_path_memory_cap():
     big = _p(heads=128, seq_len=64 * 8192, group=64)
     assert dsa.choose_path(big, [4096] * 128, 0.1) == dsa.PATH_DENSE
     assert dsa.choose_path(big, [8] * 128, 0.1) == dsa.PATH_SPARSE
+
+
+def test_predictor_loss_grad_validation():
+    lib = dsa.library()
+    big = 1 << 40
+    p = _p()
+    pc = ctypes.byref(p.c())
+    args = [FAKE] * 7     # Q, K, Wq, Wk, loss, dWq, dWk
+    for i in range(7):
+        bad = list(args)
+        bad[i] = None
+        assert lib.dsa_predictor_loss_grad(pc, *bad, FAKE, big, None) == -1, i
+        bad[i] = ctypes.c_void_p(0x100004)
+        assert lib.dsa_predictor_loss_grad(pc, *bad, FAKE, big, None) == -4, i
+    need = dsa.workspace_bytes(p, None, dsa.DSA_WS_PRED_GRAD)
+    # qbar, kbar, qhat, khat, E, Y, Z, row losses (16 groups x 16 blocks x 2 heads), each 256-byte aligned
+    sections = [16 * 64, 16 * 64, 16 * 16, 16 * 16, 16 * 16, 16 * 16, 16 * 16, 16]
+    partials = 4 * 2 * 2 * 16 * 64 * 16            # [H, W_q or W_k, 16 row ranges, d, r] fp32
+    assert need == sum((4 * 2 * n + 255) // 256 * 256 for n in sections) + partials
+    assert need == dsa.workspace_bytes(p, [1, 1], dsa.DSA_WS_PRED_GRAD)
+    assert lib.dsa_predictor_loss_grad(pc, *args, FAKE, need - 1, None) == -6
+    assert lib.dsa_predictor_loss_grad(pc, *args, None, big, None) == -6
+    assert lib.dsa_predictor_loss_grad(pc, *args, ctypes.c_void_p(0x100008), big, None) == -4
+    assert lib.dsa_predictor_loss_grad(ctypes.byref(_p(rank=12).c()), *args, FAKE, big, None) == -5
+    assert lib.dsa_predictor_loss_grad(None, *args, FAKE, big, None) == -1

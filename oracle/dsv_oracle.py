@@ -19,6 +19,9 @@ groups of consecutive tokens):
    the group-to-block attention logits              [hi §2.A, §2.B query grouping]
 4. per group, the k_h blocks of largest score, ties to the lowest block id,
    listed ascending -- the "critical" KV blocks     [hi §2.A, §2.B fused MM + top-k]
+   or, by coverage, the shortest run of blocks in score order whose estimated
+   attention mass (softmax of the block scores) reaches a fraction, capped
+   per head (rows then differ in length)            [hi §2.A critical KV ~90%]
 5. exact softmax attention of every query of the group over the keys of its
    kept blocks only (no mask beyond the selection; bidirectional)
                                                     [hi §2.A stage 2, nl §2.A fase 2]
@@ -28,13 +31,13 @@ groups of consecutive tokens):
    and, for the OP dispatcher's other branch, full (dense) attention over all
    keys, with the dispatcher's rule: sparse iff the skipped fraction of
    (head, group, block) tiles exceeds a threshold   [hi §2.A, nl §2.A stage 2]
-7. stage-1 predictor training: a loss on the row-centred difference between
-   the block scores and the true pooled logits, and its gradient with respect
-   to W_q and W_k                                    [hi §2.A, nl §2.A stage 1]
 6. the gradient of L = sum(dO * O) with the selection held fixed: dQ, dK, dV
    (keys in no kept block get exactly zero).  The pages call the method a
    training system but never write the backward out; this is the standard
    softmax-attention gradient restricted to the kept keys.
+7. stage-1 predictor training: a loss on the row-centred difference between
+   the block scores and the true pooled logits, and its gradient with respect
+   to W_q and W_k                                    [hi §2.A, nl §2.A stage 1]
 
 Every function here is pinned by tests/test_oracle.py against brute force on
 tiny inputs, a library routine (torch's scaled_dot_product_attention and
@@ -116,10 +119,11 @@ def select(scores: np.ndarray, k_per_head: Sequence[int]) -> List[List[np.ndarra
              for h in range(H)] for b in range(B)]
 
 
-def reverse_index(idx_bh: np.ndarray, n_blocks: int) -> List[np.ndarray]:
-    """For each KV block j, the ascending list of query groups whose selection holds j."""
+def reverse_index(idx_bh, n_blocks: int) -> List[np.ndarray]:
+    """For each KV block j, the ascending list of query groups whose selection holds j (rows may differ in
+    length)."""
     lists: List[List[int]] = [[] for _ in range(n_blocks)]
-    for g in range(idx_bh.shape[0]):
+    for g in range(len(idx_bh)):
         for j in idx_bh[g]:
             lists[int(j)].append(g)
     return [np.asarray(l, dtype=np.int64) for l in lists]
@@ -128,6 +132,34 @@ def reverse_index(idx_bh: np.ndarray, n_blocks: int) -> List[np.ndarray]:
 def reverse_list(idx_bh: np.ndarray, j: int) -> np.ndarray:
     """Ascending query groups whose selection holds block j (one entry of reverse_index)."""
     return np.nonzero((np.asarray(idx_bh) == j).any(axis=1))[0].astype(np.int64)
+
+
+def block_mass(scores_row: np.ndarray) -> np.ndarray:
+    """Estimated share of a query's attention that falls in each KV block: every block holds 64 keys and
+    its score estimates their mean logit, so the shares are the softmax of the row's block scores."""
+    s = np.asarray(scores_row, dtype=np.float64)
+    e = np.exp(s - s.max())
+    return e / e.sum()
+
+
+def select_coverage_row(scores_row: np.ndarray, coverage: float, k_cap: int) -> np.ndarray:
+    """The critical blocks by attention coverage (hi §2.A: the critical KV pairs are those that carry about
+    90% of the attention score): in the order of decreasing score (ties to the lowest id), the shortest
+    prefix whose estimated mass reaches ``coverage`` (0 < coverage <= 1), at most ``k_cap`` blocks;
+    returned ascending."""
+    nb = len(scores_row)
+    s = np.asarray(scores_row)
+    order = np.lexsort((np.arange(nb), -s))
+    cum = np.cumsum(block_mass(s)[order])
+    c = 1 + int(np.count_nonzero(cum < coverage))
+    return np.sort(order[:min(c, k_cap, nb)]).astype(np.int64)
+
+
+def select_coverage(scores: np.ndarray, coverage: float, k_cap_per_head: Sequence[int]):
+    """Per (b, h): a list of NG ascending arrays (lengths vary by row)."""
+    B, H, NG, _ = scores.shape
+    return [[[select_coverage_row(scores[b, h, g], coverage, int(k_cap_per_head[h])) for g in range(NG)]
+             for h in range(H)] for b in range(B)]
 
 
 def kept_keys(idx_row: np.ndarray, block: int = BLOCK) -> np.ndarray:

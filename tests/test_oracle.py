@@ -426,6 +426,78 @@ def check_pred_loss_closed_forms(seed=42, n=384, d=8, group=128):
     np.testing.assert_allclose(gbk[0], 0.5 * (g1k + gk_r), rtol=1e-12, atol=1e-15)
 
 
+def _brute_coverage(row, coverage, cap):
+    # Python sort of (-s, j) tuples, masses from math.exp normalised with math.fsum, accumulate to the target
+    mx = max(float(x) for x in row)
+    w = [math.exp(float(x) - mx) for x in row]
+    z = math.fsum(w)
+    pairs = sorted((-float(x), j) for j, x in enumerate(row))
+    taken, acc = [], []
+    for _, j in pairs:
+        taken.append(j)
+        acc.append(w[j] / z)
+        if math.fsum(acc) >= coverage or len(taken) == cap:
+            break
+    return sorted(taken)
+
+
+def check_coverage_brute(seed=51):
+    rng = _rng(seed)
+    for trial in range(60):
+        nb = int(rng.integers(1, 40))
+        row = rng.standard_normal(nb) * float(rng.choice([0.3, 1.0, 4.0]))
+        if trial % 3 == 0:                                   # heavy ties
+            row = np.round(row * 2) / 2
+        for cov in (0.05, 0.5, 0.9, 0.99):
+            for cap in (1, max(1, nb // 2), nb):
+                got = list(O.select_coverage_row(row, cov, cap))
+                want = _brute_coverage(row, cov, cap)
+                if got != want:
+                    # only a cumulative mass within rounding of the target may flip the count by one
+                    m = np.sort(O.block_mass(row))[::-1]
+                    c = min(len(got), len(want))
+                    assert abs(len(got) - len(want)) == 1 and abs(m[:c].sum() - cov) < 1e-12, (row, cov, cap)
+                else:
+                    # a coverage selection is the top-c selection for its own c
+                    assert got == list(O.select_row(row, len(got)))
+
+
+def check_coverage_closed_forms():
+    flat = np.zeros(16)
+    for cov, c in ((0.5, 8), (0.25, 4), (1.0 / 16, 1), (0.9, 15), (1.0, 16)):
+        assert list(O.select_coverage_row(flat, cov, 16)) == list(range(c)), cov   # uniform: ceil(cov NB), lowest ids
+    peak = np.zeros(10)
+    peak[7] = 50.0
+    assert list(O.select_coverage_row(peak, 0.999, 10)) == [7]
+    row = _rng(52).standard_normal(12)
+    assert len(O.select_coverage_row(row, 1.0, 12)) == 12
+    assert list(O.select_coverage_row(row, 0.999999, 3)) == list(O.select_row(row, 3))   # the cap
+    np.testing.assert_allclose(O.block_mass(row).sum(), 1.0, rtol=1e-15)
+    np.testing.assert_allclose(O.block_mass(row + 100.0), O.block_mass(row), rtol=1e-13)  # shift-invariant
+
+
+def check_ragged_attention_brute(seed=53, n=384, group=64):
+    # rows of different lengths: forward and backward against masked brute force and autograd
+    q, k, v, do, _, _ = _tiny(seed, n=n, d=8)
+    rng = _rng(seed)
+    nb = n // 64
+    idx = [np.sort(rng.choice(nb, size=int(rng.integers(1, nb + 1)), replace=False)) for _ in range(n // group)]
+    mask = brute.mask_from_idx(idx, n, group)
+    o_ref, lse_ref, _ = brute.masked_attention(q, k, v, mask)
+    o, lse = O.forward_head(q, k, v, idx, group)
+    np.testing.assert_allclose(o, o_ref, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=1e-12, atol=1e-12)
+    tq, tk, tv = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None],
+                                                           attn_mask=torch.tensor(mask)[None])[0]
+    (ref * torch.tensor(do)).sum().backward()
+    for mine, theirs in zip(O.backward_head(q, k, v, do, idx, group), (tq, tk, tv)):
+        np.testing.assert_allclose(mine, theirs.grad.numpy(), rtol=1e-10, atol=1e-11)
+    rev = O.reverse_index(idx, nb)
+    for j in range(nb):
+        assert list(rev[j]) == [g for g in range(len(idx)) if j in set(idx[g].tolist())]
+
+
 ALL_CHECKS = [
     check_scores_brute, check_identity_predictor, check_select_brute, check_select_special,
     check_duplicate_blocks_tie, check_linearity, check_forward_brute, check_dense_equals_sdpa,
@@ -433,7 +505,8 @@ ALL_CHECKS = [
     check_sampled_match_full, check_reverse_index, check_batched_api, check_split_bounds,
     check_split_merge_equals_unsplit, check_partial_states_brute, check_merge_algebra, check_dense_sdpa,
     check_dense_brute, check_dense_closed_forms, check_dense_sampled, check_dispatch_rule,
-    check_pred_loss_brute, check_pred_loss_closed_forms,
+    check_pred_loss_brute, check_pred_loss_closed_forms, check_coverage_brute, check_coverage_closed_forms,
+    check_ragged_attention_brute,
 ]
 
 
@@ -644,3 +717,32 @@ def test_mutation_pred_grad_half(monkeypatch):
         ds = e / e.size                       # the factor 2 of d(e^2) dropped
         return loss, tau * (qbar.T @ (ds @ khat)), tau * (kbar.T @ (ds.T @ qhat))
     assert _fails_some_pin(monkeypatch, "predictor_loss_grad_head", bad, [check_pred_loss_brute])
+
+
+def test_mutation_coverage_inclusive(monkeypatch):
+    def bad(scores_row, coverage, k_cap):       # stops one block late when a prefix lands exactly on the target
+        nb = len(scores_row)
+        s_ = np.asarray(scores_row)
+        order = np.lexsort((np.arange(nb), -s_))
+        cum = np.cumsum(O.block_mass(s_)[order])
+        c = 1 + int(np.count_nonzero(cum <= coverage))
+        return np.sort(order[:min(c, k_cap, nb)])
+    assert _fails_some_pin(monkeypatch, "select_coverage_row", bad, [check_coverage_closed_forms])
+
+
+def test_mutation_coverage_unnormalised(monkeypatch):
+    def bad(scores_row):
+        s_ = np.asarray(scores_row, dtype=np.float64)
+        return np.exp(s_ - s_.max())
+    assert _fails_some_pin(monkeypatch, "block_mass", bad, [check_coverage_brute, check_coverage_closed_forms])
+
+
+def test_mutation_coverage_ties_high(monkeypatch):
+    def bad(scores_row, coverage, k_cap):
+        nb = len(scores_row)
+        s_ = np.asarray(scores_row)
+        order = np.lexsort((-np.arange(nb), -s_))
+        cum = np.cumsum(O.block_mass(s_)[order])
+        c = 1 + int(np.count_nonzero(cum < coverage))
+        return np.sort(order[:min(c, k_cap, nb)])
+    assert _fails_some_pin(monkeypatch, "select_coverage_row", bad, [check_coverage_brute, check_coverage_closed_forms])

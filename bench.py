@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--dispatch-sweep", action="store_true",
                     help="also time dense attention against the sparse step over a sweep of keep fractions "
                          "(the dispatcher's break-even sparsity)")
+    ap.add_argument("--coverage", type=float, default=0.0,
+                    help="also time the step with selection by attention coverage (this fraction; the workload's "
+                         "k as each row's cap) and per-row counts")
     ap.add_argument("--predictor-grad", action="store_true",
                     help="also time the stage-1 predictor loss + gradient call on the same inputs")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -187,6 +190,50 @@ def time_predictor_grad(args, p, Q, K, Wt, stream, w):
             "hbm_gbs_algorithmic": round(qk_bytes / (t / 1e3) / 1e9, 1),
             "hbm_frac_algorithmic": round(qk_bytes / (t / 1e3) / PEAK_HBM, 4),
             "hbm_gbs_with_diff_matrix": round((qk_bytes + e_bytes) / (t / 1e3) / 1e9, 1)}
+
+
+def time_coverage(args, p, kph, Q, K, V, Wt, dO, stream, w):
+    """The step with coverage selection: predict, select by coverage, forward and backward over rows of
+    different lengths, each stage timed with HIP events on the bench stream."""
+    import torch
+    import dynamic_sparse_attention_qk_amd as dsa
+    plan = dsa.SparseAttentionPlan(p, kph, materialise_scores=not w.streamed, backward=dO is not None,
+                                   coverage=args.coverage)
+    plan.idx.zero_()
+    plan.rev_idx.zero_()
+    plan.predict(Q, K, Wt, Wt, stream)
+    plan.select(stream)
+    torch.cuda.synchronize()
+    cnt = plan.cnt.cpu().numpy()
+    assert cnt.min() >= 1 and cnt.max() <= max(kph), "count out of range"
+    names = ["predict", "select", "fwd"] + (["bwd"] if dO is not None else [])
+    stages = {n: [] for n in names}
+    for i in range(args.warmup + args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        ev[0].record(stream)
+        plan.predict(Q, K, Wt, Wt, stream)
+        ev[1].record(stream)
+        plan.select(stream)
+        ev[2].record(stream)
+        plan.forward(Q, K, V, stream)
+        ev[3].record(stream)
+        if dO is not None:
+            plan.backward(Q, K, V, dO, stream)
+            ev[4].record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            for j, n in enumerate(names):
+                stages[n].append(ev[j].elapsed_time(ev[j + 1]))
+    ms = {n: float(np.mean(v)) for n, v in stages.items()}
+    pairs = int(cnt.sum())
+    unit = 64 * w.group * w.head_dim
+    flops = 4.0 * unit * pairs * (3.5 if dO is not None else 1.0)
+    step = sum(ms.values())
+    return {"coverage": args.coverage, "cap": max(kph), "mean_count": round(float(cnt.mean()), 3),
+            "max_count": int(cnt.max()), "capped_rows": int((cnt == max(kph)).sum()), "kept_pairs": pairs,
+            "stage_ms": {n: round(v, 4) for n, v in ms.items()}, "ms_per_step": round(step, 4),
+            "tflops": round(flops / (step / 1e3) / 1e12, 2),
+            "tokens_per_s": round(w.batch * w.seq_len / (step / 1e3), 1)}
 
 
 SWEEP_KEEP = (0.02, 0.05, 0.1, 0.2, 0.3, 0.5, 0.7, 0.8, 0.9, 0.95, 1.0)
@@ -404,6 +451,8 @@ def main():
     }
     if args.split_kv:
         rec["split_kv"] = time_split_kv(args, p, plan, Q, K, V, stream, stage_ms["fwd"], f_fwd, w)
+    if args.coverage:
+        rec["coverage_select"] = time_coverage(args, p, kph, Q, K, V, Wt, dO, stream, w)
     if args.predictor_grad:
         rec["predictor_grad"] = time_predictor_grad(args, p, Q, K, Wt, stream, w)
     if args.dispatch_sweep:

@@ -78,11 +78,17 @@ def library() -> ctypes.CDLL:
         lib.dsa_dense_attn_bwd.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, f32p, f32p, f32p, vp, sz, vp]
         lib.dsa_choose_path.argtypes = [pp, kph, ctypes.c_double, sz]
         lib.dsa_predictor_loss_grad.argtypes = [pp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp, sz, vp]
+        lib.dsa_select_coverage_blocks.argtypes = [pp, f32p, f32p, f32p, kph, ctypes.c_double, i32p, i32p, i32p,
+                                                   i32p, f32p, vp, sz, vp]
+        lib.dsa_sparse_attn_fwd_varlen.argtypes = [pp, vp, vp, vp, i32p, i32p, kph, f32p, f32p, vp, sz, vp]
+        lib.dsa_sparse_attn_bwd_varlen.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, i32p, kph, i32p, i32p,
+                                                   f32p, f32p, f32p, vp, sz, vp]
         for name in ("dsa_index_layout", "dsa_predict_block_scores", "dsa_select_topk_blocks",
                      "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_preprocess",
                      "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_fwd_split",
                      "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd", "dsa_choose_path",
-                     "dsa_predictor_loss_grad"):
+                     "dsa_predictor_loss_grad", "dsa_select_coverage_blocks", "dsa_sparse_attn_fwd_varlen",
+                     "dsa_sparse_attn_bwd_varlen"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -92,7 +98,8 @@ EXPORTED = ("dsa_version", "dsa_status_string", "dsa_index_layout", "dsa_workspa
             "dsa_predict_block_scores", "dsa_select_topk_blocks", "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd",
             "dsa_sparse_attn_bwd_preprocess", "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq",
             "dsa_sparse_attn_fwd_split", "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd",
-            "dsa_choose_path", "dsa_predictor_loss_grad")
+            "dsa_choose_path", "dsa_predictor_loss_grad", "dsa_select_coverage_blocks", "dsa_sparse_attn_fwd_varlen",
+            "dsa_sparse_attn_bwd_varlen")
 MAX_SPLIT = 64  # DSA_MAX_SPLIT
 PATH_DENSE, PATH_SPARSE = 0, 1  # dsa_path
 DEFAULT_MIN_SPARSITY = 0.06     # DSA_DEFAULT_MIN_SPARSITY
@@ -182,6 +189,31 @@ def select_topk_blocks(p: Problem, scores, qhat, khat, k_per_head, idx, rev_ptr,
         _stream(stream)))
 
 
+def select_coverage_blocks(p: Problem, scores, qhat, khat, k_per_head, coverage: float, idx, cnt, rev_ptr, rev_idx,
+                           workspace, scores_dump=None, stream=None) -> None:
+    """Per row, the shortest run of blocks in score order whose estimated attention mass reaches coverage
+    (at most k_h); counts to cnt [B, H, NG]."""
+    _check("dsa_select_coverage_blocks", library().dsa_select_coverage_blocks(
+        ctypes.byref(p.c()), _ptr(scores), _ptr(qhat), _ptr(khat), _kph(k_per_head), float(coverage), _ptr(idx),
+        _ptr(cnt), _ptr(rev_ptr), _ptr(rev_idx), _ptr(scores_dump), _ptr(workspace), _nbytes(workspace),
+        _stream(stream)))
+
+
+def sparse_attn_fwd_varlen(p: Problem, Q, K, V, idx, cnt, k_per_head, O, LSE, workspace=None, stream=None) -> None:
+    nbytes = 0 if workspace is None else _nbytes(workspace)
+    _check("dsa_sparse_attn_fwd_varlen", library().dsa_sparse_attn_fwd_varlen(
+        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(cnt), _kph(k_per_head), _ptr(O), _ptr(LSE),
+        _ptr(workspace), nbytes, _stream(stream)))
+
+
+def sparse_attn_bwd_varlen(p: Problem, Q, K, V, O, dO, LSE, idx, cnt, k_per_head, rev_ptr, rev_idx, dQ, dK, dV,
+                           workspace, stream=None) -> None:
+    _check("dsa_sparse_attn_bwd_varlen", library().dsa_sparse_attn_bwd_varlen(
+        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(idx), _ptr(cnt),
+        _kph(k_per_head), _ptr(rev_ptr), _ptr(rev_idx), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace),
+        _nbytes(workspace), _stream(stream)))
+
+
 def sparse_attn_fwd(p: Problem, Q, K, V, idx, k_per_head, O, LSE, workspace=None, stream=None) -> None:
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("dsa_sparse_attn_fwd", library().dsa_sparse_attn_fwd(
@@ -268,9 +300,14 @@ class SparseAttentionPlan:
     """Outputs and workspaces of one problem, allocated once with torch, plus the calls in order."""
 
     def __init__(self, p: Problem, k_per_head: Sequence[int], device="cuda", materialise_scores: bool = True,
-                 backward: bool = True):
+                 backward: bool = True, coverage: Optional[float] = None):
+        """coverage: select by attention coverage (k_per_head is then each row's capacity) and run the
+        per-row-count forward and backward."""
         self.p = p
         self.k_per_head = [int(x) for x in k_per_head]
+        self.coverage = coverage
+        self.cnt = (torch.empty(p.batch, p.heads, p.n_groups, dtype=torch.int32, device=device)
+                    if coverage is not None else None)
         self.row_base = index_layout(p, self.k_per_head)
         total = int(self.row_base[-1])
         B, H, N, D, R = p.batch, p.heads, p.seq_len, p.head_dim, p.rank
@@ -299,18 +336,33 @@ class SparseAttentionPlan:
         predict_block_scores(self.p, Q, K, Wq, Wk, self.qhat, self.khat, self.scores, stream)
 
     def select(self, stream=None, scores_dump=None):
-        select_topk_blocks(self.p, self.scores, self.qhat, self.khat, self.k_per_head, self.idx, self.rev_ptr,
-                           self.rev_idx, self.ws_select, scores_dump=scores_dump, stream=stream)
+        if self.coverage is not None:
+            select_coverage_blocks(self.p, self.scores, self.qhat, self.khat, self.k_per_head, self.coverage,
+                                   self.idx, self.cnt, self.rev_ptr, self.rev_idx, self.ws_select,
+                                   scores_dump=scores_dump, stream=stream)
+        else:
+            select_topk_blocks(self.p, self.scores, self.qhat, self.khat, self.k_per_head, self.idx, self.rev_ptr,
+                               self.rev_idx, self.ws_select, scores_dump=scores_dump, stream=stream)
 
     def forward(self, Q, K, V, stream=None):
-        sparse_attn_fwd(self.p, Q, K, V, self.idx, self.k_per_head, self.O, self.LSE, self.ws_fwd, stream)
+        if self.cnt is not None:
+            sparse_attn_fwd_varlen(self.p, Q, K, V, self.idx, self.cnt, self.k_per_head, self.O, self.LSE,
+                                   self.ws_fwd, stream)
+        else:
+            sparse_attn_fwd(self.p, Q, K, V, self.idx, self.k_per_head, self.O, self.LSE, self.ws_fwd, stream)
 
     def backward(self, Q, K, V, dO, stream=None):
-        sparse_attn_bwd(self.p, Q, K, V, self.O, dO, self.LSE, self.idx, self.k_per_head, self.rev_ptr,
-                        self.rev_idx, self.dQ, self.dK, self.dV, self.ws_bwd, stream)
+        if self.cnt is not None:
+            sparse_attn_bwd_varlen(self.p, Q, K, V, self.O, dO, self.LSE, self.idx, self.cnt, self.k_per_head,
+                                   self.rev_ptr, self.rev_idx, self.dQ, self.dK, self.dV, self.ws_bwd, stream)
+        else:
+            sparse_attn_bwd(self.p, Q, K, V, self.O, dO, self.LSE, self.idx, self.k_per_head, self.rev_ptr,
+                            self.rev_idx, self.dQ, self.dK, self.dV, self.ws_bwd, stream)
 
     def backward_stages(self, Q, K, V, dO, stream=None):
-        """The backward as its three stages (same result as backward())."""
+        """The backward as its three stages (same result as backward()); top-k selection only."""
+        if self.cnt is not None:
+            raise ValueError("the staged backward takes no per-row counts: use backward()")
         sparse_attn_bwd_preprocess(self.p, Q, K, V, self.O, dO, self.LSE, self.ws_bwd, stream)
         sparse_attn_bwd_dkdv(self.p, self.k_per_head, self.rev_ptr, self.rev_idx, self.dK, self.dV, self.ws_bwd,
                              stream)

@@ -201,9 +201,9 @@ int dsa_predict_block_scores(const dsa_problem* p, const void* Q, const void* K,
   return hip_status(e);
 }
 
-int dsa_select_topk_blocks(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,
-                           const int32_t* k_per_head, int32_t* idx, int32_t* rev_ptr, int32_t* rev_idx,
-                           float* scores_dump, void* workspace, size_t workspace_bytes, void* stream) {
+static int select_impl(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,
+                       const int32_t* k_per_head, int32_t* idx, int32_t* cnt, float coverage, int32_t* rev_ptr,
+                       int32_t* rev_idx, float* scores_dump, void* workspace, size_t workspace_bytes, void* stream) {
   Shape s;
   HeadTable ht;
   int kmax = 0;
@@ -223,14 +223,33 @@ int dsa_select_topk_blocks(const dsa_problem* p, const float* scores, const floa
   int32_t* counters = static_cast<int32_t*>(workspace);
   int32_t* scratch = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                                 align256((size_t)s.B * s.H * s.NB * sizeof(int32_t)));
-  hipError_t e = dsa::launch_topk_select(s, scores, qhat, khat, idx, scores ? nullptr : scores_dump, ht, tau, kmax, hs);
+  hipError_t e = dsa::launch_topk_select(s, scores, qhat, khat, idx, scores ? nullptr : scores_dump, ht, tau, kmax, hs,
+                                         cnt, coverage);
   if (e == hipSuccess) e = dsa::launch_reverse_index(s, idx, rev_ptr, rev_idx, counters, scratch, ht, kmax, hs);
   return hip_status(e);
 }
 
-int dsa_sparse_attn_fwd(const dsa_problem* p, const void* Q, const void* K, const void* V, const int32_t* idx,
-                        const int32_t* k_per_head, float* O, float* LSE, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+int dsa_select_topk_blocks(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,
+                           const int32_t* k_per_head, int32_t* idx, int32_t* rev_ptr, int32_t* rev_idx,
+                           float* scores_dump, void* workspace, size_t workspace_bytes, void* stream) {
+  return select_impl(p, scores, qhat, khat, k_per_head, idx, nullptr, 1.0f, rev_ptr, rev_idx, scores_dump, workspace,
+                     workspace_bytes, stream);
+}
+
+int dsa_select_coverage_blocks(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,
+                               const int32_t* k_per_head, double coverage, int32_t* idx, int32_t* cnt,
+                               int32_t* rev_ptr, int32_t* rev_idx, float* scores_dump, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!(coverage > 0.0 && coverage <= 1.0)) return DSA_ERR_INVALID_ARG;
+  if (!cnt) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(cnt)) return DSA_ERR_ALIGN;
+  return select_impl(p, scores, qhat, khat, k_per_head, idx, cnt, (float)coverage, rev_ptr, rev_idx, scores_dump,
+                     workspace, workspace_bytes, stream);
+}
+
+static int fwd_impl(const dsa_problem* p, const void* Q, const void* K, const void* V, const int32_t* idx,
+                    const int32_t* cnt, const int32_t* k_per_head, float* O, float* LSE, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   Shape s;
   HeadTable ht;
   int st = check_problem(p, &s);
@@ -243,7 +262,21 @@ int dsa_sparse_attn_fwd(const dsa_problem* p, const void* Q, const void* K, cons
   if (need && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
   if (need && !aligned16(workspace)) return DSA_ERR_ALIGN;
   return hip_status(dsa::launch_attn_fwd(s, Q, K, V, idx, O, LSE, static_cast<uint16_t*>(workspace), ht, 1,
-                                         static_cast<hipStream_t>(stream)));
+                                         static_cast<hipStream_t>(stream), cnt));
+}
+
+int dsa_sparse_attn_fwd(const dsa_problem* p, const void* Q, const void* K, const void* V, const int32_t* idx,
+                        const int32_t* k_per_head, float* O, float* LSE, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return fwd_impl(p, Q, K, V, idx, nullptr, k_per_head, O, LSE, workspace, workspace_bytes, stream);
+}
+
+int dsa_sparse_attn_fwd_varlen(const dsa_problem* p, const void* Q, const void* K, const void* V, const int32_t* idx,
+                               const int32_t* cnt, const int32_t* k_per_head, float* O, float* LSE, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!cnt) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(cnt)) return DSA_ERR_ALIGN;
+  return fwd_impl(p, Q, K, V, idx, cnt, k_per_head, O, LSE, workspace, workspace_bytes, stream);
 }
 
 int dsa_sparse_attn_fwd_split(const dsa_problem* p, const void* Q, const void* K, const void* V, const int32_t* idx,
@@ -330,10 +363,10 @@ int dsa_sparse_attn_bwd_dq(const dsa_problem* p, const int32_t* idx, const int32
   return hip_status(dsa::launch_bwd_dq(s, bwd_work(s, workspace), idx, dQ, ht, static_cast<hipStream_t>(stream)));
 }
 
-int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
-                        const void* dO, const float* LSE, const int32_t* idx, const int32_t* k_per_head,
-                        const int32_t* rev_ptr, const int32_t* rev_idx, float* dQ, float* dK, float* dV,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+static int bwd_impl(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O, const void* dO,
+                    const float* LSE, const int32_t* idx, const int32_t* cnt, const int32_t* k_per_head,
+                    const int32_t* rev_ptr, const int32_t* rev_idx, float* dQ, float* dK, float* dV, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   Shape s;
   HeadTable ht;
   int st = check_bwd_common(p, k_per_head, &s, &ht);
@@ -349,8 +382,26 @@ int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, cons
   const dsa::BwdWork w = bwd_work(s, workspace);
   hipError_t e = dsa::launch_bwd_pre(s, Q, K, V, O, dO, LSE, w, hs);
   if (e == hipSuccess) e = dsa::launch_bwd_dkdv(s, w, rev_ptr, rev_idx, dK, dV, ht, hs);
-  if (e == hipSuccess) e = dsa::launch_bwd_dq(s, w, idx, dQ, ht, hs);
+  if (e == hipSuccess) e = dsa::launch_bwd_dq(s, w, idx, dQ, ht, hs, cnt);
   return hip_status(e);
+}
+
+int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
+                        const void* dO, const float* LSE, const int32_t* idx, const int32_t* k_per_head,
+                        const int32_t* rev_ptr, const int32_t* rev_idx, float* dQ, float* dK, float* dV,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(p, Q, K, V, O, dO, LSE, idx, nullptr, k_per_head, rev_ptr, rev_idx, dQ, dK, dV, workspace,
+                  workspace_bytes, stream);
+}
+
+int dsa_sparse_attn_bwd_varlen(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
+                               const void* dO, const float* LSE, const int32_t* idx, const int32_t* cnt,
+                               const int32_t* k_per_head, const int32_t* rev_ptr, const int32_t* rev_idx, float* dQ,
+                               float* dK, float* dV, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cnt) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(cnt)) return DSA_ERR_ALIGN;
+  return bwd_impl(p, Q, K, V, O, dO, LSE, idx, cnt, k_per_head, rev_ptr, rev_idx, dQ, dK, dV, workspace,
+                  workspace_bytes, stream);
 }
 
 int dsa_dense_attn_fwd(const dsa_problem* p, const void* Q, const void* K, const void* V, float* O, float* LSE,

@@ -73,7 +73,8 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ V16,
                                                           const uint16_t* __restrict__ dO16,
                                                           const float* __restrict__ NL2, const float* __restrict__ Dvec,
-                                                          const int32_t* __restrict__ idx, float* __restrict__ dQ,
+                                                          const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ cnt, float* __restrict__ dQ,
                                                           HeadTable ht, XcdSplit sp, int N, int H, int B, float scale_log2,
                                                           float tau) {
   constexpr int NRT = G / 32;
@@ -90,9 +91,10 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
   if (task < 0) return;
   const uint32_t L = (uint32_t)task;
   const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
-  const int k = ht.k[h];
+  // blocks of this row: cnt (if given, clamped to [1, k_h]) or k_h; rows are k_h entries apart
+  const int k = (kLists && cnt) ? min(max(cnt[((size_t)b * H + h) * NG + g], 1), ht.k[h]) : ht.k[h];
   const int NB = N / kBlock;
-  const int32_t* irow = kLists ? idx + row_base(ht, b, h, NG) + (int64_t)g * k : nullptr;
+  const int32_t* irow = kLists ? idx + row_base(ht, b, h, NG) + (int64_t)g * ht.k[h] : nullptr;
   const size_t bh = (size_t)b * H + h;
   const uint16_t* Kbh = K16 + bh * (size_t)N * D;
   const uint16_t* Vbh = V16 + bh * (size_t)N * D;
@@ -500,14 +502,14 @@ hipError_t dkdv_launch(const Shape& s, const BwdWork& w, const int32_t* rev_ptr,
 }
 
 template <int D, int G>
-hipError_t dq_launch(const Shape& s, const BwdWork& w, const int32_t* idx, float* dQ, const HeadTable& ht,
-                     hipStream_t st) {
+hipError_t dq_launch(const Shape& s, const BwdWork& w, const int32_t* idx, const int32_t* cnt, float* dQ,
+                     const HeadTable& ht, hipStream_t st) {
   const float tau = 1.0f / sqrtf((float)D);
   unsigned nwg = 0;
   const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0, 1.0, &nwg);  // a group costs k_h blocks + 1
   auto kern = idx ? bwd_dq_kernel<D, G, true> : bwd_dq_kernel<D, G, false>;
-  hipLaunchKernelGGL(kern, dim3(nwg), dim3(G * 4), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, idx, dQ, ht, sp,
-                     s.N, s.H, s.B, tau * kLog2e, tau);
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(G * 4), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, idx, cnt, dQ, ht,
+                     sp, s.N, s.H, s.B, tau * kLog2e, tau);
   return hipGetLastError();
 }
 
@@ -532,10 +534,10 @@ hipError_t launch_bwd_dkdv(const Shape& s, const BwdWork& w, const int32_t* rev_
 }
 
 hipError_t launch_bwd_dq(const Shape& s, const BwdWork& w, const int32_t* idx, float* dQ, const HeadTable& ht,
-                         hipStream_t st) {
+                         hipStream_t st, const int32_t* cnt) {
   if (s.D == 64)
-    return s.G == 64 ? dq_launch<64, 64>(s, w, idx, dQ, ht, st) : dq_launch<64, 128>(s, w, idx, dQ, ht, st);
-  return s.G == 64 ? dq_launch<128, 64>(s, w, idx, dQ, ht, st) : dq_launch<128, 128>(s, w, idx, dQ, ht, st);
+    return s.G == 64 ? dq_launch<64, 64>(s, w, idx, cnt, dQ, ht, st) : dq_launch<64, 128>(s, w, idx, cnt, dQ, ht, st);
+  return s.G == 64 ? dq_launch<128, 64>(s, w, idx, cnt, dQ, ht, st) : dq_launch<128, 128>(s, w, idx, cnt, dQ, ht, st);
 }
 
 }  // namespace dsa

@@ -31,14 +31,16 @@ struct FwdTask {
   int g, h, b, part, kbeg, klen;
 };
 
-__device__ __forceinline__ FwdTask fwd_task(uint32_t L, int NG, int H, int n_split, const HeadTable& ht) {
+// cnt (if not null): blocks kept by each (b, h, g) row, clamped to [1, k_h] (k_h: the row's list capacity)
+__device__ __forceinline__ FwdTask fwd_task(uint32_t L, int NG, int H, int n_split, const HeadTable& ht,
+                                            const int32_t* __restrict__ cnt) {
   FwdTask t;
   t.part = (int)(L % (uint32_t)n_split);
   const uint32_t r = L / (uint32_t)n_split;
   t.g = r % NG;
   t.h = (r / NG) % H;
   t.b = r / (NG * H);
-  const int k = ht.k[t.h];
+  const int k = cnt ? min(max(cnt[((size_t)t.b * H + t.h) * NG + t.g], 1), ht.k[t.h]) : ht.k[t.h];
   t.kbeg = t.part * k / n_split;
   t.klen = (t.part + 1) * k / n_split - t.kbeg;
   return t;
@@ -62,6 +64,7 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
                                                                  const bf16_t* __restrict__ K,
                                                                  const uint16_t* __restrict__ V16,
                                                                  const int32_t* __restrict__ idx,
+                                                                 const int32_t* __restrict__ cnt,
                                                                  float* __restrict__ O, float* __restrict__ LSE,
                                                                  HeadTable ht, XcdSplit sp, int N, int H, int B,
                                                                  int n_split, float scale_log2) {
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
   const int NG = N / G;
   const int64_t task = xcd_task(sp, blockIdx.x);
   if (task < 0) return;
-  const FwdTask tk = fwd_task((uint32_t)task, NG, H, n_split, ht);
+  const FwdTask tk = fwd_task((uint32_t)task, NG, H, n_split, ht, kLists ? cnt : nullptr);
   const int g = tk.g, h = tk.h, b = tk.b;
   const int k = tk.klen;  // blocks of this part
   const int NB = N / kBlock;
@@ -255,7 +258,8 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
 template <int D, int G, bool kLists>
 __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                              const float* __restrict__ V,
-                                                             const int32_t* __restrict__ idx, float* __restrict__ O,
+                                                             const int32_t* __restrict__ idx,
+                                                             const int32_t* __restrict__ cnt, float* __restrict__ O,
                                                              float* __restrict__ LSE, HeadTable ht, XcdSplit sp, int N, int H,
                                                              int B, int n_split, float scale_log2) {
   constexpr int NT = G * 2;
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __rest
   const int NG = N / G;
   const int64_t task = xcd_task(sp, blockIdx.x);
   if (task < 0) return;
-  const FwdTask tk = fwd_task((uint32_t)task, NG, H, n_split, ht);
+  const FwdTask tk = fwd_task((uint32_t)task, NG, H, n_split, ht, kLists ? cnt : nullptr);
   const int g = tk.g, h = tk.h, b = tk.b;
   const int k = tk.klen;  // blocks of this part
   const int32_t* irow = kLists ? idx + row_base(ht, b, h, NG) + (int64_t)g * ht.k[h] + tk.kbeg : nullptr;
@@ -387,8 +391,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
 }
 
 template <int D, int G>
-hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx, float* O,
-                      float* LSE, uint16_t* V16, const HeadTable& ht, int n_split, hipStream_t st) {
+hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx,
+                      const int32_t* cnt, float* O, float* LSE, uint16_t* V16, const HeadTable& ht, int n_split,
+                      hipStream_t st) {
   const float scale_log2 = (1.0f / sqrtf((float)D)) * kLog2e;
   unsigned nwg = 0;
   // a (group, part) task costs k_h / n_split blocks + 1
@@ -399,11 +404,11 @@ hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* 
     if (e != hipSuccess) return e;
     auto kern = idx ? attn_fwd_bf16_kernel<D, G, true> : attn_fwd_bf16_kernel<D, G, false>;
     hipLaunchKernelGGL(kern, grid, dim3(G * 4), 0, st, static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K),
-                       V16, idx, O, LSE, ht, sp, s.N, s.H, s.B, n_split, scale_log2);
+                       V16, idx, cnt, O, LSE, ht, sp, s.N, s.H, s.B, n_split, scale_log2);
   } else {
     auto kern = idx ? attn_fwd_f32_kernel<D, G, true> : attn_fwd_f32_kernel<D, G, false>;
     hipLaunchKernelGGL(kern, grid, dim3(G * 2), 0, st, static_cast<const float*>(Q), static_cast<const float*>(K),
-                       static_cast<const float*>(V), idx, O, LSE, ht, sp, s.N, s.H, s.B, n_split, scale_log2);
+                       static_cast<const float*>(V), idx, cnt, O, LSE, ht, sp, s.N, s.H, s.B, n_split, scale_log2);
   }
   return hipGetLastError();
 }
@@ -411,13 +416,14 @@ hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* 
 }  // namespace
 
 hipError_t launch_attn_fwd(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx, float* O,
-                           float* LSE, uint16_t* V16, const HeadTable& ht, int n_split, hipStream_t st) {
+                           float* LSE, uint16_t* V16, const HeadTable& ht, int n_split, hipStream_t st,
+                           const int32_t* cnt) {
   if (s.D == 64)
-    return s.G == 64 ? fwd_launch<64, 64>(s, Q, K, V, idx, O, LSE, V16, ht, n_split, st)
-                     : fwd_launch<64, 128>(s, Q, K, V, idx, O, LSE, V16, ht, n_split, st);
+    return s.G == 64 ? fwd_launch<64, 64>(s, Q, K, V, idx, cnt, O, LSE, V16, ht, n_split, st)
+                     : fwd_launch<64, 128>(s, Q, K, V, idx, cnt, O, LSE, V16, ht, n_split, st);
   if (s.D == 128)
-    return s.G == 64 ? fwd_launch<128, 64>(s, Q, K, V, idx, O, LSE, V16, ht, n_split, st)
-                     : fwd_launch<128, 128>(s, Q, K, V, idx, O, LSE, V16, ht, n_split, st);
+    return s.G == 64 ? fwd_launch<128, 64>(s, Q, K, V, idx, cnt, O, LSE, V16, ht, n_split, st)
+                     : fwd_launch<128, 128>(s, Q, K, V, idx, cnt, O, LSE, V16, ht, n_split, st);
   return hipErrorInvalidValue;
 }
 

@@ -19,14 +19,17 @@ hipError_t launch_pool_project(const Shape& s, const void* X, const float* W, fl
                                hipStream_t st, float* mean_out = nullptr);
 hipError_t launch_block_scores(const Shape& s, const float* qhat, const float* khat, float* scores,
                                float tau, hipStream_t st);
+// cnt (if not null): select by attention coverage (kept counts per row to cnt [B,H,NG], unused slots -1)
 hipError_t launch_topk_select(const Shape& s, const float* scores, const float* qhat, const float* khat,
                               int32_t* idx, float* dump, const HeadTable& ht, float tau, int kmax,
-                              hipStream_t st);
+                              hipStream_t st, int32_t* cnt = nullptr, float coverage = 1.0f);
 hipError_t launch_reverse_index(const Shape& s, const int32_t* idx, int32_t* rev_ptr, int32_t* rev_idx,
                                 int32_t* counters, int32_t* scratch, const HeadTable& ht, int kmax,
                                 hipStream_t st);
+// cnt (if not null): per-row kept counts [B,H,NG] within the k_h-entry rows of idx
 hipError_t launch_attn_fwd(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx,
-                           float* O, float* LSE, uint16_t* V16, const HeadTable& ht, int n_split, hipStream_t st);
+                           float* O, float* LSE, uint16_t* V16, const HeadTable& ht, int n_split, hipStream_t st,
+                           const int32_t* cnt = nullptr);
 hipError_t launch_attn_merge(const Shape& s, int n_parts, const float* O_part, const float* LSE_part, float* O,
                              float* LSE, hipStream_t st);
 // Backward workspace: D, -LSE*log2(e) and exact fp16 copies of Q, K, V, dO.
@@ -45,7 +48,7 @@ hipError_t launch_bwd_pre(const Shape& s, const void* Q, const void* K, const vo
 hipError_t launch_bwd_dkdv(const Shape& s, const BwdWork& w, const int32_t* rev_ptr, const int32_t* rev_idx,
                            float* dK, float* dV, const HeadTable& ht, hipStream_t st);
 hipError_t launch_bwd_dq(const Shape& s, const BwdWork& w, const int32_t* idx, float* dQ, const HeadTable& ht,
-                         hipStream_t st);
+                         hipStream_t st, const int32_t* cnt = nullptr);
 
 // Stage-1 predictor training workspace (fp32): qbar [B,H,NG,d], kbar [B,H,NB,d], qhat [B,H,NG,r],
 // khat [B,H,NB,r], E [B,H,NG,NB], Y [B,H,NG,r], Z [B,H,NB,r], lrow [B,H,NG], part [H,2,16,d,r].

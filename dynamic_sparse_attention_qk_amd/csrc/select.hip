@@ -33,13 +33,32 @@ __device__ __forceinline__ uint32_t wave_count_ge(const uint32_t (&key)[KPL], ui
   return c;
 }
 
-template <int KPL, int R, bool STREAM>
+// The score whose order-preserving key is k (inverse of score_key; -0.0 comes back as +0.0).
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <int KPL>
+__device__ __forceinline__ float wave_mass_ge(const uint32_t (&key)[KPL], const float (&e)[KPL], uint32_t cand) {
+  float m = 0.f;
+#pragma unroll
+  for (int t = 0; t < KPL; ++t) m += key[t] >= cand ? e[t] : 0.f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m += __shfl_xor(m, off);
+  return m;
+}
+
+// COVER: the row keeps the shortest run of blocks, in score order, whose estimated attention mass (the
+// softmax of the row's block scores) reaches `coverage` of the total, at most k_h; the count goes to
+// cnt[b,h,g] and the row's unused slots get -1.
+template <int KPL, int R, bool STREAM, bool COVER>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* __restrict__ scores,
                                                                    const float* __restrict__ qhat,
                                                                    const float* __restrict__ khat,
                                                                    int32_t* __restrict__ idx,
+                                                                   int32_t* __restrict__ cnt,
                                                                    float* __restrict__ dump, HeadTable ht, int NG,
-                                                                   int NB, int H, float tau) {
+                                                                   int NB, int H, float tau, float coverage) {
   constexpr int CH = KPL < 4 ? KPL : (R > 32 ? 2 : 4);  // 64-block chunks of khat staged per LDS round
   __shared__ float sk[STREAM ? 64 * CH : 1][R + 1];
   const int b = blockIdx.z, h = blockIdx.y;
@@ -91,18 +110,62 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
   }
   if (!valid) return;  // wave-uniform; all barriers are behind us
 
-  const int k = ht.k[h];
-  // Bisection for T = max{x : #(key >= x) >= k}; keys of real scores are > 0.
-  uint32_t T = 0;
+  const int kcap = ht.k[h];
+  int k = kcap;
+  uint32_t T = 0, need = 0;
+  bool counted = true;  // T and need still to be found by the count bisection for k
+  if constexpr (COVER) {
+    // masses e_j = exp(s_j - s_max) (0 for the padding keys, which are 0), total Z = M(0)
+    uint32_t kmax = 0;
+#pragma unroll
+    for (int t = 0; t < KPL; ++t) kmax = max(kmax, key[t]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+    const float smax = key_score(kmax);
+    float e[KPL];
+#pragma unroll
+    for (int t = 0; t < KPL; ++t) e[t] = key[t] ? expf(key_score(key[t]) - smax) : 0.f;
+    const float target = coverage * wave_mass_ge<KPL>(key, e, 0u);
+    // T = max{x : M(x) >= target}, M(x) = mass of the keys >= x (non-increasing in x)
 #pragma unroll 1
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = T | (1u << bit);
-    if (wave_count_ge<KPL>(key, cand) >= (uint32_t)k) T = cand;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      if (wave_mass_ge<KPL>(key, e, cand) >= target) T = cand;
+    }
+    const bool top = T == 0xFFFFFFFFu;
+    const uint32_t n_gt = top ? 0u : wave_count_ge<KPL>(key, T + 1u);
+    const uint32_t n_eq = wave_count_ge<KPL>(key, T) - n_gt;
+    const float m_gt = top ? 0.f : wave_mass_ge<KPL>(key, e, T + 1u);
+    // the keys equal to T share one mass; take them, lowest id first, until the target is reached
+    const float e_t = expf(key_score(T) - smax);
+    // smallest m >= 1 (at most n_eq) with m_gt + m e_t >= target: start near the quotient, then step
+    uint32_t m = 1;
+    if (e_t > 0.f) m = (uint32_t)fminf(fmaxf((target - m_gt) / e_t - 1.f, 1.f), (float)n_eq);
+    while (m > 1 && m_gt + (float)(m - 1) * e_t >= target) --m;
+    while (m < n_eq && m_gt + (float)m * e_t < target) ++m;
+    if ((int)(n_gt + m) <= kcap) {
+      k = (int)(n_gt + m);
+      need = m;
+      counted = false;
+    }
   }
-  const uint32_t n_gt = (T == 0xFFFFFFFFu) ? 0u : wave_count_ge<KPL>(key, T + 1u);
-  const uint32_t need = (uint32_t)k - n_gt;  // equal keys to take, lowest index first
+  if (counted) {
+    // Bisection for T = max{x : #(key >= x) >= k}; keys of real scores are > 0.
+    T = 0;
+#pragma unroll 1
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      if (wave_count_ge<KPL>(key, cand) >= (uint32_t)k) T = cand;
+    }
+    const uint32_t n_gt = (T == 0xFFFFFFFFu) ? 0u : wave_count_ge<KPL>(key, T + 1u);
+    need = (uint32_t)k - n_gt;  // equal keys to take, lowest index first
+  }
 
-  int32_t* out = idx + row_base(ht, b, h, NG) + (int64_t)g * k;
+  int32_t* out = idx + row_base(ht, b, h, NG) + (int64_t)g * kcap;
+  if constexpr (COVER) {
+    for (int p = k + lane; p < kcap; p += 64) out[p] = -1;
+    if (lane == 0) cnt[bh * NG + g] = k;
+  }
   uint32_t pos = 0, eq_seen = 0;
 #pragma unroll
   for (int t = 0; t < KPL; ++t) {
@@ -117,29 +180,39 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
   }
 }
 
-template <int KPL, int R>
-hipError_t select_launch(const Shape& s, const float* scores, const float* qhat, const float* khat, int32_t* idx,
-                         float* dump, const HeadTable& ht, float tau, hipStream_t st) {
+template <int KPL, int R, bool COVER>
+void select_launch_c(const Shape& s, const float* scores, const float* qhat, const float* khat, int32_t* idx,
+                     int32_t* cnt, float* dump, const HeadTable& ht, float tau, float coverage, hipStream_t st) {
   dim3 grid((s.NG + 3) / 4, s.H, s.B);
   if (scores)
-    hipLaunchKernelGGL((topk_select_kernel<KPL, R, false>), grid, dim3(kSelThreads), 0, st, scores, qhat, khat, idx,
-                       dump, ht, s.NG, s.NB, s.H, tau);
+    hipLaunchKernelGGL((topk_select_kernel<KPL, R, false, COVER>), grid, dim3(kSelThreads), 0, st, scores, qhat, khat,
+                       idx, cnt, dump, ht, s.NG, s.NB, s.H, tau, coverage);
   else
-    hipLaunchKernelGGL((topk_select_kernel<KPL, R, true>), grid, dim3(kSelThreads), 0, st, scores, qhat, khat, idx,
-                       dump, ht, s.NG, s.NB, s.H, tau);
+    hipLaunchKernelGGL((topk_select_kernel<KPL, R, true, COVER>), grid, dim3(kSelThreads), 0, st, scores, qhat, khat,
+                       idx, cnt, dump, ht, s.NG, s.NB, s.H, tau, coverage);
+}
+
+template <int KPL, int R>
+hipError_t select_launch(const Shape& s, const float* scores, const float* qhat, const float* khat, int32_t* idx,
+                         int32_t* cnt, float* dump, const HeadTable& ht, float tau, float coverage, hipStream_t st) {
+  if (cnt)
+    select_launch_c<KPL, R, true>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+  else
+    select_launch_c<KPL, R, false>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
   return hipGetLastError();
 }
 
 template <int KPL>
 hipError_t select_dispatch_r(const Shape& s, const float* scores, const float* qhat, const float* khat,
-                             int32_t* idx, float* dump, const HeadTable& ht, float tau, hipStream_t st) {
+                             int32_t* idx, int32_t* cnt, float* dump, const HeadTable& ht, float tau, float coverage,
+                             hipStream_t st) {
   if (scores)  // the rank only matters when streaming
-    return select_launch<KPL, 8>(s, scores, qhat, khat, idx, dump, ht, tau, st);
+    return select_launch<KPL, 8>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
   switch (s.R) {
-    case 8: return select_launch<KPL, 8>(s, scores, qhat, khat, idx, dump, ht, tau, st);
-    case 16: return select_launch<KPL, 16>(s, scores, qhat, khat, idx, dump, ht, tau, st);
-    case 32: return select_launch<KPL, 32>(s, scores, qhat, khat, idx, dump, ht, tau, st);
-    case 64: return select_launch<KPL, 64>(s, scores, qhat, khat, idx, dump, ht, tau, st);
+    case 8: return select_launch<KPL, 8>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+    case 16: return select_launch<KPL, 16>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+    case 32: return select_launch<KPL, 32>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+    case 64: return select_launch<KPL, 64>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -258,17 +331,18 @@ __global__ __launch_bounds__(256) void rev_sort_kernel(const int32_t* __restrict
 }  // namespace
 
 hipError_t launch_topk_select(const Shape& s, const float* scores, const float* qhat, const float* khat, int32_t* idx,
-                              float* dump, const HeadTable& ht, float tau, int kmax, hipStream_t st) {
+                              float* dump, const HeadTable& ht, float tau, int kmax, hipStream_t st, int32_t* cnt,
+                              float coverage) {
   (void)kmax;
   const int kpl = (s.NB + 63) / 64;
-  if (kpl <= 1) return select_dispatch_r<1>(s, scores, qhat, khat, idx, dump, ht, tau, st);
-  if (kpl <= 2) return select_dispatch_r<2>(s, scores, qhat, khat, idx, dump, ht, tau, st);
-  if (kpl <= 4) return select_dispatch_r<4>(s, scores, qhat, khat, idx, dump, ht, tau, st);
-  if (kpl <= 8) return select_dispatch_r<8>(s, scores, qhat, khat, idx, dump, ht, tau, st);
-  if (kpl <= 16) return select_dispatch_r<16>(s, scores, qhat, khat, idx, dump, ht, tau, st);
-  if (kpl <= 32) return select_dispatch_r<32>(s, scores, qhat, khat, idx, dump, ht, tau, st);
-  if (kpl <= 64) return select_dispatch_r<64>(s, scores, qhat, khat, idx, dump, ht, tau, st);
-  if (kpl <= 128) return select_dispatch_r<128>(s, scores, qhat, khat, idx, dump, ht, tau, st);
+  if (kpl <= 1) return select_dispatch_r<1>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+  if (kpl <= 2) return select_dispatch_r<2>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+  if (kpl <= 4) return select_dispatch_r<4>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+  if (kpl <= 8) return select_dispatch_r<8>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+  if (kpl <= 16) return select_dispatch_r<16>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+  if (kpl <= 32) return select_dispatch_r<32>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+  if (kpl <= 64) return select_dispatch_r<64>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+  if (kpl <= 128) return select_dispatch_r<128>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
   return hipErrorInvalidValue;
 }
 

@@ -156,6 +156,48 @@ int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, cons
                         float* dQ, float* dK, float* dV, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/*
+ * Selection by attention coverage (hi §2.A: the critical KV pairs are the
+ * ones that carry about 90% of the attention score), with per-row counts.
+ *
+ * dsa_select_coverage_blocks -- as dsa_select_topk_blocks, except that row
+ * (b,h,g) keeps the shortest run of blocks, in the order of decreasing score
+ * (ties towards the lowest id), whose estimated attention mass reaches
+ * `coverage` of the row's total, and at most k_h blocks (k_per_head is the
+ * per-head capacity of the rows).  Each block holds 64 keys and its score
+ * estimates their mean logit, so the estimated masses are the softmax of the
+ * row's scores, computed in fp32 (exp(s_j - max s), summed per wave).
+ * Writes the kept count to cnt[b,h,g] (int32 [B,H,NG], 1 <= cnt <= k_h), the
+ * cnt ascending ids to the first slots of the row (same layout as idx, rows
+ * k_h entries apart) and -1 to the unused slots; rev_ptr/rev_idx index the
+ * kept entries only.  0 < coverage <= 1, else DSA_ERR_INVALID_ARG.  Where the
+ * cumulative mass comes within fp32 rounding of the target, the run may end
+ * earlier or later than an exact computation would (at coverage 1, blocks
+ * whose mass is below fp32 resolution of the total are not needed).
+ * Workspace DSA_WS_SELECT.
+ */
+int dsa_select_coverage_blocks(const dsa_problem* p, const float* scores, const float* qhat,
+                               const float* khat, const int32_t* k_per_head, double coverage, int32_t* idx,
+                               int32_t* cnt, int32_t* rev_ptr, int32_t* rev_idx, float* scores_dump,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_sparse_attn_fwd_varlen / dsa_sparse_attn_bwd_varlen -- the forward and
+ * backward above for rows of different lengths: row (b,h,g) attends to the
+ * first cnt[b,h,g] blocks of its idx row (counts outside [1, k_h] are
+ * clamped to it).  idx, cnt, rev_ptr and rev_idx as written by
+ * dsa_select_coverage_blocks.  Other arguments, workspaces and errors as
+ * dsa_sparse_attn_fwd / dsa_sparse_attn_bwd.
+ */
+int dsa_sparse_attn_fwd_varlen(const dsa_problem* p, const void* Q, const void* K, const void* V,
+                               const int32_t* idx, const int32_t* cnt, const int32_t* k_per_head, float* O,
+                               float* LSE, void* workspace, size_t workspace_bytes, void* stream);
+int dsa_sparse_attn_bwd_varlen(const dsa_problem* p, const void* Q, const void* K, const void* V,
+                               const float* O, const void* dO, const float* LSE, const int32_t* idx,
+                               const int32_t* cnt, const int32_t* k_per_head, const int32_t* rev_ptr,
+                               const int32_t* rev_idx, float* dQ, float* dK, float* dV, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* Most parts a split-KV forward or a merge takes. */
 #define DSA_MAX_SPLIT 64
 

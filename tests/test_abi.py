@@ -253,3 +253,33 @@ def test_predictor_loss_grad_validation():
     assert lib.dsa_predictor_loss_grad(pc, *args, ctypes.c_void_p(0x100008), big, None) == -4
     assert lib.dsa_predictor_loss_grad(ctypes.byref(_p(rank=12).c()), *args, FAKE, big, None) == -5
     assert lib.dsa_predictor_loss_grad(None, *args, FAKE, big, None) == -1
+
+
+def test_coverage_calls_validation():
+    lib = dsa.library()
+    big = 1 << 40
+    p = _p()
+    pc = ctypes.byref(p.c())
+    kph = dsa._kph([4, 4])
+    # select: scores, qhat, khat, kph, coverage, idx, cnt, rev_ptr, rev_idx, dump, ws, bytes, stream
+    sel = lambda cov, cnt, ws=FAKE: lib.dsa_select_coverage_blocks(pc, FAKE, FAKE, FAKE, kph, cov, FAKE, cnt, FAKE,
+                                                                   FAKE, None, ws, big, None)
+    for cov in (0.0, -0.5, 1.0000001, float("nan")):
+        assert sel(cov, FAKE) == -1, cov
+    assert sel(0.9, None) == -1
+    assert sel(0.9, ctypes.c_void_p(0x100004)) == -4
+    assert sel(0.9, FAKE, None) == -6
+    assert lib.dsa_select_coverage_blocks(pc, FAKE, FAKE, FAKE, dsa._kph([0, 4]), 0.9, FAKE, FAKE, FAKE, FAKE, None,
+                                          FAKE, big, None) == -2
+    # forward / backward with counts
+    assert lib.dsa_sparse_attn_fwd_varlen(pc, FAKE, FAKE, FAKE, FAKE, None, kph, FAKE, FAKE, FAKE, big, None) == -1
+    assert lib.dsa_sparse_attn_fwd_varlen(pc, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x100004), kph, FAKE, FAKE,
+                                          FAKE, big, None) == -4
+    assert lib.dsa_sparse_attn_fwd_varlen(pc, FAKE, FAKE, FAKE, None, FAKE, kph, FAKE, FAKE, FAKE, big, None) == -1
+    args = [FAKE] * 6 + [FAKE, None, kph] + [FAKE] * 5
+    assert lib.dsa_sparse_attn_bwd_varlen(pc, *args, FAKE, big, None) == -1
+    args[7] = ctypes.c_void_p(0x100004)
+    assert lib.dsa_sparse_attn_bwd_varlen(pc, *args, FAKE, big, None) == -4
+    args[7] = FAKE
+    f32 = ctypes.byref(_p(dtype=dsa.DSA_F32).c())
+    assert lib.dsa_sparse_attn_bwd_varlen(f32, *args, FAKE, big, None) == -3

@@ -420,6 +420,8 @@ def main():
     dom_tflops = kernel_flops[dom] / (stage_ms[dom] / 1e3) / 1e12
     peak = PEAK_BF16 if w.dtype == "bf16" else PEAK_F32_MFMA
     elt = 2 if w.dtype == "bf16" else 4
+    sel_bytes = (w.batch * w.heads * w.n_groups * w.n_blocks * 4 if not w.streamed else 0) + \
+        2 * 4 * pairs + w.batch * w.heads * (w.n_blocks + 1) * 4
     pred_bytes = 2 * w.batch * w.heads * w.seq_len * w.head_dim * elt + \
         (w.batch * w.heads * w.n_groups * w.n_blocks * 4 if not w.streamed else 0)
     traffic = stored_traffic(kernel_names[dom], w.name) if w.dtype == "bf16" else None
@@ -445,6 +447,13 @@ def main():
         "counted_tflop_per_step": round((f_fwd + f_bwd) / 1e12, 4),
         "stage_ms": {n: round(v, 4) for n, v in stage_ms.items()},
         "predict_hbm_gbs": round(pred_bytes / (stage_ms["predict"] / 1e3) / 1e9, 1),
+        # the HBM-bound stages against 8 TB/s: predict reads Q and K once and writes the scores; select reads
+        # the scores and writes the kept-block list and its reverse index (plus rev_ptr)
+        "hbm_stages": {
+            "predict": {"bytes": pred_bytes, "gbs": round(pred_bytes / (stage_ms["predict"] / 1e3) / 1e9, 1),
+                        "frac": round(pred_bytes / (stage_ms["predict"] / 1e3) / PEAK_HBM, 4)},
+            "select": {"bytes": sel_bytes, "gbs": round(sel_bytes / (stage_ms["select"] / 1e3) / 1e9, 1),
+                       "frac": round(sel_bytes / (stage_ms["select"] / 1e3) / PEAK_HBM, 4)}},
         "roofline": {"kernel": kernel_names[dom], "bound": "mfma", "achieved": round(dom_tflops, 2),
                      "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(dom_tflops * 1e12 / peak, 4),
                      "traffic": traffic},

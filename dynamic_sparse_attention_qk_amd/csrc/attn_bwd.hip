@@ -243,18 +243,19 @@ __device__ __forceinline__ void join4_f16_split(const f32x4& a, const f32x4& b, 
   }
 }
 
-// Order of the dK/dV tasks within each XCD range: the blocks whose reverse
-// list is longer than half the head's mean first, the rest after, each part in
-// task order (so neighbouring blocks still run together).  The workgroups that
-// start last then have short lists, which trims the tail of the launch.  One
-// workgroup per range; a stable partition by block-wide prefix counts.
+// Order of the dK/dV tasks within each XCD segment (a contiguous range, or an
+// XCD's part of one (b, h) run): the blocks whose reverse list is longer than
+// half the head's mean first, the rest after, each in task order (so
+// neighbouring blocks still run together).  The workgroups that start last
+// then have short lists, which trims the tail of the launch.  One workgroup
+// per segment; a stable partition by block-wide prefix counts.
 __global__ __launch_bounds__(256) void dkdv_order_kernel(const int32_t* __restrict__ rev_ptr,
                                                          int32_t* __restrict__ order, HeadTable ht, XcdSplit sp,
                                                          int NB, int NG, int H) {
   __shared__ int wsum[4];
   __shared__ int run[2];
-  const int x = blockIdx.x;
-  const int32_t t0 = sp.start[x], t1 = sp.start[x + 1];
+  int32_t t0, t1;
+  xcd_segment(sp, blockIdx.x, t0, t1);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   auto is_long = [&](int32_t t) {
     const int32_t bh = t / NB, j = t % NB, h = bh % H;
@@ -488,13 +489,13 @@ template <int D, int G>
 hipError_t dkdv_launch(const Shape& s, const BwdWork& w, const int32_t* rev_ptr, const int32_t* rev_idx, float* dK,
                        float* dV, const HeadTable& ht, hipStream_t st) {
   const float tau = 1.0f / sqrtf((float)D);
-  // a KV block costs its reverse-list length, NG * k_h / NB on average, + 1
+  // a KV block costs its reverse-list length, NG * k_h / NB on average, + 1; a head streams its Q and dO
   unsigned nwg = 0;
-  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NB, ht, (double)s.NG / s.NB, 1.0, &nwg);
+  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NB, ht, (double)s.NG / s.NB, 1.0, 4.0 * s.N * D, &nwg);
+  const unsigned nseg = sp.items ? kXcds * (unsigned)sp.runs : kXcds;
   // dense (no reverse lists): every block has all NG groups and the order is the identity
   if (rev_ptr)
-    hipLaunchKernelGGL(dkdv_order_kernel, dim3(kXcds), dim3(256), 0, st, rev_ptr, w.order, ht, sp, s.NB, s.NG,
-                       s.H);
+    hipLaunchKernelGGL(dkdv_order_kernel, dim3(nseg), dim3(256), 0, st, rev_ptr, w.order, ht, sp, s.NB, s.NG, s.H);
   auto kern = rev_ptr ? bwd_dkdv_kernel<D, G, true> : bwd_dkdv_kernel<D, G, false>;
   hipLaunchKernelGGL(kern, dim3(nwg), dim3(256), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, rev_ptr, rev_idx,
                      w.order, dK, dV, ht, sp, s.N, s.H, s.NB, s.B, tau);
@@ -506,7 +507,7 @@ hipError_t dq_launch(const Shape& s, const BwdWork& w, const int32_t* idx, const
                      const HeadTable& ht, hipStream_t st) {
   const float tau = 1.0f / sqrtf((float)D);
   unsigned nwg = 0;
-  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0, 1.0, &nwg);  // a group costs k_h blocks + 1
+  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0, 1.0, 4.0 * s.N * D, &nwg);  // a group costs k_h + 1
   auto kern = idx ? bwd_dq_kernel<D, G, true> : bwd_dq_kernel<D, G, false>;
   hipLaunchKernelGGL(kern, dim3(nwg), dim3(G * 4), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, idx, cnt, dQ, ht,
                      sp, s.N, s.H, s.B, tau * kLog2e, tau);

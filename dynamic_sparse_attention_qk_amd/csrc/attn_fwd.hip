@@ -396,8 +396,8 @@ hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* 
                       hipStream_t st) {
   const float scale_log2 = (1.0f / sqrtf((float)D)) * kLog2e;
   unsigned nwg = 0;
-  // a (group, part) task costs k_h / n_split blocks + 1
-  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG * n_split, ht, 1.0 / n_split, 1.0, &nwg);
+  // a (group, part) task costs k_h / n_split blocks + 1; a head streams its K and V
+  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG * n_split, ht, 1.0 / n_split, 1.0, 4.0 * s.N * D, &nwg);
   dim3 grid(nwg);
   if (s.bf16) {
     const hipError_t e = launch_cvt_f16(V, V16, (int64_t)s.B * s.H * s.N * D, st);

@@ -374,22 +374,51 @@ constexpr uint32_t kXcds = 8;
 // contiguous ranges of about equal work; workgroup w runs task start[x] + w / 8
 // of XCD x = w % 8, or exits at once when that is past the range.  The grid is
 // 8 x the longest range.  With equal work per task this is xcd_remap.
+// Workgroup w runs on XCD w % 8.  Tasks are numbered run by run ((b, h) pairs), `items` per run, and
+// split over the XCDs in one of two ways:
+//  - contiguous (items == 0 in the struct): XCD x runs tasks [start[x], start[x+1]), eight ranges of
+//    equal estimated work; each XCD then works through a few heads of its own;
+//  - head-synchronous (items > 0): every run is cut into eight contiguous parts of equal count and XCD
+//    x takes part x of every run, runs in order, so all XCDs work on the same head at a time.
+// Both keep contiguous groups (or blocks) of one head on each XCD, which is what its L2 reuses.  The
+// host picks head-synchronous when eight heads' K and V (or Q and dO) would not fit the 256 MB MALL.
 struct XcdSplit {
   int32_t start[kXcds + 1];
+  int32_t items;  // head-synchronous: tasks per run (0: contiguous ranges)
+  int32_t runs;   // head-synchronous: B * H
 };
 
 __device__ __forceinline__ int64_t xcd_task(const XcdSplit& sp, uint32_t w) {
-  const uint32_t x = w % kXcds, i = w / kXcds;
-  const int64_t t = (int64_t)sp.start[x] + i;
-  return t < sp.start[x + 1] ? t : -1;
+  const int32_t x = (int32_t)(w % kXcds), i = (int32_t)(w / kXcds);
+  if (sp.items == 0) {
+    const int64_t t = (int64_t)sp.start[x] + i;
+    return t < sp.start[x + 1] ? t : -1;
+  }
+  const int32_t lo = (int32_t)((int64_t)x * sp.items / kXcds);
+  const int32_t len = (int32_t)((int64_t)(x + 1) * sp.items / kXcds) - lo;
+  if (len <= 0) return -1;
+  const int32_t run = i / len;
+  if (run >= sp.runs) return -1;
+  return (int64_t)run * sp.items + lo + i % len;
 }
 
-// Host: split of the B*H*items tasks when a task of head h costs k_h * scale + overhead.
+// Host: the split of the B*H*items tasks, a task of head h costing k_h * scale + overhead; head_bytes is
+// what one (b, h) run streams (K and V, or Q and dO), which decides the mode.  grid covers the largest part.
 inline XcdSplit make_xcd_split(int B, int H, int items, const HeadTable& ht, double scale, double overhead,
-                               unsigned* grid) {
+                               double head_bytes, unsigned* grid) {
+  constexpr double kMallBytes = 256.0 * 1024 * 1024;
+  XcdSplit sp;
+  if (kXcds * head_bytes > kMallBytes) {
+    sp.items = items;
+    sp.runs = B * H;
+    for (uint32_t i = 0; i <= kXcds; ++i) sp.start[i] = 0;
+    *grid = kXcds * (unsigned)((items + kXcds - 1) / kXcds) * (unsigned)(B * H);
+    return sp;
+  }
+  sp.items = 0;
+  sp.runs = 0;
   double total = 0.0;
   for (int h = 0; h < H; ++h) total += (double)B * items * (ht.k[h] * scale + overhead);
-  XcdSplit sp;
   sp.start[0] = 0;
   uint32_t x = 1;
   double cum = 0.0;
@@ -410,6 +439,18 @@ inline XcdSplit make_xcd_split(int B, int H, int items, const HeadTable& ht, dou
   for (uint32_t i = 0; i < kXcds; ++i) longest = std::max(longest, sp.start[i + 1] - sp.start[i]);
   *grid = kXcds * (unsigned)longest;
   return sp;
+}
+
+// The XCD parts as segments [first, last) of the task range: the contiguous ranges, or one per (run, XCD).
+__device__ __forceinline__ void xcd_segment(const XcdSplit& sp, int s, int32_t& first, int32_t& last) {
+  if (sp.items == 0) {
+    first = sp.start[s];
+    last = sp.start[s + 1];
+    return;
+  }
+  const int x = s % kXcds, run = s / kXcds;
+  first = run * sp.items + (int32_t)((int64_t)x * sp.items / kXcds);
+  last = run * sp.items + (int32_t)((int64_t)(x + 1) * sp.items / kXcds);
 }
 
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t n) {

@@ -22,6 +22,8 @@ groups of consecutive tokens):
    or, by coverage, the shortest run of blocks in score order whose estimated
    attention mass (softmax of the block scores) reaches a fraction, capped
    per head (rows then differ in length)            [hi §2.A critical KV ~90%]
+   and, in either rule, optionally with the blocks that hold the group's own
+   tokens always kept (a forced diagonal; a variant, not from the pages)
 5. exact softmax attention of every query of the group over the keys of its
    kept blocks only (no mask beyond the selection; bidirectional)
                                                     [hi §2.A stage 2, nl §2.A fase 2]
@@ -110,6 +112,40 @@ def select_row(scores_row: np.ndarray, k: int) -> np.ndarray:
     s = np.asarray(scores_row)
     order = np.lexsort((np.arange(nb), -s))      # primary key -s, secondary key j
     return np.sort(order[:k]).astype(np.int64)
+
+
+def diagonal_blocks(g: int, group: int, n_blocks: int, block: int = BLOCK) -> np.ndarray:
+    """The KV blocks that hold query group g's own tokens."""
+    return np.arange(g * group // block, min((g + 1) * group // block, n_blocks))
+
+
+def select_order(scores_row: np.ndarray, forced: Sequence[int] = ()) -> np.ndarray:
+    """Blocks in selection order: the forced ones first (ascending), then the rest by decreasing score,
+    ties to the lowest id."""
+    nb = len(scores_row)
+    s = np.asarray(scores_row)
+    order = np.lexsort((np.arange(nb), -s))
+    f = np.asarray(sorted(int(j) for j in forced), dtype=np.int64)
+    return np.concatenate([f, order[~np.isin(order, f)]]).astype(np.int64)
+
+
+def select_row_diag(scores_row: np.ndarray, k: int, g: int, group: int, block: int = BLOCK) -> np.ndarray:
+    """Top-k with the group's own blocks always kept (k at least their number): the first k blocks of
+    select_order with those blocks forced, ascending."""
+    forced = diagonal_blocks(g, group, len(scores_row), block)
+    assert len(forced) <= k <= len(scores_row)
+    return np.sort(select_order(scores_row, forced)[:k])
+
+
+def select_coverage_row_diag(scores_row: np.ndarray, coverage: float, k_cap: int, g: int, group: int,
+                             block: int = BLOCK) -> np.ndarray:
+    """Coverage selection whose run starts with the group's own blocks (always kept, their estimated mass
+    counted), then the rest in score order; at most k_cap blocks (k_cap at least the forced count)."""
+    forced = diagonal_blocks(g, group, len(scores_row), block)
+    order = select_order(scores_row, forced)
+    cum = np.cumsum(block_mass(scores_row)[order])
+    c = max(len(forced), 1 + int(np.count_nonzero(cum < coverage)))
+    return np.sort(order[:min(c, k_cap, len(scores_row))])
 
 
 def select(scores: np.ndarray, k_per_head: Sequence[int]) -> List[List[np.ndarray]]:

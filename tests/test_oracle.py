@@ -498,6 +498,43 @@ def check_ragged_attention_brute(seed=53, n=384, group=64):
         assert list(rev[j]) == [g for g in range(len(idx)) if j in set(idx[g].tolist())]
 
 
+def check_diagonal_brute(seed=54):
+    rng = _rng(seed)
+    for trial in range(40):
+        group = int(rng.choice([64, 128]))
+        ng = int(rng.integers(1, 9))
+        nb = ng * group // 64
+        g = int(rng.integers(0, ng))
+        row = rng.standard_normal(nb) * float(rng.choice([0.5, 3.0]))
+        if trial % 2:
+            row = np.round(row)                            # ties
+        own = list(range(g * group // 64, (g + 1) * group // 64))
+        rest = [j for _, j in sorted((-float(row[j]), j) for j in range(nb) if j not in own)]
+        for k in range(len(own), nb + 1):
+            assert list(O.select_row_diag(row, k, g, group)) == sorted(own + rest[:k - len(own)])
+        mx = max(float(x) for x in row)
+        w = [math.exp(float(x) - mx) for x in row]
+        z = math.fsum(w)
+        for cov in (0.01, 0.5, 0.9, 1.0):
+            for cap in (len(own), nb):
+                taken = []
+                for j in own + rest:
+                    taken.append(j)
+                    done = len(taken) >= len(own) and math.fsum(w[t] / z for t in taken) >= cov
+                    if done or len(taken) == cap:
+                        break
+                got = list(O.select_coverage_row_diag(row, cov, cap, g, group))
+                if got != sorted(taken):   # only a prefix mass within rounding of the target may differ
+                    cum = np.cumsum(O.block_mass(row)[O.select_order(row, own)])
+                    c = min(len(got), len(taken))
+                    assert abs(len(got) - len(taken)) == 1 and abs(cum[c - 1] - cov) < 1e-12
+    # the forced blocks alone when k is their number; without a diagonal the rules are the plain ones
+    row = np.arange(8.0)
+    assert list(O.select_row_diag(row, 2, 0, 128)) == [0, 1]
+    assert list(O.select_row_diag(row, 3, 0, 128)) == [0, 1, 7]
+    assert list(O.select_order(row)) == list(range(7, -1, -1))
+
+
 ALL_CHECKS = [
     check_scores_brute, check_identity_predictor, check_select_brute, check_select_special,
     check_duplicate_blocks_tie, check_linearity, check_forward_brute, check_dense_equals_sdpa,
@@ -506,7 +543,7 @@ ALL_CHECKS = [
     check_split_merge_equals_unsplit, check_partial_states_brute, check_merge_algebra, check_dense_sdpa,
     check_dense_brute, check_dense_closed_forms, check_dense_sampled, check_dispatch_rule,
     check_pred_loss_brute, check_pred_loss_closed_forms, check_coverage_brute, check_coverage_closed_forms,
-    check_ragged_attention_brute,
+    check_ragged_attention_brute, check_diagonal_brute,
 ]
 
 
@@ -746,3 +783,9 @@ def test_mutation_coverage_ties_high(monkeypatch):
         c = 1 + int(np.count_nonzero(cum < coverage))
         return np.sort(order[:min(c, k_cap, nb)])
     assert _fails_some_pin(monkeypatch, "select_coverage_row", bad, [check_coverage_brute, check_coverage_closed_forms])
+
+
+def test_mutation_diagonal_off_by_one_group(monkeypatch):
+    def bad(g, group, n_blocks, block=64):
+        return np.arange((g + 1) * group // block, min((g + 2) * group // block, n_blocks))
+    assert _fails_some_pin(monkeypatch, "diagonal_blocks", bad, [check_diagonal_brute])

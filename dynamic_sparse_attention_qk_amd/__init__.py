@@ -81,6 +81,8 @@ def library() -> ctypes.CDLL:
         lib.dsa_select_coverage_blocks.argtypes = [pp, f32p, f32p, f32p, kph, ctypes.c_double, i32p, i32p, i32p,
                                                    i32p, f32p, vp, sz, vp]
         lib.dsa_sparse_attn_fwd_varlen.argtypes = [pp, vp, vp, vp, i32p, i32p, kph, f32p, f32p, vp, sz, vp]
+        lib.dsa_select_blocks.argtypes = [pp, f32p, f32p, f32p, kph, ctypes.c_double, ctypes.c_int, i32p, i32p, i32p,
+                                          i32p, f32p, vp, sz, vp]
         lib.dsa_sparse_attn_bwd_varlen.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, i32p, kph, i32p, i32p,
                                                    f32p, f32p, f32p, vp, sz, vp]
         for name in ("dsa_index_layout", "dsa_predict_block_scores", "dsa_select_topk_blocks",
@@ -88,7 +90,7 @@ def library() -> ctypes.CDLL:
                      "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_fwd_split",
                      "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd", "dsa_choose_path",
                      "dsa_predictor_loss_grad", "dsa_select_coverage_blocks", "dsa_sparse_attn_fwd_varlen",
-                     "dsa_sparse_attn_bwd_varlen"):
+                     "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -99,7 +101,8 @@ EXPORTED = ("dsa_version", "dsa_status_string", "dsa_index_layout", "dsa_workspa
             "dsa_sparse_attn_bwd_preprocess", "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq",
             "dsa_sparse_attn_fwd_split", "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd",
             "dsa_choose_path", "dsa_predictor_loss_grad", "dsa_select_coverage_blocks", "dsa_sparse_attn_fwd_varlen",
-            "dsa_sparse_attn_bwd_varlen")
+            "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks")
+SELECT_DIAGONAL = 1  # DSA_SELECT_DIAGONAL
 MAX_SPLIT = 64  # DSA_MAX_SPLIT
 PATH_DENSE, PATH_SPARSE = 0, 1  # dsa_path
 DEFAULT_MIN_SPARSITY = 0.06     # DSA_DEFAULT_MIN_SPARSITY
@@ -196,6 +199,15 @@ def select_coverage_blocks(p: Problem, scores, qhat, khat, k_per_head, coverage:
     _check("dsa_select_coverage_blocks", library().dsa_select_coverage_blocks(
         ctypes.byref(p.c()), _ptr(scores), _ptr(qhat), _ptr(khat), _kph(k_per_head), float(coverage), _ptr(idx),
         _ptr(cnt), _ptr(rev_ptr), _ptr(rev_idx), _ptr(scores_dump), _ptr(workspace), _nbytes(workspace),
+        _stream(stream)))
+
+
+def select_blocks(p: Problem, scores, qhat, khat, k_per_head, coverage: float, flags: int, idx, cnt, rev_ptr,
+                  rev_idx, workspace, scores_dump=None, stream=None) -> None:
+    """The general selection: top-k (coverage 0) or by coverage, optionally with the diagonal forced."""
+    _check("dsa_select_blocks", library().dsa_select_blocks(
+        ctypes.byref(p.c()), _ptr(scores), _ptr(qhat), _ptr(khat), _kph(k_per_head), float(coverage), int(flags),
+        _ptr(idx), _ptr(cnt), _ptr(rev_ptr), _ptr(rev_idx), _ptr(scores_dump), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
 
 
@@ -300,12 +312,13 @@ class SparseAttentionPlan:
     """Outputs and workspaces of one problem, allocated once with torch, plus the calls in order."""
 
     def __init__(self, p: Problem, k_per_head: Sequence[int], device="cuda", materialise_scores: bool = True,
-                 backward: bool = True, coverage: Optional[float] = None):
+                 backward: bool = True, coverage: Optional[float] = None, select_flags: int = 0):
         """coverage: select by attention coverage (k_per_head is then each row's capacity) and run the
-        per-row-count forward and backward."""
+        per-row-count forward and backward; select_flags: SELECT_DIAGONAL keeps each group's own blocks."""
         self.p = p
         self.k_per_head = [int(x) for x in k_per_head]
         self.coverage = coverage
+        self.select_flags = int(select_flags)
         self.cnt = (torch.empty(p.batch, p.heads, p.n_groups, dtype=torch.int32, device=device)
                     if coverage is not None else None)
         self.row_base = index_layout(p, self.k_per_head)
@@ -336,7 +349,11 @@ class SparseAttentionPlan:
         predict_block_scores(self.p, Q, K, Wq, Wk, self.qhat, self.khat, self.scores, stream)
 
     def select(self, stream=None, scores_dump=None):
-        if self.coverage is not None:
+        if self.select_flags:
+            select_blocks(self.p, self.scores, self.qhat, self.khat, self.k_per_head,
+                          0.0 if self.coverage is None else self.coverage, self.select_flags, self.idx, self.cnt,
+                          self.rev_ptr, self.rev_idx, self.ws_select, scores_dump=scores_dump, stream=stream)
+        elif self.coverage is not None:
             select_coverage_blocks(self.p, self.scores, self.qhat, self.khat, self.k_per_head, self.coverage,
                                    self.idx, self.cnt, self.rev_ptr, self.rev_idx, self.ws_select,
                                    scores_dump=scores_dump, stream=stream)

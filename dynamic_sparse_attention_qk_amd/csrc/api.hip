@@ -202,14 +202,19 @@ int dsa_predict_block_scores(const dsa_problem* p, const void* Q, const void* K,
 }
 
 static int select_impl(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,
-                       const int32_t* k_per_head, int32_t* idx, int32_t* cnt, float coverage, int32_t* rev_ptr,
-                       int32_t* rev_idx, float* scores_dump, void* workspace, size_t workspace_bytes, void* stream) {
+                       const int32_t* k_per_head, int32_t* idx, int32_t* cnt, float coverage, int flags,
+                       int32_t* rev_ptr, int32_t* rev_idx, float* scores_dump, void* workspace,
+                       size_t workspace_bytes, void* stream) {
   Shape s;
   HeadTable ht;
   int kmax = 0;
   int st = check_problem(p, &s);
   if (st) return st;
   if ((st = check_heads(s, k_per_head, &ht, &kmax))) return st;
+  if (flags & ~DSA_SELECT_DIAGONAL) return DSA_ERR_INVALID_ARG;
+  const int diag = (flags & DSA_SELECT_DIAGONAL) ? s.G : 0;
+  for (int h = 0; diag && h < s.H; ++h)
+    if (ht.k[h] < s.G / dsa::kBlock) return DSA_ERR_SHAPE;  // room for the forced blocks
   if (!idx || !rev_ptr || !rev_idx) return DSA_ERR_INVALID_ARG;
   if (!scores && (!qhat || !khat)) return DSA_ERR_INVALID_ARG;
   if ((scores && !aligned16(scores)) || (!scores && (!aligned16(qhat) || !aligned16(khat))) || !aligned16(idx) ||
@@ -224,7 +229,7 @@ static int select_impl(const dsa_problem* p, const float* scores, const float* q
   int32_t* scratch = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
                                                 align256((size_t)s.B * s.H * s.NB * sizeof(int32_t)));
   hipError_t e = dsa::launch_topk_select(s, scores, qhat, khat, idx, scores ? nullptr : scores_dump, ht, tau, kmax, hs,
-                                         cnt, coverage);
+                                         cnt, coverage, diag);
   if (e == hipSuccess) e = dsa::launch_reverse_index(s, idx, rev_ptr, rev_idx, counters, scratch, ht, kmax, hs);
   return hip_status(e);
 }
@@ -232,8 +237,21 @@ static int select_impl(const dsa_problem* p, const float* scores, const float* q
 int dsa_select_topk_blocks(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,
                            const int32_t* k_per_head, int32_t* idx, int32_t* rev_ptr, int32_t* rev_idx,
                            float* scores_dump, void* workspace, size_t workspace_bytes, void* stream) {
-  return select_impl(p, scores, qhat, khat, k_per_head, idx, nullptr, 1.0f, rev_ptr, rev_idx, scores_dump, workspace,
-                     workspace_bytes, stream);
+  return select_impl(p, scores, qhat, khat, k_per_head, idx, nullptr, 1.0f, 0, rev_ptr, rev_idx, scores_dump,
+                     workspace, workspace_bytes, stream);
+}
+
+int dsa_select_blocks(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,
+                      const int32_t* k_per_head, double coverage, int flags, int32_t* idx, int32_t* cnt,
+                      int32_t* rev_ptr, int32_t* rev_idx, float* scores_dump, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!(coverage >= 0.0 && coverage <= 1.0)) return DSA_ERR_INVALID_ARG;
+  if (coverage > 0.0) {
+    if (!cnt) return DSA_ERR_INVALID_ARG;
+    if (!aligned16(cnt)) return DSA_ERR_ALIGN;
+  }
+  return select_impl(p, scores, qhat, khat, k_per_head, idx, coverage > 0.0 ? cnt : nullptr, (float)coverage, flags,
+                     rev_ptr, rev_idx, scores_dump, workspace, workspace_bytes, stream);
 }
 
 int dsa_select_coverage_blocks(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,
@@ -243,7 +261,7 @@ int dsa_select_coverage_blocks(const dsa_problem* p, const float* scores, const 
   if (!(coverage > 0.0 && coverage <= 1.0)) return DSA_ERR_INVALID_ARG;
   if (!cnt) return DSA_ERR_INVALID_ARG;
   if (!aligned16(cnt)) return DSA_ERR_ALIGN;
-  return select_impl(p, scores, qhat, khat, k_per_head, idx, cnt, (float)coverage, rev_ptr, rev_idx, scores_dump,
+  return select_impl(p, scores, qhat, khat, k_per_head, idx, cnt, (float)coverage, 0, rev_ptr, rev_idx, scores_dump,
                      workspace, workspace_bytes, stream);
 }
 

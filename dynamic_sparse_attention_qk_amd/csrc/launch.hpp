@@ -19,10 +19,11 @@ hipError_t launch_pool_project(const Shape& s, const void* X, const float* W, fl
                                hipStream_t st, float* mean_out = nullptr);
 hipError_t launch_block_scores(const Shape& s, const float* qhat, const float* khat, float* scores,
                                float tau, hipStream_t st);
-// cnt (if not null): select by attention coverage (kept counts per row to cnt [B,H,NG], unused slots -1)
+// cnt (if not null): select by attention coverage (kept counts per row to cnt [B,H,NG], unused slots -1);
+// diag_group > 0: the blocks holding each group's own diag_group tokens are always kept
 hipError_t launch_topk_select(const Shape& s, const float* scores, const float* qhat, const float* khat,
                               int32_t* idx, float* dump, const HeadTable& ht, float tau, int kmax,
-                              hipStream_t st, int32_t* cnt = nullptr, float coverage = 1.0f);
+                              hipStream_t st, int32_t* cnt = nullptr, float coverage = 1.0f, int diag_group = 0);
 hipError_t launch_reverse_index(const Shape& s, const int32_t* idx, int32_t* rev_ptr, int32_t* rev_idx,
                                 int32_t* counters, int32_t* scratch, const HeadTable& ht, int kmax,
                                 hipStream_t st);

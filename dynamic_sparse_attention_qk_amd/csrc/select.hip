@@ -51,6 +51,8 @@ __device__ __forceinline__ float wave_mass_ge(const uint32_t (&key)[KPL], const 
 // COVER: the row keeps the shortest run of blocks, in score order, whose estimated attention mass (the
 // softmax of the row's block scores) reaches `coverage` of the total, at most k_h; the count goes to
 // cnt[b,h,g] and the row's unused slots get -1.
+// diag_group > 0: the blocks holding the row's own diag_group query tokens are kept first (their keys are
+// raised above every score; in COVER mode their real masses still count).
 template <int KPL, int R, bool STREAM, bool COVER>
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* __restrict__ scores,
                                                                    const float* __restrict__ qhat,
@@ -58,7 +60,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
                                                                    int32_t* __restrict__ idx,
                                                                    int32_t* __restrict__ cnt,
                                                                    float* __restrict__ dump, HeadTable ht, int NG,
-                                                                   int NB, int H, float tau, float coverage) {
+                                                                   int NB, int H, float tau, float coverage,
+                                                                   int diag_group) {
   constexpr int CH = KPL < 4 ? KPL : (R > 32 ? 2 : 4);  // 64-block chunks of khat staged per LDS round
   __shared__ float sk[STREAM ? 64 * CH : 1][R + 1];
   const int b = blockIdx.z, h = blockIdx.y;
@@ -111,6 +114,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
   if (!valid) return;  // wave-uniform; all barriers are behind us
 
   const int kcap = ht.k[h];
+  // forced blocks [d0, d1): the ones that hold this group's tokens
+  const int d0 = diag_group ? g * diag_group / kBlock : 0, d1 = diag_group ? (g + 1) * diag_group / kBlock : 0;
   int k = kcap;
   uint32_t T = 0, need = 0;
   bool counted = true;  // T and need still to be found by the count bisection for k
@@ -124,7 +129,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
     const float smax = key_score(kmax);
     float e[KPL];
 #pragma unroll
-    for (int t = 0; t < KPL; ++t) e[t] = key[t] ? expf(key_score(key[t]) - smax) : 0.f;
+    for (int t = 0; t < KPL; ++t) {
+      e[t] = key[t] ? expf(key_score(key[t]) - smax) : 0.f;
+      const int j = lane + 64 * t;
+      if (j >= d0 && j < d1) key[t] = 0xFFFFFFFFu;  // forced: above every real score (their masses stay)
+    }
     const float target = coverage * wave_mass_ge<KPL>(key, e, 0u);
     // T = max{x : M(x) >= target}, M(x) = mass of the keys >= x (non-increasing in x)
 #pragma unroll 1
@@ -140,9 +149,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
     const float e_t = expf(key_score(T) - smax);
     // smallest m >= 1 (at most n_eq) with m_gt + m e_t >= target: start near the quotient, then step
     uint32_t m = 1;
-    if (e_t > 0.f) m = (uint32_t)fminf(fmaxf((target - m_gt) / e_t - 1.f, 1.f), (float)n_eq);
-    while (m > 1 && m_gt + (float)(m - 1) * e_t >= target) --m;
-    while (m < n_eq && m_gt + (float)m * e_t < target) ++m;
+    if (top) {
+      m = n_eq;  // the forced blocks alone reach the target: all of them, nothing else
+    } else {
+      if (e_t > 0.f) m = (uint32_t)fminf(fmaxf((target - m_gt) / e_t - 1.f, 1.f), (float)n_eq);
+      while (m > 1 && m_gt + (float)(m - 1) * e_t >= target) --m;
+      while (m < n_eq && m_gt + (float)m * e_t < target) ++m;
+    }
     if ((int)(n_gt + m) <= kcap) {
       k = (int)(n_gt + m);
       need = m;
@@ -150,6 +163,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
     }
   }
   if (counted) {
+    if constexpr (!COVER) {
+#pragma unroll
+      for (int t = 0; t < KPL; ++t) {
+        const int j = lane + 64 * t;
+        if (j >= d0 && j < d1) key[t] = 0xFFFFFFFFu;  // forced: above every real score
+      }
+    }
     // Bisection for T = max{x : #(key >= x) >= k}; keys of real scores are > 0.
     T = 0;
 #pragma unroll 1
@@ -182,37 +202,39 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
 
 template <int KPL, int R, bool COVER>
 void select_launch_c(const Shape& s, const float* scores, const float* qhat, const float* khat, int32_t* idx,
-                     int32_t* cnt, float* dump, const HeadTable& ht, float tau, float coverage, hipStream_t st) {
+                     int32_t* cnt, float* dump, const HeadTable& ht, float tau, float coverage, int diag,
+                     hipStream_t st) {
   dim3 grid((s.NG + 3) / 4, s.H, s.B);
   if (scores)
     hipLaunchKernelGGL((topk_select_kernel<KPL, R, false, COVER>), grid, dim3(kSelThreads), 0, st, scores, qhat, khat,
-                       idx, cnt, dump, ht, s.NG, s.NB, s.H, tau, coverage);
+                       idx, cnt, dump, ht, s.NG, s.NB, s.H, tau, coverage, diag);
   else
     hipLaunchKernelGGL((topk_select_kernel<KPL, R, true, COVER>), grid, dim3(kSelThreads), 0, st, scores, qhat, khat,
-                       idx, cnt, dump, ht, s.NG, s.NB, s.H, tau, coverage);
+                       idx, cnt, dump, ht, s.NG, s.NB, s.H, tau, coverage, diag);
 }
 
 template <int KPL, int R>
 hipError_t select_launch(const Shape& s, const float* scores, const float* qhat, const float* khat, int32_t* idx,
-                         int32_t* cnt, float* dump, const HeadTable& ht, float tau, float coverage, hipStream_t st) {
+                         int32_t* cnt, float* dump, const HeadTable& ht, float tau, float coverage, int diag,
+                         hipStream_t st) {
   if (cnt)
-    select_launch_c<KPL, R, true>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+    select_launch_c<KPL, R, true>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
   else
-    select_launch_c<KPL, R, false>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+    select_launch_c<KPL, R, false>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
   return hipGetLastError();
 }
 
 template <int KPL>
 hipError_t select_dispatch_r(const Shape& s, const float* scores, const float* qhat, const float* khat,
                              int32_t* idx, int32_t* cnt, float* dump, const HeadTable& ht, float tau, float coverage,
-                             hipStream_t st) {
+                             int diag, hipStream_t st) {
   if (scores)  // the rank only matters when streaming
-    return select_launch<KPL, 8>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+    return select_launch<KPL, 8>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
   switch (s.R) {
-    case 8: return select_launch<KPL, 8>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
-    case 16: return select_launch<KPL, 16>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
-    case 32: return select_launch<KPL, 32>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
-    case 64: return select_launch<KPL, 64>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+    case 8: return select_launch<KPL, 8>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
+    case 16: return select_launch<KPL, 16>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
+    case 32: return select_launch<KPL, 32>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
+    case 64: return select_launch<KPL, 64>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -332,17 +354,18 @@ __global__ __launch_bounds__(256) void rev_sort_kernel(const int32_t* __restrict
 
 hipError_t launch_topk_select(const Shape& s, const float* scores, const float* qhat, const float* khat, int32_t* idx,
                               float* dump, const HeadTable& ht, float tau, int kmax, hipStream_t st, int32_t* cnt,
-                              float coverage) {
+                              float coverage, int diag_group) {
+  const int diag = diag_group;
   (void)kmax;
   const int kpl = (s.NB + 63) / 64;
-  if (kpl <= 1) return select_dispatch_r<1>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
-  if (kpl <= 2) return select_dispatch_r<2>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
-  if (kpl <= 4) return select_dispatch_r<4>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
-  if (kpl <= 8) return select_dispatch_r<8>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
-  if (kpl <= 16) return select_dispatch_r<16>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
-  if (kpl <= 32) return select_dispatch_r<32>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
-  if (kpl <= 64) return select_dispatch_r<64>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
-  if (kpl <= 128) return select_dispatch_r<128>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, st);
+  if (kpl <= 1) return select_dispatch_r<1>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
+  if (kpl <= 2) return select_dispatch_r<2>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
+  if (kpl <= 4) return select_dispatch_r<4>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
+  if (kpl <= 8) return select_dispatch_r<8>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
+  if (kpl <= 16) return select_dispatch_r<16>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
+  if (kpl <= 32) return select_dispatch_r<32>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
+  if (kpl <= 64) return select_dispatch_r<64>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
+  if (kpl <= 128) return select_dispatch_r<128>(s, scores, qhat, khat, idx, cnt, dump, ht, tau, coverage, diag, st);
   return hipErrorInvalidValue;
 }
 

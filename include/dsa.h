@@ -181,6 +181,28 @@ int dsa_select_coverage_blocks(const dsa_problem* p, const float* scores, const 
                                int32_t* cnt, int32_t* rev_ptr, int32_t* rev_idx, float* scores_dump,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* Flags of dsa_select_blocks. */
+#define DSA_SELECT_DIAGONAL 1
+
+/*
+ * dsa_select_blocks -- the general selection call.  coverage == 0: each row
+ * keeps its top k_h blocks (dsa_select_topk_blocks; cnt is not written and
+ * may be NULL); 0 < coverage <= 1: the coverage rule of
+ * dsa_select_coverage_blocks (cnt required).  flags: 0, or
+ * DSA_SELECT_DIAGONAL: the blocks holding the row's own G query tokens
+ * (blocks g*G/64 .. (g+1)*G/64 - 1) are always kept and come first in the
+ * selection order, ahead of every score (a variant, not from the pages: a
+ * local window next to the predicted blocks); in coverage mode their
+ * estimated masses count towards the target.  With it every k_h must be at
+ * least G/64 (else DSA_ERR_SHAPE).  Other flags, or coverage outside
+ * [0, 1]: DSA_ERR_INVALID_ARG.  Output layout, workspace and the other
+ * arguments as dsa_select_topk_blocks / dsa_select_coverage_blocks.
+ */
+int dsa_select_blocks(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,
+                      const int32_t* k_per_head, double coverage, int flags, int32_t* idx, int32_t* cnt,
+                      int32_t* rev_ptr, int32_t* rev_idx, float* scores_dump, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /*
  * dsa_sparse_attn_fwd_varlen / dsa_sparse_attn_bwd_varlen -- the forward and
  * backward above for rows of different lengths: row (b,h,g) attends to the

@@ -283,3 +283,22 @@ def test_coverage_calls_validation():
     args[7] = FAKE
     f32 = ctypes.byref(_p(dtype=dsa.DSA_F32).c())
     assert lib.dsa_sparse_attn_bwd_varlen(f32, *args, FAKE, big, None) == -3
+
+
+def test_select_blocks_validation():
+    lib = dsa.library()
+    big = 1 << 40
+
+    def call(p, kph, cov, flags, cnt=FAKE):
+        return lib.dsa_select_blocks(ctypes.byref(p.c()), FAKE, FAKE, FAKE, dsa._kph(kph), cov, flags, FAKE, cnt, FAKE,
+                                     FAKE, None, FAKE, big, None)
+    p64, p128 = _p(), _p(group=128)
+    assert call(p64, [4, 4], 0.0, 2) == -1                  # unknown flag
+    assert call(p64, [4, 4], -0.1, 0) == -1
+    assert call(p64, [4, 4], 1.5, 0) == -1
+    assert call(p64, [4, 4], float("nan"), 0) == -1
+    assert call(p64, [4, 4], 0.5, 0, None) == -1            # coverage needs the counts
+    assert call(p64, [4, 4], 0.5, 0, ctypes.c_void_p(0x100004)) == -4
+    assert call(p128, [1, 4], 0.0, dsa.SELECT_DIAGONAL) == -2   # G = 128 forces two blocks: k_h >= 2
+    assert lib.dsa_select_blocks(ctypes.byref(p64.c()), FAKE, FAKE, FAKE, dsa._kph([4, 4]), 0.0, 0, FAKE, None, FAKE,
+                                 FAKE, None, None, 0, None) == -6

@@ -23,10 +23,10 @@ def _gpu():
     dsa.library()
 
 
-def _wl(grid, heads, d, group, rank=16, dtype="bf16", backward=True, seed=71):
+def _wl(grid, heads, d, group, rank=16, dtype="bf16", backward=True, seed=71, batch=1):
     nb = grid[0] * grid[1] * grid[2] // 64
-    return synth.Workload(f"dense_{grid}_{heads}_{d}_{group}_{dtype}", seed, 1, heads, d, grid, 8, 3.0, rank, group,
-                          k=nb, dtype=dtype, backward=backward)
+    return synth.Workload(f"dense_{grid}_{heads}_{d}_{group}_{dtype}_{batch}", seed, batch, heads, d, grid, 8, 3.0,
+                          rank, group, k=nb, dtype=dtype, backward=backward)
 
 
 CASES = [
@@ -37,6 +37,7 @@ CASES = [
     ("d128_g64_one_block", _wl((1, 8, 8), 3, 128, 64, rank=8)),
     ("d64_g128_two_blocks", _wl((1, 8, 16), 2, 64, 128)),
     ("d128_g64_ragged_tail", _wl((5, 8, 24), 2, 128, 64, rank=64)),   # 15 blocks: a partial last 8-block wave
+    ("batch2_d64_g128", _wl((2, 16, 16), 2, 64, 128, batch=2)),
 ]
 
 

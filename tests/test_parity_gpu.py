@@ -28,9 +28,10 @@ def _gpu():
     dsa.library()
 
 
-def _wl(grid, heads, d, group, k=None, rank=16, dtype="bf16", backward=True, centres=8, seed=77, kph=None):
-    w = synth.Workload(f"small_{grid}_{heads}_{d}_{group}", seed, 1, heads, d, grid, centres, 3.0, rank, group,
-                       k=k, dtype=dtype, backward=backward)
+def _wl(grid, heads, d, group, k=None, rank=16, dtype="bf16", backward=True, centres=8, seed=77, kph=None,
+        batch=1):
+    w = synth.Workload(f"small_{grid}_{heads}_{d}_{group}_{batch}", seed, batch, heads, d, grid, centres, 3.0, rank,
+                       group, k=k, dtype=dtype, backward=backward)
     return w
 
 
@@ -58,6 +59,8 @@ SMALL = [
     ("d64_g64_nb70", _wl((4, 28, 40), 2, 64, 64, k=9, rank=8), None),
     ("d128_ragged_heads", _wl((4, 16, 32), 4, 128, 64, k=1, rank=64), [1, 3, 32, 9]),
     ("d64_g128_k1", _wl((4, 16, 32), 2, 64, 128, k=1, rank=16), None),
+    ("batch3_ragged_heads", _wl((2, 16, 32), 3, 128, 64, k=4, rank=32, batch=3), [2, 7, 4]),
+    ("batch2_fp32_fwd", _wl((2, 16, 16), 2, 64, 64, k=3, dtype="f32", backward=False, batch=2), None),
 ]
 
 

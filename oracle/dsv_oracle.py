@@ -17,6 +17,8 @@ groups of consecutive tokens):
    (d x r, r << d)                                   [hi §2.A, nl §2.A]
 3. block score s[g, j] = tau * qhat_g . khat_j -- the predictor's estimate of
    the group-to-block attention logits              [hi §2.A, §2.B query grouping]
+   (a variant pools the token-level predicted logits of each G x 64 tile by
+   max or by log-mean-exp instead of pooling Q and K first)
 4. per group, the k_h blocks of largest score, ties to the lowest block id,
    listed ascending -- the "critical" KV blocks     [hi §2.A, §2.B fused MM + top-k]
    or, by coverage, the shortest run of blocks in score order whose estimated
@@ -94,6 +96,26 @@ def predict(q: np.ndarray, k: np.ndarray, wq: np.ndarray, wk: np.ndarray,
     khat = np.stack([np.stack([o[1] for o in row]) for row in out])
     scores = np.stack([np.stack([o[2] for o in row]) for row in out])
     return qhat, khat, scores
+
+
+def predict_head_pooled(q: np.ndarray, k: np.ndarray, wq: np.ndarray, wk: np.ndarray, group: int, pooling: str,
+                        block: int = BLOCK) -> np.ndarray:
+    """Block scores pooled from the token-level predicted logits l[i, m] = tau (q_i W_q) . (k_m W_k) over each
+    G x 64 tile, a predictor variant: "mean" (equal to predict_head's scores), "max" (the tile's largest
+    logit), or "lse" (log of the tile's mean of exp(l): the log of the predicted attention mass per key pair,
+    so that exp(score) ranks blocks by their predicted share of the softmax)."""
+    n, d = q.shape
+    tau = 1.0 / np.sqrt(d)
+    lg = tau * ((q @ wq) @ (k @ wk).T)                              # N x N predicted logits
+    t = lg.reshape(n // group, group, n // block, block)           # [g, i, j, m]
+    if pooling == "mean":
+        return t.mean(axis=(1, 3))
+    if pooling == "max":
+        return t.max(axis=(1, 3))
+    if pooling == "lse":
+        m = t.max(axis=(1, 3), keepdims=True)
+        return (m + np.log(np.exp(t - m).mean(axis=(1, 3), keepdims=True)))[:, 0, :, 0]
+    raise ValueError(pooling)
 
 
 # ----------------------------------------------------------------------------

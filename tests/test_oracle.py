@@ -535,6 +535,36 @@ def check_diagonal_brute(seed=54):
     assert list(O.select_order(row)) == list(range(7, -1, -1))
 
 
+def check_pooled_scores_brute(seed=56, n=256, d=8, r=4, group=128):
+    q, k, _, _, wq, wk = _tiny(seed, n=n, d=d, r=r)
+    tau = 1.0 / math.sqrt(d)
+    pq, pk = q @ wq, k @ wk
+    ng, nb = n // group, n // 64
+    for pooling in ("max", "lse", "mean"):
+        got = O.predict_head_pooled(q, k, wq, wk, group, pooling)
+        for g in range(ng):
+            for j in range(nb):
+                vals = [tau * float(pq[i] @ pk[m]) for i in range(g * group, (g + 1) * group)
+                        for m in range(j * 64, (j + 1) * 64)]
+                if pooling == "max":
+                    want = max(vals)
+                elif pooling == "mean":
+                    want = math.fsum(vals) / len(vals)
+                else:
+                    mx = max(vals)
+                    want = mx + math.log(math.fsum(math.exp(v - mx) for v in vals) / len(vals))
+                assert abs(got[g, j] - want) <= 1e-12 * max(1.0, abs(want)), (pooling, g, j)
+    # mean pooling of the token logits is the pooled-proxy score of predict_head
+    np.testing.assert_allclose(O.predict_head_pooled(q, k, wq, wk, group, "mean"),
+                               O.predict_head(q, k, wq, wk, group)[2], rtol=1e-11, atol=1e-12)
+    # mean <= lse <= max, tile by tile; equal logits make all three equal
+    mean, lse, mx = (O.predict_head_pooled(q, k, wq, wk, group, x) for x in ("mean", "lse", "max"))
+    assert (mean <= lse + 1e-12).all() and (lse <= mx + 1e-12).all()
+    z = np.zeros((d, r))
+    for x in ("mean", "lse", "max"):
+        np.testing.assert_allclose(O.predict_head_pooled(q, k, z, z, group, x), 0.0, atol=1e-15)
+
+
 ALL_CHECKS = [
     check_scores_brute, check_identity_predictor, check_select_brute, check_select_special,
     check_duplicate_blocks_tie, check_linearity, check_forward_brute, check_dense_equals_sdpa,
@@ -543,7 +573,7 @@ ALL_CHECKS = [
     check_split_merge_equals_unsplit, check_partial_states_brute, check_merge_algebra, check_dense_sdpa,
     check_dense_brute, check_dense_closed_forms, check_dense_sampled, check_dispatch_rule,
     check_pred_loss_brute, check_pred_loss_closed_forms, check_coverage_brute, check_coverage_closed_forms,
-    check_ragged_attention_brute, check_diagonal_brute,
+    check_ragged_attention_brute, check_diagonal_brute, check_pooled_scores_brute,
 ]
 
 
@@ -789,3 +819,12 @@ def test_mutation_diagonal_off_by_one_group(monkeypatch):
     def bad(g, group, n_blocks, block=64):
         return np.arange((g + 1) * group // block, min((g + 2) * group // block, n_blocks))
     assert _fails_some_pin(monkeypatch, "diagonal_blocks", bad, [check_diagonal_brute])
+
+
+def test_mutation_pooled_lse_without_mean(monkeypatch):
+    orig = O.predict_head_pooled
+
+    def bad(q, k, wq, wk, group, pooling, block=64):   # log-sum-exp instead of log-mean-exp
+        out = orig(q, k, wq, wk, group, pooling, block)
+        return out + math.log(group * block) if pooling == "lse" else out
+    assert _fails_some_pin(monkeypatch, "predict_head_pooled", bad, [check_pooled_scores_brute])

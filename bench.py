@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--coverage", type=float, default=0.0,
                     help="also time the step with selection by attention coverage (this fraction; the workload's "
                          "k as each row's cap) and per-row counts")
+    ap.add_argument("--pooled", choices=["max", "lse"], default=None,
+                    help="also time the predictor variant that pools token-level logits (and the step with it)")
     ap.add_argument("--predictor-grad", action="store_true",
                     help="also time the stage-1 predictor loss + gradient call on the same inputs")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -234,6 +236,32 @@ def time_coverage(args, p, kph, Q, K, V, Wt, dO, stream, w):
             "stage_ms": {n: round(v, 4) for n, v in ms.items()}, "ms_per_step": round(step, 4),
             "tflops": round(flops / (step / 1e3) / 1e12, 2),
             "tokens_per_s": round(w.batch * w.seq_len / (step / 1e3), 1)}
+
+
+def time_pooled(args, p, kph, Q, K, Wt, stream, w):
+    """The pooled-logit predictor on the step's inputs, timed with HIP events on the bench stream, then the
+    top-k selection on its scores.  Work: the N x N low-rank product (2 N^2 r FLOP per head, fp16 MFMA)."""
+    import torch
+    import dynamic_sparse_attention_qk_amd as dsa
+    pool = {"max": dsa.POOL_MAX, "lse": dsa.POOL_LSE}[args.pooled]
+    plan = dsa.SparseAttentionPlan(p, kph, backward=False)
+    ws = torch.empty(dsa.workspace_bytes(p, None, dsa.DSA_WS_PRED_POOLED), dtype=torch.uint8, device=Q.device)
+    ms, sel = [], []
+    for i in range(args.warmup + args.steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        dsa.predict_block_scores_pooled(p, Q, K, Wt, Wt, pool, plan.scores, ws, stream)
+        ev[1].record(stream)
+        plan.select(stream)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            ms.append(ev[0].elapsed_time(ev[1]))
+            sel.append(ev[1].elapsed_time(ev[2]))
+    t = float(np.mean(ms))
+    flop = 2.0 * w.batch * w.heads * w.seq_len * w.seq_len * w.rank
+    return {"pooling": args.pooled, "predict_ms": round(t, 4), "select_ms": round(float(np.mean(sel)), 4),
+            "lowrank_tflops": round(flop / (t / 1e3) / 1e12, 2), "frac_of_fp16_peak": round(flop / (t / 1e3) / PEAK_BF16, 4)}
 
 
 SWEEP_KEEP = (0.02, 0.05, 0.1, 0.2, 0.3, 0.5, 0.7, 0.8, 0.9, 0.95, 1.0)
@@ -462,6 +490,8 @@ def main():
         rec["split_kv"] = time_split_kv(args, p, plan, Q, K, V, stream, stage_ms["fwd"], f_fwd, w)
     if args.coverage:
         rec["coverage_select"] = time_coverage(args, p, kph, Q, K, V, Wt, dO, stream, w)
+    if args.pooled:
+        rec["pooled_predictor"] = time_pooled(args, p, kph, Q, K, Wt, stream, w)
     if args.predictor_grad:
         rec["predictor_grad"] = time_predictor_grad(args, p, Q, K, Wt, stream, w)
     if args.dispatch_sweep:

@@ -28,7 +28,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdsa.so")
 
 DSA_F32, DSA_BF16 = 0, 1
-DSA_WS_SELECT, DSA_WS_BWD, DSA_WS_FWD, DSA_WS_PRED_GRAD = 0, 1, 2, 3
+DSA_WS_SELECT, DSA_WS_BWD, DSA_WS_FWD, DSA_WS_PRED_GRAD, DSA_WS_PRED_POOLED = 0, 1, 2, 3, 4
 
 
 class DsaError(RuntimeError):
@@ -81,6 +81,7 @@ def library() -> ctypes.CDLL:
         lib.dsa_select_coverage_blocks.argtypes = [pp, f32p, f32p, f32p, kph, ctypes.c_double, i32p, i32p, i32p,
                                                    i32p, f32p, vp, sz, vp]
         lib.dsa_sparse_attn_fwd_varlen.argtypes = [pp, vp, vp, vp, i32p, i32p, kph, f32p, f32p, vp, sz, vp]
+        lib.dsa_predict_block_scores_pooled.argtypes = [pp, vp, vp, f32p, f32p, ctypes.c_int, f32p, vp, sz, vp]
         lib.dsa_select_blocks.argtypes = [pp, f32p, f32p, f32p, kph, ctypes.c_double, ctypes.c_int, i32p, i32p, i32p,
                                           i32p, f32p, vp, sz, vp]
         lib.dsa_sparse_attn_bwd_varlen.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, i32p, kph, i32p, i32p,
@@ -90,7 +91,7 @@ def library() -> ctypes.CDLL:
                      "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_fwd_split",
                      "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd", "dsa_choose_path",
                      "dsa_predictor_loss_grad", "dsa_select_coverage_blocks", "dsa_sparse_attn_fwd_varlen",
-                     "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks"):
+                     "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks", "dsa_predict_block_scores_pooled"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -101,8 +102,9 @@ EXPORTED = ("dsa_version", "dsa_status_string", "dsa_index_layout", "dsa_workspa
             "dsa_sparse_attn_bwd_preprocess", "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq",
             "dsa_sparse_attn_fwd_split", "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd",
             "dsa_choose_path", "dsa_predictor_loss_grad", "dsa_select_coverage_blocks", "dsa_sparse_attn_fwd_varlen",
-            "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks")
+            "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks", "dsa_predict_block_scores_pooled")
 SELECT_DIAGONAL = 1  # DSA_SELECT_DIAGONAL
+POOL_MAX, POOL_LSE = 1, 2  # DSA_POOL_MAX, DSA_POOL_LSE
 MAX_SPLIT = 64  # DSA_MAX_SPLIT
 PATH_DENSE, PATH_SPARSE = 0, 1  # dsa_path
 DEFAULT_MIN_SPARSITY = 0.06     # DSA_DEFAULT_MIN_SPARSITY
@@ -200,6 +202,13 @@ def select_coverage_blocks(p: Problem, scores, qhat, khat, k_per_head, coverage:
         ctypes.byref(p.c()), _ptr(scores), _ptr(qhat), _ptr(khat), _kph(k_per_head), float(coverage), _ptr(idx),
         _ptr(cnt), _ptr(rev_ptr), _ptr(rev_idx), _ptr(scores_dump), _ptr(workspace), _nbytes(workspace),
         _stream(stream)))
+
+
+def predict_block_scores_pooled(p: Problem, Q, K, Wq, Wk, pooling: int, scores, workspace, stream=None) -> None:
+    """Block scores pooled from the token-level low-rank logits (POOL_MAX or POOL_LSE)."""
+    _check("dsa_predict_block_scores_pooled", library().dsa_predict_block_scores_pooled(
+        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), int(pooling), _ptr(scores), _ptr(workspace),
+        _nbytes(workspace), _stream(stream)))
 
 
 def select_blocks(p: Problem, scores, qhat, khat, k_per_head, coverage: float, flags: int, idx, cnt, rev_ptr,

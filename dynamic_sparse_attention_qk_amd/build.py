@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["api.hip", "predict.hip", "predict_train.hip", "select.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["api.hip", "predict.hip", "predict_train.hip", "predict_pooled.hip", "select.hip", "attn_fwd.hip",
+           "attn_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -113,6 +113,9 @@ dsa::PredWork pred_work(const Shape& s, void* ws) {
   return w;
 }
 
+// pooled scores: fp16 token projections of Q and K
+size_t pooled_ws(const Shape& s) { return 2 * align256((size_t)s.B * s.H * s.N * s.R * 2); }
+
 // forward: an fp16 copy of V (bf16 inputs only)
 size_t fwd_ws(const Shape& s) { return s.bf16 ? align256((size_t)s.B * s.H * s.N * s.D * 2) : 0; }
 
@@ -177,6 +180,7 @@ size_t dsa_workspace_bytes(const dsa_problem* p, const int32_t* k_per_head, int 
   if (!k_per_head && which_call == DSA_WS_FWD) return fwd_ws(s);
   if (!k_per_head && which_call == DSA_WS_BWD) return bwd_ws(s);
   if (which_call == DSA_WS_PRED_GRAD) return pred_ws(s);
+  if (which_call == DSA_WS_PRED_POOLED) return pooled_ws(s);
   if (check_heads(s, k_per_head, &ht, nullptr)) return 0;
   if (which_call == DSA_WS_SELECT) return select_ws(s, ht);
   if (which_call == DSA_WS_BWD) return bwd_ws(s);
@@ -232,6 +236,23 @@ static int select_impl(const dsa_problem* p, const float* scores, const float* q
                                          cnt, coverage, diag);
   if (e == hipSuccess) e = dsa::launch_reverse_index(s, idx, rev_ptr, rev_idx, counters, scratch, ht, kmax, hs);
   return hip_status(e);
+}
+
+int dsa_predict_block_scores_pooled(const dsa_problem* p, const void* Q, const void* K, const float* Wq,
+                                    const float* Wk, int pooling, float* scores, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  Shape s;
+  int st = check_problem(p, &s);
+  if (st) return st;
+  if (pooling != DSA_POOL_MAX && pooling != DSA_POOL_LSE) return DSA_ERR_INVALID_ARG;
+  if (!Q || !K || !Wq || !Wk || !scores) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(scores)) return DSA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < pooled_ws(s)) return DSA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return DSA_ERR_ALIGN;
+  _Float16* pq = static_cast<_Float16*>(workspace);
+  _Float16* pk = reinterpret_cast<_Float16*>(static_cast<char*>(workspace) + pooled_ws(s) / 2);
+  return hip_status(dsa::launch_pooled_scores(s, Q, K, Wq, Wk, pooling, scores, pq, pk,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int dsa_select_topk_blocks(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,

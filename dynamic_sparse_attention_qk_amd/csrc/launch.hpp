@@ -51,6 +51,10 @@ hipError_t launch_bwd_dkdv(const Shape& s, const BwdWork& w, const int32_t* rev_
 hipError_t launch_bwd_dq(const Shape& s, const BwdWork& w, const int32_t* idx, float* dQ, const HeadTable& ht,
                          hipStream_t st, const int32_t* cnt = nullptr);
 
+// Block scores pooled from token-level logits (pooling 1: max, 2: log-mean-exp); pq, pk: fp16 [B,H,N,r]
+hipError_t launch_pooled_scores(const Shape& s, const void* Q, const void* K, const float* Wq, const float* Wk,
+                                int pooling, float* scores, _Float16* pq, _Float16* pk, hipStream_t st);
+
 // Stage-1 predictor training workspace (fp32): qbar [B,H,NG,d], kbar [B,H,NB,d], qhat [B,H,NG,r],
 // khat [B,H,NB,r], E [B,H,NG,NB], Y [B,H,NG,r], Z [B,H,NB,r], lrow [B,H,NG], part [H,2,16,d,r].
 constexpr int kPredWgParts = 16;

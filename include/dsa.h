@@ -69,7 +69,13 @@ typedef struct {
 } dsa_problem;
 
 /* Which call a workspace is sized for. */
-typedef enum { DSA_WS_SELECT = 0, DSA_WS_BWD = 1, DSA_WS_FWD = 2, DSA_WS_PRED_GRAD = 3 } dsa_ws_call;
+typedef enum {
+  DSA_WS_SELECT = 0,
+  DSA_WS_BWD = 1,
+  DSA_WS_FWD = 2,
+  DSA_WS_PRED_GRAD = 3,
+  DSA_WS_PRED_POOLED = 4
+} dsa_ws_call;
 
 /* Library version string. */
 const char* dsa_version(void);
@@ -86,9 +92,9 @@ int dsa_index_layout(const dsa_problem* p, const int32_t* k_per_head, int64_t* r
 
 /*
  * Bytes of workspace the given call needs (0 if the arguments are invalid).
- * k_per_head may be NULL for DSA_WS_FWD, DSA_WS_BWD and DSA_WS_PRED_GRAD,
- * whose sizes do not depend on it (the dense calls and the predictor training
- * call take no kept counts).
+ * k_per_head may be NULL for DSA_WS_FWD, DSA_WS_BWD, DSA_WS_PRED_GRAD and
+ * DSA_WS_PRED_POOLED, whose sizes do not depend on it (the dense calls and
+ * the predictor calls take no kept counts).
  */
 size_t dsa_workspace_bytes(const dsa_problem* p, const int32_t* k_per_head, int which_call);
 
@@ -104,6 +110,28 @@ size_t dsa_workspace_bytes(const dsa_problem* p, const int32_t* k_per_head, int 
 int dsa_predict_block_scores(const dsa_problem* p, const void* Q, const void* K,
                              const float* Wq, const float* Wk, float* qhat, float* khat,
                              float* scores, void* stream);
+
+/* Poolings of dsa_predict_block_scores_pooled. */
+#define DSA_POOL_MAX 1
+#define DSA_POOL_LSE 2
+
+/*
+ * dsa_predict_block_scores_pooled -- a predictor variant (not from the pages,
+ * which pool with a proxy query, hi §2.B): every token is projected,
+ * l[i,m] = tau (Q_i.Wq[h]) . (K_m.Wk[h]), and each G x 64 tile of these
+ * logits is pooled into scores[b,h,g,j]:
+ *   DSA_POOL_MAX: max_{i in g, m in j} l[i,m];
+ *   DSA_POOL_LSE: ln( mean_{i in g, m in j} exp(l[i,m]) ), the predicted
+ *                 attention mass of the tile per key pair, in log form.
+ * The projections are rounded to fp16 (workspace) and the products run on
+ * fp16 MFMA with fp32 accumulation (|projections| must stay below 65504).
+ * scores: [B,H,NG,NB] fp32, then usable by every selection call.
+ * Workspace: dsa_workspace_bytes(p, NULL, DSA_WS_PRED_POOLED).  Other
+ * pooling values: DSA_ERR_INVALID_ARG.
+ */
+int dsa_predict_block_scores_pooled(const dsa_problem* p, const void* Q, const void* K, const float* Wq,
+                                    const float* Wk, int pooling, float* scores, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /*
  * dsa_select_topk_blocks -- critical KV block selection (hi §2.A critical KV

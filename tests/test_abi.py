@@ -302,3 +302,24 @@ def test_select_blocks_validation():
     assert call(p128, [1, 4], 0.0, dsa.SELECT_DIAGONAL) == -2   # G = 128 forces two blocks: k_h >= 2
     assert lib.dsa_select_blocks(ctypes.byref(p64.c()), FAKE, FAKE, FAKE, dsa._kph([4, 4]), 0.0, 0, FAKE, None, FAKE,
                                  FAKE, None, None, 0, None) == -6
+
+
+def test_pooled_scores_validation():
+    lib = dsa.library()
+    big = 1 << 40
+    p = _p()
+    pc = ctypes.byref(p.c())
+    call = lambda pooling, *a: lib.dsa_predict_block_scores_pooled(pc, *a[:4], pooling, a[4], a[5], big, None)
+    args = [FAKE] * 6
+    for bad_pool in (0, 3, -1):
+        assert call(bad_pool, *args) == -1
+    for i in range(5):
+        bad = list(args)
+        bad[i] = None
+        assert call(dsa.POOL_MAX, *bad) == -1, i
+        bad[i] = ctypes.c_void_p(0x100004)
+        assert call(dsa.POOL_LSE, *bad) == -4, i
+    need = dsa.workspace_bytes(p, None, dsa.DSA_WS_PRED_POOLED)
+    assert need == 2 * ((2 * 1024 * 16 * 2 + 255) // 256 * 256)       # fp16 projections of Q and K
+    assert lib.dsa_predict_block_scores_pooled(pc, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, need - 1, None) == -6
+    assert lib.dsa_predict_block_scores_pooled(pc, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None, big, None) == -6

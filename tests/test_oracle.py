@@ -563,6 +563,10 @@ def check_pooled_scores_brute(seed=56, n=256, d=8, r=4, group=128):
     z = np.zeros((d, r))
     for x in ("mean", "lse", "max"):
         np.testing.assert_allclose(O.predict_head_pooled(q, k, z, z, group, x), 0.0, atol=1e-15)
+        # the row-sampled evaluator equals the full one
+        full = O.predict_head_pooled(q, k, wq, wk, group, x)
+        for g, row in O.predict_head_pooled_groups(q, k, wq, wk, group, x, [0, ng - 1]).items():
+            np.testing.assert_allclose(row, full[g], rtol=1e-12, atol=1e-13)
 
 
 ALL_CHECKS = [

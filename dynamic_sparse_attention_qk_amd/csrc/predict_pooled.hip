@@ -28,14 +28,23 @@ __global__ __launch_bounds__(256) void token_project_kernel(const T* __restrict_
   const int h = blockIdx.y;
   const int64_t t0 = (int64_t)blockIdx.x * kProjTokens;
   const T* xb = X + (bh * N + t0) * D;
-  for (int e = threadIdx.x; e < kProjTokens * D; e += 256) {
+  // 16-byte loads: VE elements each
+  constexpr int VE = 16 / sizeof(T);
+  for (int e = threadIdx.x * VE; e < kProjTokens * D; e += 256 * VE) {
     const int t = e / D, c = e % D;
-    float v = 0.f;
-    if (t0 + t < N) {
-      if constexpr (sizeof(T) == 2) v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(xb)[e] << 16);
-      else v = reinterpret_cast<const float*>(xb)[e];
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (t0 + t < N) v = ldg16(xb + e);
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&v);
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sx[t][c + 2 * q] = __uint_as_float(w[q] << 16);
+        sx[t][c + 2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sx[t][c + q] = __uint_as_float(w[q]);
     }
-    sx[t][c] = v;
   }
   for (int e = threadIdx.x; e < D * R; e += 256) sw[e / R][e % R] = W[(size_t)h * D * R + e];
   __syncthreads();
@@ -52,11 +61,9 @@ __global__ __launch_bounds__(256) void token_project_kernel(const T* __restrict_
       a3 = __builtin_fmaf(x, sw[c][r0 + 3], a3);
     }
     if (t0 + t < N) {
-      _Float16* p = P + (bh * N + t0 + t) * R + r0;
-      p[0] = (_Float16)a0;
-      p[1] = (_Float16)a1;
-      p[2] = (_Float16)a2;
-      p[3] = (_Float16)a3;
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      *reinterpret_cast<h4*>(P + (bh * N + t0 + t) * R + r0) = h4{(_Float16)a0, (_Float16)a1, (_Float16)a2,
+                                                                  (_Float16)a3};
     }
   }
 }

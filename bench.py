@@ -46,6 +46,8 @@ def parse():
                          "k as each row's cap) and per-row counts")
     ap.add_argument("--pooled", choices=["max", "lse"], default=None,
                     help="also time the predictor variant that pools token-level logits (and the step with it)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--predictor-grad", action="store_true",
                     help="also time the stage-1 predictor loss + gradient call on the same inputs")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -490,6 +492,35 @@ def main():
         rec["split_kv"] = time_split_kv(args, p, plan, Q, K, V, stream, stage_ms["fwd"], f_fwd, w)
     if args.coverage:
         rec["coverage_select"] = time_coverage(args, p, kph, Q, K, V, Wt, dO, stream, w)
+    if args.graph:
+        # the same step captured once (after a warm-up on a side stream) and replayed: launch overhead removed
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            with torch.cuda.stream(side):
+                plan.predict(Q, K, Wt, Wt)
+                plan.select()
+                plan.forward(Q, K, V)
+                if backward:
+                    plan.backward(Q, K, V, dO)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / args.steps
+        rec["graph"] = {"ms_per_step": round(gms, 4), "tflops": round((f_fwd + f_bwd) / (gms / 1e3) / 1e12, 3),
+                        "tokens_per_s": round(w.batch * w.seq_len / (gms / 1e3), 1)}
     if args.pooled:
         rec["pooled_predictor"] = time_pooled(args, p, kph, Q, K, Wt, stream, w)
     if args.predictor_grad:

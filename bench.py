@@ -105,8 +105,9 @@ def cpu_baseline(inp, target_s: float):
             "tokens_per_s": groups_done * G / elapsed}
 
 
+# the device code of the attention kernels (launch.hpp holds host declarations only)
 KERNEL_SOURCES = ("dynamic_sparse_attention_qk_amd/csrc/attn_fwd.hip", "dynamic_sparse_attention_qk_amd/csrc/attn_bwd.hip",
-                  "dynamic_sparse_attention_qk_amd/csrc/common.hpp", "dynamic_sparse_attention_qk_amd/csrc/launch.hpp")
+                  "dynamic_sparse_attention_qk_amd/csrc/common.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernels_bf16_57k_tokens_traffic.md")
 
 

@@ -17,13 +17,15 @@ from .dsv_oracle import (
     predict_head, predictor_loss_grad, predictor_loss_grad_head, predictor_loss_head, reverse_index, reverse_list,
     select, select_row, sparsity, split_bounds, use_sparse, block_mass, select_coverage_row, select_coverage,
     diagonal_blocks, select_order, select_row_diag, select_coverage_row_diag, predict_head_pooled,
+    predict_head_pooled_groups, predict_head_pooled_rows,
 )
 
 __all__ = [
     "dsv_oracle", "BLOCK", "backward", "backward_head", "dense_backward", "dense_backward_head",
     "dense_dkdv_blocks", "dense_dq_rows", "dense_forward", "dense_forward_head", "dense_rows", "sparsity",
     "use_sparse", "block_mass", "select_coverage_row", "select_coverage", "diagonal_blocks", "select_order",
-    "select_row_diag", "select_coverage_row_diag", "predict_head_pooled", "predictor_loss_head", "predictor_loss_grad_head", "predictor_loss_grad", "dkdv_blocks",
+    "select_row_diag", "select_coverage_row_diag", "predict_head_pooled",
+    "predict_head_pooled_groups", "predict_head_pooled_rows", "predictor_loss_head", "predictor_loss_grad_head", "predictor_loss_grad", "dkdv_blocks",
     "dq_groups", "forward",
     "forward_head", "forward_split_head", "group_backward", "group_forward", "kept_keys", "merge_states",
     "partial_state", "pool_mean", "predict", "predict_head", "reverse_index", "reverse_list", "select",

@@ -118,6 +118,30 @@ def predict_head_pooled(q: np.ndarray, k: np.ndarray, wq: np.ndarray, wk: np.nda
     raise ValueError(pooling)
 
 
+def predict_head_pooled_groups(q, k, wq, wk, group, pooling, groups, block=BLOCK) -> Dict[int, np.ndarray]:
+    """Rows of predict_head_pooled for the listed groups only (the same arithmetic on their query rows)."""
+    out = {}
+    for g in groups:
+        rows = slice(g * group, (g + 1) * group)
+        # the group's rows against every key: one [1, NB] row of the pooled scores
+        out[g] = predict_head_pooled_rows(q[rows], k, wq, wk, pooling, block)
+    return out
+
+
+def predict_head_pooled_rows(qg, k, wq, wk, pooling, block=BLOCK) -> np.ndarray:
+    tau = 1.0 / np.sqrt(qg.shape[1])
+    lg = tau * ((qg @ wq) @ (k @ wk).T)                                # G x N predicted logits
+    t = lg.reshape(qg.shape[0], k.shape[0] // block, block)             # [i, j, m]
+    if pooling == "mean":
+        return t.mean(axis=(0, 2))
+    if pooling == "max":
+        return t.max(axis=(0, 2))
+    if pooling == "lse":
+        m = t.max(axis=(0, 2), keepdims=True)
+        return (m + np.log(np.exp(t - m).mean(axis=(0, 2), keepdims=True)))[0, :, 0]
+    raise ValueError(pooling)
+
+
 # ----------------------------------------------------------------------------
 # Step 4: top-k critical block selection
 # ----------------------------------------------------------------------------

@@ -146,21 +146,24 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
     id_n = id_pf;
     id_pf = block_id(t + 3);
     // S^T and dP^T: rows = this half's 32 keys, columns = the wave's 32 queries
+    // S first, then dP with the exponentials of S beside its MFMAs
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      s = mfma32h(*reinterpret_cast<const f16x8*>(cur + kofs[c]), qreg[c], s);
-      dp = mfma32h(*reinterpret_cast<const f16x8*>(cur + TILE + kofs[c]), oreg[c], dp);
-    }
-    // operand reads two MFMA pairs ahead of their use
+    for (int c = 0; c < D / 16; ++c) s = mfma32h(*reinterpret_cast<const f16x8*>(cur + kofs[c]), qreg[c], s);
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < D / 16 - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    // K^T operands of dQ^T, read before the exponentials so that those hide the LDS latency
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    float pe[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pe[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, nl2));
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) dp = mfma32h(*reinterpret_cast<const f16x8*>(cur + TILE + kofs[c]), oreg[c], dp);
+    // K^T operands of dQ^T, read under the dP MFMAs
     f16x8 kt[D / 32][2];
 #pragma unroll
     for (int c = 0; c < D / 32; ++c) {
@@ -169,12 +172,17 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
       kt[c][0] = join_f16(lds_read_tr16(t0), lds_read_tr16(t1));
       kt[c][1] = join_f16(lds_read_tr16(t0 + 16 * RB), lds_read_tr16(t1 + 16 * RB));
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
+#pragma unroll
+    for (int i = 0; i < D / 16 - 2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], scale_log2, nl2));
-      dp[e] = p * (dp[e] - dvec);
-    }
+    for (int e = 0; e < 16; ++e) dp[e] = pe[e] * (dp[e] - dvec);
     const f16x8 d0 = pack_f16(dp, 0), d1 = pack_f16(dp, 1);
     // dQ^T[c][i] += K^T[c][m] dS^T[m][i]
 #pragma unroll

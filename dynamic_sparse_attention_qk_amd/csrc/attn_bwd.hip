@@ -15,9 +15,9 @@
 // bwd_dq: one workgroup per (b, h, group) over the group's kept blocks; waves
 // = 32-row tile x key half, partial dQ of the two halves summed at the end.
 // bwd_dkdv: one workgroup per (b, h, KV block) over the block's reverse list;
-// each wave owns 16 keys and every query row, dK/dV in registers.  dK's dS
-// operand is split hi + lo in fp16 (dK sums a cancelling dS against clustered
-// Q rows).
+// each wave owns 32 keys and half of every 64-row query tile, dK/dV in
+// registers.  dK's dS operand is split hi + lo in fp16 (dK sums a cancelling
+// dS against clustered Q rows).
 #include "launch.hpp"
 
 namespace dsa {
@@ -225,31 +225,6 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------- dK, dV
-//
-// Wave w owns keys 16w..16w+15 of the block and all 64 query rows of each
-// tile, on 16x16x32 MFMAs: its dK and dV accumulators are 16 x D each (2*D/16
-// registers per lane), small enough for two waves per SIMD.
-
-__device__ __forceinline__ f16x8 join4_f16(const f32x4& a, const f32x4& b) {
-  f16x8 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[e] = (_Float16)a[e];
-    r[4 + e] = (_Float16)b[e];
-  }
-  return r;
-}
-
-__device__ __forceinline__ void join4_f16_split(const f32x4& a, const f32x4& b, f16x8& hi, f16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const _Float16 ha = (_Float16)a[e], hb = (_Float16)b[e];
-    hi[e] = ha;
-    hi[4 + e] = hb;
-    lo[e] = (_Float16)(a[e] - (float)ha);
-    lo[4 + e] = (_Float16)(b[e] - (float)hb);
-  }
-}
 
 // Order of the dK/dV tasks within each XCD segment (a contiguous range, or an
 // XCD's part of one (b, h) run): the blocks whose reverse list is longer than
@@ -311,6 +286,13 @@ __global__ __launch_bounds__(256) void dkdv_order_kernel(const int32_t* __restri
 }
 
 // kLists false: dense attention (no reverse lists or order; every block has all NG groups).
+//
+// Wave w = (kh, qh) owns keys 32*kh..32*kh+31 of the block and query rows
+// 32*qh..32*qh+31 of every 64-row tile, on 16x16x32 MFMAs over two 16-key
+// halves: each operand read from LDS feeds both halves (half the LDS bytes per
+// MFMA of a wave with 16 keys), and the two query halves' dK, dV partials are
+// summed once at the end.  S starts from -LSE/tau and dP from -D, so
+// P = exp2(S tau log2 e) and dS = P dP need no per-row values afterwards.
 template <int D, int G, bool kLists>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q16,
                                                           const uint16_t* __restrict__ K16,
@@ -328,11 +310,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
   constexpr int TILE = 64 * RB;
   constexpr int STAGE = 2 * TILE + 512;  // Q16 tile, dO16 tile, -LSE*log2e row, D row
   constexpr int SUB = G / 64;            // 64-row query tiles per group
-  constexpr int NS = D / 32;             // 32-wide steps of the head dimension
+  constexpr int NT = D / 32;             // 32-wide steps of the head dimension (S, dP)
   constexpr int NC = D / 16;             // 16-wide column tiles of dK, dV
+  constexpr int XBUF = 2 * NC * 4 * 64 * 4;  // one wave's partial of one tensor
+  static_assert(2 * XBUF <= STAGE, "the partials of one key half must fit in one stage");
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
   const float scale_log2 = tau * kLog2e;
+  const float inv_scale = 1.0f / scale_log2;
 
   const int64_t slot = xcd_task(sp, blockIdx.x);
   if (slot < 0) return;
@@ -344,6 +329,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
   const size_t bh = (size_t)b * H + h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, q4 = lane >> 4;
+  const int kh = wave & 1, qh = wave >> 1;
   const int32_t total = NG * ht.k[h];  // size of the (b, h) region of the reverse list
   int32_t s0 = 0, s1 = NG;
   const int32_t* rlist = nullptr;
@@ -355,37 +341,42 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
   }
   const int iters = (s1 - s0) * SUB;
 
-  // this wave's 16 keys as B operands: K for S = Q K^T, V for dP = dO V^T
-  f16x8 kreg[NS], vreg[NS];
-  {
-    const size_t key = bh * N + (size_t)j * kBlock + 16 * wave + l16;
+  // this wave's keys as B operands (half kk: keys 32*kh + 16*kk + l16): K for
+  // S = Q K^T, V for dP = dO V^T
+  f16x8 kreg[2][NT], vreg[2][NT];
 #pragma unroll
-    for (int t = 0; t < NS; ++t) {
-      kreg[t] = ldg_f16x8(K16 + key * D + 32 * t + 8 * q4);
-      vreg[t] = ldg_f16x8(V16 + key * D + 32 * t + 8 * q4);
+  for (int kk = 0; kk < 2; ++kk) {
+    const size_t key = bh * N + (size_t)j * kBlock + 32 * kh + 16 * kk + l16;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      kreg[kk][t] = ldg_f16x8(K16 + key * D + 32 * t + 8 * q4);
+      vreg[kk][t] = ldg_f16x8(V16 + key * D + 32 * t + 8 * q4);
     }
   }
-  // A operands: query row 16*rb + l16, logical chunk 4*t + q4 (same swizzle for every rb)
-  int aofs[NS];
-#pragma unroll
-  for (int t = 0; t < NS; ++t) aofs[t] = tile_off<D>(l16, 4 * t + q4);
-  // transpose reads (B operands of dV, dK): rows 32*kc + 4*q4 + l16/4 (+16), columns 16*c + 4*(l16%4)
-  int tofs[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) tofs[c] = tile_off<D>(4 * q4 + (l16 >> 2), 2 * c + ((l16 & 3) >> 1)) + 8 * (l16 & 1);
+  // A operands of S and dP: query row 32*qh + 16*qq + l16, logical chunk 4t + q4,
+  // at byte offset (abase ^ 64t) + 16*qq*RB (the swizzle permutes chunks within
+  // a row and repeats every 16 rows)
+  const int abase = tile_off<D>(32 * qh + l16, q4);
+  // transpose reads (B operands of dV, dK): lane i of 16-lane group q4 reads row
+  // 32*qh + 4*q4 + i/4 (+16), columns 16c + 4*(i%4), at (tbase ^ 32c)
+  const int tbase = tile_off<D>(32 * qh + 4 * q4 + (l16 >> 2), (l16 & 3) >> 1) + 8 * (l16 & 1);
 
-  f32x4 dk[NC], dv[NC];
+  f32x4 dk[2][NC], dv[2][NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) { dk[c] = f32x4{}; dv[c] = f32x4{}; }
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) { dk[kk][c] = f32x4{}; dv[kk][c] = f32x4{}; }
 
-  // group of query tile min(it, iters-1) (needs iters > 0); clamped: never out of bounds
+  // group of query tile min(it, iters-1) (needs iters > 0), read ahead as a
+  // vector load; clamped when used: never out of bounds
   auto group_of = [&](int it) {
-    if constexpr (kLists) return min(max(rlist[min(it, iters - 1) / SUB], 0), NG - 1);
+    if constexpr (kLists) return ldv_i32(rlist + min(it, iters - 1) / SUB);
     else return min(it, iters - 1) / SUB;
   };
   // groups read ahead: at step it, g_n = group of tile it+1 and g_pf = group of tile it+2 are in registers
   int g_n = 0, g_pf = 0;
-  auto fetch = [&](int it, int g, char* dst) {
+  auto fetch = [&](int it, int graw, char* dst) {
+    const int g = min(max(__builtin_amdgcn_readfirstlane(graw), 0), NG - 1);
     const size_t row0 = bh * N + (size_t)g * G + (size_t)(it % SUB) * 64;
     dma_tile<D, NW>(Q16 + row0 * D, dst, wave, lane);
     dma_tile<D, NW>(dO16 + row0 * D, dst + TILE, wave, lane);
@@ -398,65 +389,85 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
     if (it + 1 < iters) fetch(it + 1, g_n, nxt);
     g_n = g_pf;
     g_pf = group_of(it + 3);
-    // S[i][m], dP[i][m] for the 64 queries (4 row blocks) x this wave's 16 keys;
-    // element e of row block rb: query 16*rb + 4*q4 + e
-    f32x4 s[4], dp[4];
+    // offsets recomputed per step (kept out of registers across the loop)
+    int ab = abase, tb = tbase;
+    asm volatile("" : "+v"(ab), "+v"(tb));
+    // S[kk][qq], dP[kk][qq]: element e of lane l is query 32*qh + 16*qq + 4*q4 + e,
+    // key 32*kh + 16*kk + l16
+    const float* nrow = reinterpret_cast<const float*>(cur + 2 * TILE) + 32 * qh + 4 * q4;
+    const float* drow = reinterpret_cast<const float*>(cur + 2 * TILE + 256) + 32 * qh + 4 * q4;
+    f32x4 s[2][2], dp[2][2];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      s[rb] = f32x4{};
-      dp[rb] = f32x4{};
-#pragma unroll
-      for (int t = 0; t < NS; ++t) {
-        s[rb] = mfma16h(*reinterpret_cast<const f16x8*>(cur + 16 * rb * RB + aofs[t]), kreg[t], s[rb]);
-        dp[rb] = mfma16h(*reinterpret_cast<const f16x8*>(cur + TILE + 16 * rb * RB + aofs[t]), vreg[t], dp[rb]);
-      }
-    }
-    const float* nrow = reinterpret_cast<const float*>(cur + 2 * TILE) + 4 * q4;
-    const float* drow = reinterpret_cast<const float*>(cur + 2 * TILE + 256) + 4 * q4;
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const f32x4 n4 = *reinterpret_cast<const f32x4*>(nrow + 16 * rb);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(drow + 16 * rb);
+    for (int qq = 0; qq < 2; ++qq) {
+      const f32x4 n4 = *reinterpret_cast<const f32x4*>(nrow + 16 * qq);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(drow + 16 * qq);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][e], scale_log2, n4[e]));
-        s[rb][e] = p;
-        dp[rb][e] = p * (dp[rb][e] - d4[e]);
+        s[0][qq][e] = s[1][qq][e] = n4[e] * inv_scale;
+        dp[0][qq][e] = dp[1][qq][e] = -d4[e];
       }
     }
-    // S/dP phase: operand reads two MFMA pairs ahead of their use
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * 4 * NS / 2 - 2; ++i) {
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(cur + 16 * qq * RB + (ab ^ (64 * t)));
+        s[0][qq] = mfma16h(a, kreg[0][t], s[0][qq]);
+        s[1][qq] = mfma16h(a, kreg[1][t], s[1][qq]);
+      }
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const f16x8 a = *reinterpret_cast<const f16x8*>(cur + TILE + 16 * qq * RB + (ab ^ (64 * t)));
+        dp[0][qq] = mfma16h(a, vreg[0][t], dp[0][qq]);
+        dp[1][qq] = mfma16h(a, vreg[1][t], dp[1][qq]);
+      }
+    // S/dP phase: the row statistics, then each operand read one MFMA pair ahead
+    constexpr int NA = 4 * NT;  // A-operand reads of the phase
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < NA - 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // A operands over 32-query chunks kc: element e' <-> query 32*kc + 16*(e'/4) + 4*q4 + e'%4
-    const f16x8 pa0 = join4_f16(s[0], s[1]), pa1 = join4_f16(s[2], s[3]);
-    f16x8 dh0, dl0, dh1, dl1;
-    join4_f16_split(dp[0], dp[1], dh0, dl0);
-    join4_f16_split(dp[2], dp[3], dh1, dl1);
+    // P = exp2(S tau log2 e), dS = P (dP - D); A operands per key half kk:
+    // element e' <-> query 32*qh + 16*(e'/4) + 4*q4 + e'%4
+    f16x8 pa[2], dh[2], dl[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(s[kk][qq][e] * scale_log2);
+          const float ds = p * dp[kk][qq][e];
+          const _Float16 hv = (_Float16)ds;
+          pa[kk][4 * qq + e] = (_Float16)p;
+          dh[kk][4 * qq + e] = hv;
+          dl[kk][4 * qq + e] = (_Float16)(ds - (float)hv);
+        }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const char* o = cur + TILE + tofs[c];
-      dv[c] = mfma16h(pa0, join_f16(lds_read_tr16(o), lds_read_tr16(o + 16 * RB)), dv[c]);
-      dv[c] = mfma16h(pa1, join_f16(lds_read_tr16(o + 32 * RB), lds_read_tr16(o + 48 * RB)), dv[c]);
-      const char* q = cur + tofs[c];
-      const f16x8 qb0 = join_f16(lds_read_tr16(q), lds_read_tr16(q + 16 * RB));
-      const f16x8 qb1 = join_f16(lds_read_tr16(q + 32 * RB), lds_read_tr16(q + 48 * RB));
-      dk[c] = mfma16h(dh0, qb0, dk[c]);
-      dk[c] = mfma16h(dl0, qb0, dk[c]);
-      dk[c] = mfma16h(dh1, qb1, dk[c]);
-      dk[c] = mfma16h(dl1, qb1, dk[c]);
+      const char* o = cur + TILE + (tb ^ (32 * c));
+      const f16x8 ob = join_f16(lds_read_tr16(o), lds_read_tr16(o + 16 * RB));
+      const char* q = cur + (tb ^ (32 * c));
+      const f16x8 qb = join_f16(lds_read_tr16(q), lds_read_tr16(q + 16 * RB));
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        dv[kk][c] = mfma16h(pa[kk], ob, dv[kk][c]);
+        dk[kk][c] = mfma16h(dh[kk], qb, dk[kk][c]);
+        dk[kk][c] = mfma16h(dl[kk], qb, dk[kk][c]);
+      }
     }
     // dV/dK phase: the transpose reads of column tile c+1 are issued before the MFMAs of tile c
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
     for (int c = 0; c < NC - 1; ++c) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
       __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);
   };
@@ -471,15 +482,32 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
     if (it + 1 < iters) step(it + 1, st1, st0);
   }
 
-  // accumulator element e of column tile c: key 16*wave + 4*q4 + e, column 16*c + l16
-  const size_t key0 = bh * N + (size_t)j * kBlock + 16 * wave + 4 * q4;
+  // sum the two query halves: the qh = 1 wave parks its dK partial, the qh = 0
+  // wave its dV partial, in the stage of their key half; each then stores one
+  __syncthreads();
+  float* xb = reinterpret_cast<float*>(kh ? st1 : st0);
+  float* park = xb + (qh ? 0 : XBUF / 4);
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
+  for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      dK[(key0 + e) * D + 16 * c + l16] = dk[c][e] * tau;
-      dV[(key0 + e) * D + 16 * c + l16] = dv[c][e];
-    }
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) park[((kk * NC + c) * 4 + e) * 64 + lane] = qh ? dk[kk][c][e] : dv[kk][c][e];
+  __syncthreads();
+  const float* other = xb + (qh ? XBUF / 4 : 0);
+  float* out = qh ? dV : dK;
+  const float mul = qh ? 1.0f : tau;
+  // accumulator element e of column tile c, half kk: key 32*kh + 16*kk + 4*q4 + e, column 16c + l16
+  const size_t key0 = bh * N + (size_t)j * kBlock + 32 * kh + 4 * q4;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float own = qh ? dv[kk][c][e] : dk[kk][c][e];
+        out[(key0 + 16 * kk + e) * D + 16 * c + l16] = (own + other[((kk * NC + c) * 4 + e) * 64 + lane]) * mul;
+      }
 }
 
 template <int D>

@@ -293,9 +293,23 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, char*
   for (int i = 0; i < D / 8 / NW; ++i) {
     const int j = wave + i * NW;
     const int r = j * RPI + rin;
-    const uint16_t* g = src + (size_t)r * D + 8 * (p ^ tile_swz<D>(r));
+    // uniform base + 32-bit per-lane byte offset (the scalar-base addressing form)
+    uint32_t off = (uint32_t)(2 * (r * D + 8 * (p ^ tile_swz<D>(r))));
+    asm volatile("" : "+v"(off));  // keeps the offset 32-bit at the load (not widened once outside a loop)
+    const void* g = reinterpret_cast<const char*>(src) + off;
     __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds_base + j * 1024), 16, 0, 0);
   }
+}
+
+// A list entry read through the vector memory path (a per-lane address the
+// compiler cannot prove uniform), for reads issued steps ahead of their use:
+// a scalar load in flight would force every LDS operand wait of the step to
+// drain the whole LDS/scalar counter, while a vector load is counted with the
+// tile copies, which each step drains anyway.  Take readfirstlane at the use.
+__device__ __forceinline__ int32_t ldv_i32(const int32_t* __restrict__ p) {
+  int32_t z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return p[z];
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -314,7 +328,10 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0
 
 // 4-byte-per-lane DMA of 64 consecutive floats (one wave) into LDS.
 __device__ __forceinline__ void dma_row64_f32(const float* __restrict__ src, char* lds, int lane) {
-  __builtin_amdgcn_global_load_lds(src + lane, (lds_void*)lds, 4, 0, 0);
+  // 4 * lane, recomputed at each use (a loop-invariant copy would hold a register)
+  uint32_t off;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0\n\tv_lshlrev_b32 %0, 2, %0" : "=v"(off));
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(src) + off, (lds_void*)lds, 4, 0, 0);
 }
 
 // Transpose read (ds_read_b64_tr_b16): within each 16-lane group, lane i

@@ -423,16 +423,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
         dp[0][qq] = mfma16h(a, vreg[0][t], dp[0][qq]);
         dp[1][qq] = mfma16h(a, vreg[1][t], dp[1][qq]);
       }
-    // S/dP phase: the row statistics, then each operand read one MFMA pair ahead
-    constexpr int NA = 4 * NT;  // A-operand reads of the phase
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-    for (int i = 0; i < NA - 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-    __builtin_amdgcn_sched_barrier(0);
     // P = exp2(S tau log2 e), dS = P (dP - D); A operands per key half kk:
     // element e' <-> query 32*qh + 16*(e'/4) + 4*q4 + e'%4
     f16x8 pa[2], dh[2], dl[2];
@@ -462,14 +452,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
         dk[kk][c] = mfma16h(dl[kk], qb, dk[kk][c]);
       }
     }
-    // dV/dK phase: the transpose reads of column tile c+1 are issued before the MFMAs of tile c
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-#pragma unroll
-    for (int c = 0; c < NC - 1; ++c) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 6, 1);
+    // (no scheduling groups: at this register load the compiler's own order is faster, 9.33 vs 9.71 ms)
   };
 
   if (iters > 0) {

@@ -94,14 +94,6 @@ __device__ __forceinline__ f32x16 mfma32_f32(float a, float b, const f32x16& c) 
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// Pack accumulator elements [8c, 8c+8) of a 32x32 tile to bf16: for lane l
-// they hold the 16-key chunk c of the tile at keys 16c + 8*(e/4) + 4*(l/32) + e%4.
-__device__ __forceinline__ bf16x8 pack_bf16(const f32x16& x, int c) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[8 * c + e];
-  return r;
-}
 
 __device__ __forceinline__ f16x8 pack_f16(const f32x16& x, int c) {
   f16x8 r;
@@ -110,16 +102,6 @@ __device__ __forceinline__ f16x8 pack_f16(const f32x16& x, int c) {
   return r;
 }
 
-// hi + lo fp16 split of accumulator elements [8c, 8c+8): hi = fp16(x),
-// lo = fp16(x - hi); hi + lo carries ~22 significant bits of x.
-__device__ __forceinline__ void pack_f16_split(const f32x16& x, int c, f16x8& hi, f16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const _Float16 h = (_Float16)x[8 * c + e];
-    hi[e] = h;
-    lo[e] = (_Float16)(x[8 * c + e] - (float)h);
-  }
-}
 
 // Exact conversion of 8 bf16 values (one 16-byte register) to fp16: every
 // bf16 value of magnitude in [2^-14, 65504] is representable in fp16.
@@ -135,115 +117,12 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& v) {
   return r;
 }
 
-// Two 8-byte LDS reads forming the A operand that matches pack_bf16's key
-// order: row pointer `p` already points at (row, 16c + 4*(l/32)).
-__device__ __forceinline__ bf16x8 lds_pair_b64(const bf16_t* p) {
-  bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 8);
-  bf16x8 r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-  return r;
-}
 
-__device__ __forceinline__ f16x8 lds_pair_b64_h(const uint16_t* p) {
-  f16x4 lo = *reinterpret_cast<const f16x4*>(p);
-  f16x4 hi = *reinterpret_cast<const f16x4*>(p + 8);
-  f16x8 r;
-  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
-  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
-  return r;
-}
 
 // 16-byte global load / store helpers.
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Transposed store of an 8x8 16-bit sub-tile held as 8 rows x 16 bytes:
-// writes column c (8 values from rows 0..7) as 16 contiguous bytes at dst[c*ld]
-// (two 8-byte stores: transposed tiles use a row stride of 2 mod 4 dwords).
-__device__ __forceinline__ void store_transposed_8x8(const uint4 (&rows)[8], uint16_t* dst, int ld) {
-  const uint32_t* w[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) w[r] = reinterpret_cast<const uint32_t*>(&rows[r]);
-#pragma unroll
-  for (int c2 = 0; c2 < 4; ++c2) {
-    uint32_t pe[4], po[4];  // columns 2*c2 and 2*c2+1
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t a = w[2 * p][c2], b = w[2 * p + 1][c2];
-      pe[p] = (a & 0xFFFFu) | (b << 16);
-      po[p] = (a >> 16) | (b & 0xFFFF0000u);
-    }
-    uint2* de = reinterpret_cast<uint2*>(dst + (2 * c2) * ld);
-    uint2* dd = reinterpret_cast<uint2*>(dst + (2 * c2 + 1) * ld);
-    de[0] = make_uint2(pe[0], pe[1]);
-    de[1] = make_uint2(pe[2], pe[3]);
-    dd[0] = make_uint2(po[0], po[1]);
-    dd[1] = make_uint2(po[2], po[3]);
-  }
-}
 
-// Row stride (16-bit elements) of row-major LDS tiles of width D: 16 bytes of
-// padding keep the 8 rows read by one 128-bit pass on distinct banks.
-template <int D>
-constexpr int kRowLd = D + 8;
-// Row stride of transposed tiles (64 columns): 34 dwords, so 16 lanes reading
-// 8 bytes from 16 consecutive rows hit 16 distinct bank pairs.
-constexpr int kColLd = 64 + 4;
-
-// Cooperative movement of a 64 x D bf16 tile (rows of D contiguous values)
-// through registers into LDS, as 8 x 8 sub-blocks.  Sub-block sb of a thread
-// is (row block rb, column chunk cb) with rb = sb % 8 and cb = (sb / 8 + rb)
-// mod D/8: the 8 lanes of one LDS pass take a diagonal, which keeps both the
-// row-major and the transposed stores free of bank conflicts.
-template <int D, int NT>
-struct TileMover {
-  static constexpr int NC = D / 8;
-  static constexpr int NSB = 8 * NC;
-  static constexpr int SBT = (NSB + NT - 1) / NT;
-  uint4 r[SBT][8];
-
-  __device__ __forceinline__ static int rb_of(int sb) { return sb % 8; }
-  __device__ __forceinline__ static int cb_of(int sb) { return (sb / 8 + sb % 8) % NC; }
-
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ src) {  // src: first row of the tile
-#pragma unroll
-    for (int s = 0; s < SBT; ++s) {
-      const int sb = threadIdx.x + s * NT;
-      if (NSB % NT == 0 || sb < NSB) {
-        const int rb = rb_of(sb), cb = cb_of(sb);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) r[s][i] = ldg16(src + (size_t)(8 * rb + i) * D + 8 * cb);
-      }
-    }
-  }
-  __device__ __forceinline__ void store_rows(uint16_t* dst) const {  // dst[m * kRowLd + c]
-#pragma unroll
-    for (int s = 0; s < SBT; ++s) {
-      const int sb = threadIdx.x + s * NT;
-      if (NSB % NT == 0 || sb < NSB) {
-        const int rb = rb_of(sb), cb = cb_of(sb);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<uint4*>(dst + (8 * rb + i) * kRowLd<D> + 8 * cb) = r[s][i];
-      }
-    }
-  }
-  // dst[c * kColLd + m] as fp16 (exact conversion of the bf16 values)
-  __device__ __forceinline__ void store_cols_f16(uint16_t* dst) const {
-#pragma unroll
-    for (int s = 0; s < SBT; ++s) {
-      const int sb = threadIdx.x + s * NT;
-      if (NSB % NT == 0 || sb < NSB) {
-        const int rb = rb_of(sb), cb = cb_of(sb);
-        uint4 h[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) h[i] = bf16x8_to_f16x8(r[s][i]);
-        store_transposed_8x8(h, dst + (8 * cb) * kColLd + 8 * rb, kColLd);
-      }
-    }
-  }
-};
 
 // ---------------------------------------------------------------- LDS tiles filled by DMA
 // A 64 x D 16-bit tile is stored row-major without padding (row = 2*D bytes)
@@ -314,17 +193,7 @@ __device__ __forceinline__ int32_t ldv_i32(const int32_t* __restrict__ p) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmem_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-// Workgroup barrier for loops whose LDS tiles arrive by DMA: the caller has
-// already waited (vmcnt) for exactly the copies that must be visible; this
-// completes the wave's own LDS reads/writes (lgkmcnt) and synchronises, without
-// the release fence of __syncthreads(), which would also wait for copies
-// still in flight to other stages.  The memory clobber keeps the compiler from
-// moving memory accesses across it.
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // 4-byte-per-lane DMA of 64 consecutive floats (one wave) into LDS.
 __device__ __forceinline__ void dma_row64_f32(const float* __restrict__ src, char* lds, int lane) {
@@ -348,37 +217,7 @@ __device__ __forceinline__ f16x8 join_f16(i16x4 a, i16x4 b) {
   return __builtin_bit_cast(f16x8, v);
 }
 
-// A 64 x D bf16 tile staged through registers and written to a swizzled LDS
-// tile as fp16 (exact conversion); chunk c of the tile (row c / (D/8), logical
-// chunk c % (D/8)) belongs to thread c % NT.  Consecutive lanes take
-// consecutive chunks of a row: coalesced loads and conflict-free stores.
-template <int D, int NT>
-struct F16Stager {
-  static constexpr int NCH = 64 * D / 8;
-  static constexpr int PER = (NCH + NT - 1) / NT;
-  uint4 r[PER];
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ src) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + i * NT;
-      if (NCH % NT == 0 || c < NCH) r[i] = ldg16(src + (size_t)(c / (D / 8)) * D + 8 * (c % (D / 8)));
-    }
-  }
-  __device__ __forceinline__ void store(char* tile) const {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + i * NT;
-      if (NCH % NT == 0 || c < NCH)
-        *reinterpret_cast<uint4*>(tile + tile_off<D>(c / (D / 8), c % (D / 8))) = bf16x8_to_f16x8(r[i]);
-    }
-  }
-};
 
-__device__ __forceinline__ bf16x8 join_bf16(i16x4 a, i16x4 b) {
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
 
 // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
 // L2).  Map the hardware id w (of n) to a logical index such that every XCD

@@ -23,20 +23,22 @@ namespace {
 // Split-KV (partial states over parts of each row's kept list, merged by
 // log-sum-exp; DiTango explainer, nl edition, Methodologie: attention states
 // compose associatively and commutatively; DSV hi §2.C sparse sequence-wise
-// CP): task L of a forward launch with n_split parts is part L % n_split of
-// query group L / n_split (ordered b, h, g); the part covers list positions
-// [part k_h / n_split, (part + 1) k_h / n_split).  n_split = 1 is the plain
-// forward.
+// CP): tasks are ordered (part, b, h, g), so a launch works through every
+// group's first part before any second part and, since lists are ascending,
+// streams roughly one n_split-th of each head's K and V at a time; the part
+// covers list positions [part k_h / n_split, (part + 1) k_h / n_split).
+// n_split = 1 is the plain forward.
 struct FwdTask {
   int g, h, b, part, kbeg, klen;
 };
 
 // cnt (if not null): blocks kept by each (b, h, g) row, clamped to [1, k_h] (k_h: the row's list capacity)
-__device__ __forceinline__ FwdTask fwd_task(uint32_t L, int NG, int H, int n_split, const HeadTable& ht,
+__device__ __forceinline__ FwdTask fwd_task(uint32_t L, int NG, int H, int B, int n_split, const HeadTable& ht,
                                             const int32_t* __restrict__ cnt) {
   FwdTask t;
-  t.part = (int)(L % (uint32_t)n_split);
-  const uint32_t r = L / (uint32_t)n_split;
+  const uint32_t per = (uint32_t)NG * H * B;  // tasks of one part
+  t.part = (int)(L / per);
+  const uint32_t r = L % per;
   t.g = r % NG;
   t.h = (r / NG) % H;
   t.b = r / (NG * H);
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
   const int NG = N / G;
   const int64_t task = xcd_task(sp, blockIdx.x);
   if (task < 0) return;
-  const FwdTask tk = fwd_task((uint32_t)task, NG, H, n_split, ht, kLists ? cnt : nullptr);
+  const FwdTask tk = fwd_task((uint32_t)task, NG, H, B, n_split, ht, kLists ? cnt : nullptr);
   const int g = tk.g, h = tk.h, b = tk.b;
   const int k = tk.klen;  // blocks of this part
   const int NB = N / kBlock;
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __rest
   const int NG = N / G;
   const int64_t task = xcd_task(sp, blockIdx.x);
   if (task < 0) return;
-  const FwdTask tk = fwd_task((uint32_t)task, NG, H, n_split, ht, kLists ? cnt : nullptr);
+  const FwdTask tk = fwd_task((uint32_t)task, NG, H, B, n_split, ht, kLists ? cnt : nullptr);
   const int g = tk.g, h = tk.h, b = tk.b;
   const int k = tk.klen;  // blocks of this part
   const int32_t* irow = kLists ? idx + row_base(ht, b, h, NG) + (int64_t)g * ht.k[h] + tk.kbeg : nullptr;
@@ -396,8 +398,9 @@ hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* 
                       hipStream_t st) {
   const float scale_log2 = (1.0f / sqrtf((float)D)) * kLog2e;
   unsigned nwg = 0;
-  // a (group, part) task costs k_h / n_split blocks + 1; a head streams its K and V
-  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG * n_split, ht, 1.0 / n_split, 1.0, 4.0 * s.N * D, &nwg);
+  // a (part, group) task costs k_h / n_split blocks + 1; a head streams its K and V.  The parts are
+  // outermost in the task order: to the balancer they are n_split batches of the same heads
+  const XcdSplit sp = make_xcd_split(s.B * n_split, s.H, s.NG, ht, 1.0 / n_split, 1.0, 4.0 * s.N * D, &nwg);
   dim3 grid(nwg);
   if (s.bf16) {
     const hipError_t e = launch_cvt_f16(V, V16, (int64_t)s.B * s.H * s.N * D, st);

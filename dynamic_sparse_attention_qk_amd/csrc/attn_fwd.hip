@@ -28,23 +28,30 @@ namespace {
 // streams roughly one n_split-th of each head's K and V at a time; the part
 // covers list positions [part k_h / n_split, (part + 1) k_h / n_split).
 // n_split = 1 is the plain forward.
+//
+// Phases (phase >= 0, n_split = the phase count): the same segments of each
+// row's list, one launch per segment in order; the launch of phase p > 0
+// merges its state into the (O, LSE) the earlier phases stored.  Used for the
+// plain forward when one head's K and V fill more than half the MALL, so each launch
+// streams about 1/n_split of them.
 struct FwdTask {
   int g, h, b, part, kbeg, klen;
 };
 
 // cnt (if not null): blocks kept by each (b, h, g) row, clamped to [1, k_h] (k_h: the row's list capacity)
-__device__ __forceinline__ FwdTask fwd_task(uint32_t L, int NG, int H, int B, int n_split, const HeadTable& ht,
-                                            const int32_t* __restrict__ cnt) {
+__device__ __forceinline__ FwdTask fwd_task(uint32_t L, int NG, int H, int B, int n_split, int phase,
+                                            const HeadTable& ht, const int32_t* __restrict__ cnt) {
   FwdTask t;
   const uint32_t per = (uint32_t)NG * H * B;  // tasks of one part
-  t.part = (int)(L / per);
-  const uint32_t r = L % per;
+  const int seg = phase >= 0 ? phase : (int)(L / per);
+  t.part = phase >= 0 ? 0 : seg;
+  const uint32_t r = phase >= 0 ? L : L % per;
   t.g = r % NG;
   t.h = (r / NG) % H;
   t.b = r / (NG * H);
   const int k = cnt ? min(max(cnt[((size_t)t.b * H + t.h) * NG + t.g], 1), ht.k[t.h]) : ht.k[t.h];
-  t.kbeg = t.part * k / n_split;
-  t.klen = (t.part + 1) * k / n_split - t.kbeg;
+  t.kbeg = seg * k / n_split;
+  t.klen = (seg + 1) * k / n_split - t.kbeg;
   return t;
 }
 
@@ -61,7 +68,8 @@ __device__ __forceinline__ void write_empty_part(float* O, float* LSE, size_t ro
 }
 
 // kLists false: dense attention (no lists; list position t of the part is block kbeg + t).
-template <int D, int G, bool kLists>
+// kMerge: the phased launches (phase >= 0), which merge into the stored state after the first.
+template <int D, int G, bool kLists, bool kMerge>
 __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* __restrict__ Q,
                                                                  const bf16_t* __restrict__ K,
                                                                  const uint16_t* __restrict__ V16,
@@ -69,7 +77,7 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
                                                                  const int32_t* __restrict__ cnt,
                                                                  float* __restrict__ O, float* __restrict__ LSE,
                                                                  HeadTable ht, XcdSplit sp, int N, int H, int B,
-                                                                 int n_split, float scale_log2) {
+                                                                 int n_split, int phase, float scale_log2) {
   constexpr int NRT = G / 32;                  // 32-row tiles of the group
   constexpr int NW = 2 * NRT;                  // waves: row tile x key half
   constexpr int RB = 2 * D;                    // bytes per tile row
@@ -88,7 +96,7 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
   const int NG = N / G;
   const int64_t task = xcd_task(sp, blockIdx.x);
   if (task < 0) return;
-  const FwdTask tk = fwd_task((uint32_t)task, NG, H, B, n_split, ht, kLists ? cnt : nullptr);
+  const FwdTask tk = fwd_task((uint32_t)task, NG, H, B, n_split, phase, ht, kLists ? cnt : nullptr);
   const int g = tk.g, h = tk.h, b = tk.b;
   const int k = tk.klen;  // blocks of this part
   const int NB = N / kBlock;
@@ -103,8 +111,8 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
   const int l32 = lane & 31, hh = lane >> 5;
   const int rt = wave % NRT, kh = wave / NRT;  // rows 32*rt.., keys 32*kh.. of every block
   const int qrow = g * G + rt * 32 + l32;
-  if (k == 0) {  // uniform over the workgroup, before any barrier
-    if (kh == 0) write_empty_part<D>(O, LSE, bh * N + qrow, hh);
+  if (k == 0) {  // uniform over the workgroup, before any barrier; a later phase leaves the stored state
+    if (kh == 0 && (!kMerge || phase == 0)) write_empty_part<D>(O, LSE, bh * N + qrow, hh);
     return;
   }
   // block of list position min(t, k-1): past the end the last block is fetched again into a free
@@ -240,19 +248,35 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
     const float m = fmaxf(m_used, m1);
     const float a0 = __builtin_amdgcn_exp2f(m_used - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
     const float lsum = a0 * l_tot + a1 * l1;
-    const float inv = 1.0f / lsum;
+    float lse2 = m + __log2f(lsum);  // this segment's log-sum-exp, log2 domain
+    // a later phase: merge with the state of the earlier ones (weights e^{LSE_s - LSE}, normalised)
+    float wc = 1.0f, wp = 0.0f;
+    if (kMerge && phase > 0) {
+      const float lp2 = LSE[bh * N + qrow] * kLog2e;
+      const float M = fmaxf(lse2, lp2);
+      const float ec = __builtin_amdgcn_exp2f(lse2 - M), ep = __builtin_amdgcn_exp2f(lp2 - M);
+      const float W = ec + ep;
+      wc = ec / W;
+      wp = ep / W;
+      lse2 = M + __log2f(W);
+    }
+    const float inv = wc / lsum;
     const float w0 = a0 * inv, w1 = a1 * inv;
     float* orow = O + (bh * N + qrow) * (size_t)D;
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
+        float* op = orow + 32 * c + 8 * q4 + 4 * hh;
+        float4 prev = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (kMerge && phase > 0) prev = *reinterpret_cast<const float4*>(op);
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = oacc[c][4 * q4 + r] * w0 + mb[(c * 16 + 4 * q4 + r) * 64 + lane] * w1;
-        *reinterpret_cast<float4*>(orow + 32 * c + 8 * q4 + 4 * hh) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(op) =
+            make_float4(v[0] + prev.x * wp, v[1] + prev.y * wp, v[2] + prev.z * wp, v[3] + prev.w * wp);
       }
-    if (hh == 0) LSE[bh * N + qrow] = (m + __log2f(lsum)) * kLn2;
+    if (hh == 0) LSE[bh * N + qrow] = lse2 * kLn2;
   }
 }
 
@@ -272,7 +296,7 @@ __global__ __launch_bounds__(G * 2) void attn_fwd_f32_kernel(const float* __rest
   const int NG = N / G;
   const int64_t task = xcd_task(sp, blockIdx.x);
   if (task < 0) return;
-  const FwdTask tk = fwd_task((uint32_t)task, NG, H, B, n_split, ht, kLists ? cnt : nullptr);
+  const FwdTask tk = fwd_task((uint32_t)task, NG, H, B, n_split, -1, ht, kLists ? cnt : nullptr);
   const int g = tk.g, h = tk.h, b = tk.b;
   const int k = tk.klen;  // blocks of this part
   const int32_t* irow = kLists ? idx + row_base(ht, b, h, NG) + (int64_t)g * ht.k[h] + tk.kbeg : nullptr;
@@ -400,14 +424,26 @@ hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* 
   unsigned nwg = 0;
   // a (part, group) task costs k_h / n_split blocks + 1; a head streams its K and V.  The parts are
   // outermost in the task order: to the balancer they are n_split batches of the same heads
-  const XcdSplit sp = make_xcd_split(s.B * n_split, s.H, s.NG, ht, 1.0 / n_split, 1.0, 4.0 * s.N * D, &nwg);
+  const double head_bytes = 4.0 * s.N * D;  // one head's K (bf16) and V (fp16 copy)
+  const XcdSplit sp = make_xcd_split(s.B * n_split, s.H, s.NG, ht, 1.0 / n_split, 1.0, head_bytes, &nwg);
   dim3 grid(nwg);
   if (s.bf16) {
     const hipError_t e = launch_cvt_f16(V, V16, (int64_t)s.B * s.H * s.N * D, st);
     if (e != hipSuccess) return e;
-    auto kern = idx ? attn_fwd_bf16_kernel<D, G, true> : attn_fwd_bf16_kernel<D, G, false>;
+    auto kern = idx ? attn_fwd_bf16_kernel<D, G, true, false> : attn_fwd_bf16_kernel<D, G, false, false>;
+    // the plain forward over heads whose K and V fill more than half the MALL: kFwdPhases launches in sequence
+    if (n_split == 1 && head_bytes > 0.5 * kMallBytes) {
+      unsigned nwg_p = 0;
+      const XcdSplit spp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0 / kFwdPhases, 1.0, head_bytes, &nwg_p);
+      auto kern_m = idx ? attn_fwd_bf16_kernel<D, G, true, true> : attn_fwd_bf16_kernel<D, G, false, true>;
+      for (int ph = 0; ph < kFwdPhases; ++ph)
+        hipLaunchKernelGGL(kern_m, dim3(nwg_p), dim3(G * 4), 0, st, static_cast<const bf16_t*>(Q),
+                           static_cast<const bf16_t*>(K), V16, idx, cnt, O, LSE, ht, spp, s.N, s.H, s.B, kFwdPhases, ph,
+                           scale_log2);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL(kern, grid, dim3(G * 4), 0, st, static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K),
-                       V16, idx, cnt, O, LSE, ht, sp, s.N, s.H, s.B, n_split, scale_log2);
+                       V16, idx, cnt, O, LSE, ht, sp, s.N, s.H, s.B, n_split, -1, scale_log2);
   } else {
     auto kern = idx ? attn_fwd_f32_kernel<D, G, true> : attn_fwd_f32_kernel<D, G, false>;
     hipLaunchKernelGGL(kern, grid, dim3(G * 2), 0, st, static_cast<const float*>(Q), static_cast<const float*>(K),

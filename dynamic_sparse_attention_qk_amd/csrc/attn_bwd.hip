@@ -67,7 +67,9 @@ __device__ __forceinline__ f16x8 ldg_f16x8(const uint16_t* p) { return __builtin
 // ---------------------------------------------------------------- dQ
 
 // kLists false: dense attention (no lists; list position t is block t).
-template <int D, int G, bool kLists>
+// kMerge: phase `phase` of n_phase launches in sequence, each over one segment of every row's list (for
+// heads whose K and V fill more than half the MALL); launches after the first add into the stored dQ.
+template <int D, int G, bool kLists, bool kMerge>
 __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __restrict__ Q16,
                                                           const uint16_t* __restrict__ K16,
                                                           const uint16_t* __restrict__ V16,
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
                                                           const int32_t* __restrict__ idx,
                                                           const int32_t* __restrict__ cnt, float* __restrict__ dQ,
                                                           HeadTable ht, XcdSplit sp, int N, int H, int B, float scale_log2,
-                                                          float tau) {
+                                                          float tau, int n_phase, int phase) {
   constexpr int NRT = G / 32;
   constexpr int NW = 2 * NRT;
   constexpr int RB = 2 * D;
@@ -92,9 +94,11 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
   const uint32_t L = (uint32_t)task;
   const int g = L % NG, h = (L / NG) % H, b = L / (NG * H);
   // blocks of this row: cnt (if given, clamped to [1, k_h]) or k_h; rows are k_h entries apart
-  const int k = (kLists && cnt) ? min(max(cnt[((size_t)b * H + h) * NG + g], 1), ht.k[h]) : ht.k[h];
+  const int kfull = (kLists && cnt) ? min(max(cnt[((size_t)b * H + h) * NG + g], 1), ht.k[h]) : ht.k[h];
+  const int kbeg = kMerge ? phase * kfull / n_phase : 0;  // this phase's segment of the list
+  const int k = kMerge ? (phase + 1) * kfull / n_phase - kbeg : kfull;
   const int NB = N / kBlock;
-  const int32_t* irow = kLists ? idx + row_base(ht, b, h, NG) + (int64_t)g * ht.k[h] : nullptr;
+  const int32_t* irow = kLists ? idx + row_base(ht, b, h, NG) + (int64_t)g * ht.k[h] + kbeg : nullptr;
   const size_t bh = (size_t)b * H + h;
   const uint16_t* Kbh = K16 + bh * (size_t)N * D;
   const uint16_t* Vbh = V16 + bh * (size_t)N * D;
@@ -102,10 +106,21 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
   const int l32 = lane & 31, hh = lane >> 5;
   const int rt = wave % NRT, kh = wave / NRT;
   const size_t qrow = bh * N + (size_t)g * G + rt * 32 + l32;
+  if (kMerge && k == 0) {  // an empty segment (uniform over the workgroup, before any barrier)
+    if (phase == 0 && kh == 0) {
+      float* orow = dQ + qrow * D;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<float4*>(orow + 32 * c + 8 * q4 + 4 * hh) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
   // block of list position min(t, k-1); ids are valid by contract, clamped so a bad list cannot read out of bounds
   auto block_id = [&](int t) {
     if constexpr (kLists) return min(max(irow[min(t, k - 1)], 0), NB - 1);
-    else return min(t, k - 1);
+    else return kbeg + min(t, k - 1);
   };
 
   f16x8 qreg[D / 16], oreg[D / 16];
@@ -216,10 +231,13 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
     for (int c = 0; c < D / 32; ++c)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
+        float* op = orow + 32 * c + 8 * q4 + 4 * hh;
+        float4 prev = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (kMerge && phase > 0) prev = *reinterpret_cast<const float4*>(op);
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = (acc[c][4 * q4 + r] + mb[(c * 16 + 4 * q4 + r) * 64 + lane]) * tau;
-        *reinterpret_cast<float4*>(orow + 32 * c + 8 * q4 + 4 * hh) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(op) = make_float4(prev.x + v[0], prev.y + v[1], prev.z + v[2], prev.w + v[3]);
       }
   }
 }
@@ -293,7 +311,9 @@ __global__ __launch_bounds__(256) void dkdv_order_kernel(const int32_t* __restri
 // MFMA of a wave with 16 keys), and the two query halves' dK, dV partials are
 // summed once at the end.  S starts from -LSE/tau and dP from -D, so
 // P = exp2(S tau log2 e) and dS = P dP need no per-row values afterwards.
-template <int D, int G, bool kLists>
+// kMerge: phase `phase` of n_phase launches in sequence, each over one segment of every reverse list
+// (for heads whose Q and dO fill more than half the MALL); launches after the first add into dK, dV.
+template <int D, int G, bool kLists, bool kMerge>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q16,
                                                           const uint16_t* __restrict__ K16,
                                                           const uint16_t* __restrict__ V16,
@@ -304,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
                                                           const int32_t* __restrict__ rev_idx,
                                                           const int32_t* __restrict__ order, float* __restrict__ dK,
                                                           float* __restrict__ dV, HeadTable ht, XcdSplit sp, int N, int H, int NB,
-                                                          int B, float tau) {
+                                                          int B, float tau, int n_phase, int phase) {
   constexpr int NW = 4;
   constexpr int RB = 2 * D;
   constexpr int TILE = 64 * RB;
@@ -337,8 +357,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
     const int32_t* rp = rev_ptr + bh * (NB + 1);
     s0 = min(max(rp[j], 0), total);
     s1 = min(max(rp[j + 1], s0), total);
-    rlist = rev_idx + row_base(ht, b, h, NG) + s0;
   }
+  if constexpr (kMerge) {  // this phase's segment of the list
+    const int32_t len = s1 - s0, base = s0;
+    s0 = base + (int32_t)((int64_t)phase * len / n_phase);
+    s1 = base + (int32_t)((int64_t)(phase + 1) * len / n_phase);
+    if (phase > 0 && s1 == s0) return;  // nothing to add (uniform over the workgroup, before any barrier)
+  }
+  if constexpr (kLists) rlist = rev_idx + row_base(ht, b, h, NG) + s0;
   const int iters = (s1 - s0) * SUB;
 
   // this wave's keys as B operands (half kk: keys 32*kh + 16*kk + l16): K for
@@ -371,7 +397,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
   // vector load; clamped when used: never out of bounds
   auto group_of = [&](int it) {
     if constexpr (kLists) return ldv_i32(rlist + min(it, iters - 1) / SUB);
-    else return min(it, iters - 1) / SUB;
+    else return s0 + min(it, iters - 1) / SUB;
   };
   // groups read ahead: at step it, g_n = group of tile it+1 and g_pf = group of tile it+2 are in registers
   int g_n = 0, g_pf = 0;
@@ -489,7 +515,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float own = qh ? dv[kk][c][e] : dk[kk][c][e];
-        out[(key0 + 16 * kk + e) * D + 16 * c + l16] = (own + other[((kk * NC + c) * 4 + e) * 64 + lane]) * mul;
+        float* op = out + (key0 + 16 * kk + e) * D + 16 * c + l16;
+        const float prev = (kMerge && phase > 0) ? *op : 0.0f;
+        *op = prev + (own + other[((kk * NC + c) * 4 + e) * 64 + lane]) * mul;
       }
 }
 
@@ -510,14 +538,23 @@ hipError_t dkdv_launch(const Shape& s, const BwdWork& w, const int32_t* rev_ptr,
   const float tau = 1.0f / sqrtf((float)D);
   // a KV block costs its reverse-list length, NG * k_h / NB on average, + 1; a head streams its Q and dO
   unsigned nwg = 0;
-  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NB, ht, (double)s.NG / s.NB, 1.0, 4.0 * s.N * D, &nwg);
+  const double head_bytes = 4.0 * s.N * D;  // one head's Q and dO (fp16 copies)
+  const int nph = head_bytes > 0.5 * kMallBytes ? kMallPhases : 1;  // phases over segments of every list
+  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NB, ht, (double)s.NG / s.NB / nph, 1.0, head_bytes, &nwg);
   const unsigned nseg = sp.items ? kXcds * (unsigned)sp.runs : kXcds;
   // dense (no reverse lists): every block has all NG groups and the order is the identity
   if (rev_ptr)
     hipLaunchKernelGGL(dkdv_order_kernel, dim3(nseg), dim3(256), 0, st, rev_ptr, w.order, ht, sp, s.NB, s.NG, s.H);
-  auto kern = rev_ptr ? bwd_dkdv_kernel<D, G, true> : bwd_dkdv_kernel<D, G, false>;
+  if (nph > 1) {
+    auto kern = rev_ptr ? bwd_dkdv_kernel<D, G, true, true> : bwd_dkdv_kernel<D, G, false, true>;
+    for (int ph = 0; ph < nph; ++ph)
+      hipLaunchKernelGGL(kern, dim3(nwg), dim3(256), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, rev_ptr,
+                         rev_idx, w.order, dK, dV, ht, sp, s.N, s.H, s.NB, s.B, tau, nph, ph);
+    return hipGetLastError();
+  }
+  auto kern = rev_ptr ? bwd_dkdv_kernel<D, G, true, false> : bwd_dkdv_kernel<D, G, false, false>;
   hipLaunchKernelGGL(kern, dim3(nwg), dim3(256), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, rev_ptr, rev_idx,
-                     w.order, dK, dV, ht, sp, s.N, s.H, s.NB, s.B, tau);
+                     w.order, dK, dV, ht, sp, s.N, s.H, s.NB, s.B, tau, 1, -1);
   return hipGetLastError();
 }
 
@@ -526,10 +563,19 @@ hipError_t dq_launch(const Shape& s, const BwdWork& w, const int32_t* idx, const
                      const HeadTable& ht, hipStream_t st) {
   const float tau = 1.0f / sqrtf((float)D);
   unsigned nwg = 0;
-  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0, 1.0, 4.0 * s.N * D, &nwg);  // a group costs k_h + 1
-  auto kern = idx ? bwd_dq_kernel<D, G, true> : bwd_dq_kernel<D, G, false>;
+  const double head_bytes = 4.0 * s.N * D;  // one head's K and V (fp16 copies)
+  if (head_bytes > 0.5 * kMallBytes) {  // phases over segments of every list, each streaming ~1/kMallPhases
+    const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0 / kMallPhases, 1.0, head_bytes, &nwg);
+    auto kern = idx ? bwd_dq_kernel<D, G, true, true> : bwd_dq_kernel<D, G, false, true>;
+    for (int ph = 0; ph < kMallPhases; ++ph)
+      hipLaunchKernelGGL(kern, dim3(nwg), dim3(G * 4), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, idx, cnt, dQ,
+                         ht, sp, s.N, s.H, s.B, tau * kLog2e, tau, kMallPhases, ph);
+    return hipGetLastError();
+  }
+  const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0, 1.0, head_bytes, &nwg);  // a group costs k_h + 1
+  auto kern = idx ? bwd_dq_kernel<D, G, true, false> : bwd_dq_kernel<D, G, false, false>;
   hipLaunchKernelGGL(kern, dim3(nwg), dim3(G * 4), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, idx, cnt, dQ, ht,
-                     sp, s.N, s.H, s.B, tau * kLog2e, tau);
+                     sp, s.N, s.H, s.B, tau * kLog2e, tau, 1, -1);
   return hipGetLastError();
 }
 

@@ -262,9 +262,9 @@ __device__ __forceinline__ int64_t xcd_task(const XcdSplit& sp, uint32_t w) {
 // what one (b, h) run streams (K and V, or Q and dO), which decides the mode.  grid covers the largest part.
 // MI355X's Infinity Cache (MALL), shared by the XCDs
 constexpr double kMallBytes = 256.0 * 1024 * 1024;
-// Phases of the plain bf16 forward when one head's K and V fill more than half the MALL (measured at 520k tokens:
-// 4 segments of each list, in sequence, 14% faster than one pass)
-constexpr int kFwdPhases = 4;
+// Phases of the attention kernels when one head's K and V (or Q and dO) fill more than half the MALL:
+// segments of every list in sequence (measured at 520k tokens: the forward 14% faster than one pass)
+constexpr int kMallPhases = 4;
 
 inline XcdSplit make_xcd_split(int B, int H, int items, const HeadTable& ht, double scale, double overhead,
                                double head_bytes, unsigned* grid) {

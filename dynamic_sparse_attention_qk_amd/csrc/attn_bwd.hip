@@ -539,7 +539,7 @@ hipError_t dkdv_launch(const Shape& s, const BwdWork& w, const int32_t* rev_ptr,
   // a KV block costs its reverse-list length, NG * k_h / NB on average, + 1; a head streams its Q and dO
   unsigned nwg = 0;
   const double head_bytes = 4.0 * s.N * D;  // one head's Q and dO (fp16 copies)
-  const int nph = head_bytes > 0.5 * kMallBytes ? kMallPhases : 1;  // phases over segments of every list
+  const int nph = head_bytes > 0.5 * kMallBytes ? kMallPhasesQdO : 1;  // phases over segments of every list
   const XcdSplit sp = make_xcd_split(s.B, s.H, s.NB, ht, (double)s.NG / s.NB / nph, 1.0, head_bytes, &nwg);
   const unsigned nseg = sp.items ? kXcds * (unsigned)sp.runs : kXcds;
   // dense (no reverse lists): every block has all NG groups and the order is the identity
@@ -564,12 +564,12 @@ hipError_t dq_launch(const Shape& s, const BwdWork& w, const int32_t* idx, const
   const float tau = 1.0f / sqrtf((float)D);
   unsigned nwg = 0;
   const double head_bytes = 4.0 * s.N * D;  // one head's K and V (fp16 copies)
-  if (head_bytes > 0.5 * kMallBytes) {  // phases over segments of every list, each streaming ~1/kMallPhases
-    const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0 / kMallPhases, 1.0, head_bytes, &nwg);
+  if (head_bytes > 0.5 * kMallBytes) {  // phases over segments of every list, each streaming ~1/kMallPhasesKV
+    const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0 / kMallPhasesKV, 1.0, head_bytes, &nwg);
     auto kern = idx ? bwd_dq_kernel<D, G, true, true> : bwd_dq_kernel<D, G, false, true>;
-    for (int ph = 0; ph < kMallPhases; ++ph)
+    for (int ph = 0; ph < kMallPhasesKV; ++ph)
       hipLaunchKernelGGL(kern, dim3(nwg), dim3(G * 4), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, idx, cnt, dQ,
-                         ht, sp, s.N, s.H, s.B, tau * kLog2e, tau, kMallPhases, ph);
+                         ht, sp, s.N, s.H, s.B, tau * kLog2e, tau, kMallPhasesKV, ph);
     return hipGetLastError();
   }
   const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0, 1.0, head_bytes, &nwg);  // a group costs k_h + 1

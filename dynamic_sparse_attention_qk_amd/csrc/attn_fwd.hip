@@ -431,14 +431,14 @@ hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* 
     const hipError_t e = launch_cvt_f16(V, V16, (int64_t)s.B * s.H * s.N * D, st);
     if (e != hipSuccess) return e;
     auto kern = idx ? attn_fwd_bf16_kernel<D, G, true, false> : attn_fwd_bf16_kernel<D, G, false, false>;
-    // the plain forward over heads whose K and V fill more than half the MALL: kMallPhases launches in sequence
+    // the plain forward over heads whose K and V fill more than half the MALL: kMallPhasesKV launches in sequence
     if (n_split == 1 && head_bytes > 0.5 * kMallBytes) {
       unsigned nwg_p = 0;
-      const XcdSplit spp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0 / kMallPhases, 1.0, head_bytes, &nwg_p);
+      const XcdSplit spp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0 / kMallPhasesKV, 1.0, head_bytes, &nwg_p);
       auto kern_m = idx ? attn_fwd_bf16_kernel<D, G, true, true> : attn_fwd_bf16_kernel<D, G, false, true>;
-      for (int ph = 0; ph < kMallPhases; ++ph)
+      for (int ph = 0; ph < kMallPhasesKV; ++ph)
         hipLaunchKernelGGL(kern_m, dim3(nwg_p), dim3(G * 4), 0, st, static_cast<const bf16_t*>(Q),
-                           static_cast<const bf16_t*>(K), V16, idx, cnt, O, LSE, ht, spp, s.N, s.H, s.B, kMallPhases, ph,
+                           static_cast<const bf16_t*>(K), V16, idx, cnt, O, LSE, ht, spp, s.N, s.H, s.B, kMallPhasesKV, ph,
                            scale_log2);
       return hipGetLastError();
     }

@@ -263,8 +263,10 @@ __device__ __forceinline__ int64_t xcd_task(const XcdSplit& sp, uint32_t w) {
 // MI355X's Infinity Cache (MALL), shared by the XCDs
 constexpr double kMallBytes = 256.0 * 1024 * 1024;
 // Phases of the attention kernels when one head's K and V (or Q and dO) fill more than half the MALL:
-// segments of every list in sequence (measured at 520k tokens: the forward 14% faster than one pass)
-constexpr int kMallPhases = 4;
+// segments of every list in sequence.  Measured at 520k tokens (one pass / 4 / 8 phases, ms): forward
+// 688 / 578 / 542, dQ 677 / 600 / 569, dK/dV 828 / 793 / 825.
+constexpr int kMallPhasesKV = 8;   // kernels streaming K and V tiles (forward, dQ)
+constexpr int kMallPhasesQdO = 4;  // the kernel streaming Q and dO tiles (dK/dV)
 
 inline XcdSplit make_xcd_split(int B, int H, int items, const HeadTable& ht, double scale, double overhead,
                                double head_bytes, unsigned* grid) {

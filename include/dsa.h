@@ -162,6 +162,10 @@ int dsa_select_topk_blocks(const dsa_problem* p, const float* scores, const floa
  * for bf16 inputs; 0 bytes, NULL allowed, for fp32 inputs).  bf16 V, and every
  * bf16 input of the backward, must be below 65504 in magnitude (products with
  * softmax probabilities run on fp16 operands, converted exactly from bf16).
+ * When one head's K and V copies (4*N*d bytes) fill more than half of the
+ * 256 MiB Infinity Cache, the call runs as several launches over segments of
+ * every list, the later ones merging into O and LSE in place; O and LSE hold
+ * partial states until the call's work on the stream has finished.
  */
 int dsa_sparse_attn_fwd(const dsa_problem* p, const void* Q, const void* K, const void* V,
                         const int32_t* idx, const int32_t* k_per_head, float* O, float* LSE,
@@ -175,7 +179,9 @@ int dsa_sparse_attn_fwd(const dsa_problem* p, const void* Q, const void* K, cons
  *   dQ_g = tau dS K, dK_m = tau sum dS^T Q, dV_m = sum P^T dO,
  * keys of blocks no group kept get dK = dV = 0.  Needs the forward's O and
  * LSE, and rev_ptr/rev_idx from dsa_select_topk_blocks.  dQ, dK, dV:
- * [B,H,N,d] fp32.  bf16 inputs only.  Deterministic (no atomics).
+ * [B,H,N,d] fp32.  bf16 inputs only.  Deterministic (no atomics).  For
+ * heads beyond half the Infinity Cache (as for the forward) the dQ and dK/dV
+ * stages run as several launches that add into dQ, dK, dV in place.
  * Workspace: dsa_workspace_bytes(p, k_per_head, DSA_WS_BWD).
  */
 int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, const void* V,

@@ -64,7 +64,7 @@ def cpu_baseline(inp, target_s: float):
     heads in order, each predicted and selected whole, then fwd(+bwd) group by
     group until about target_s seconds of CPU work."""
     import oracle
-    from tests.parity import f64
+    from synth.device import f64
     try:
         from threadpoolctl import threadpool_info
         threads = max([t.get("num_threads", 1) for t in threadpool_info() if t.get("user_api") == "blas"] or [1])
@@ -289,7 +289,7 @@ def dispatch_sweep(args, w, stream):
     import torch
     import synth
     import dynamic_sparse_attention_qk_amd as dsa
-    from tests.parity import problem_of, to_device
+    from synth.device import problem_of, to_device
 
     wb = w.with_(backward=True)
     inp = synth.generate(wb)
@@ -361,7 +361,7 @@ def main():
     import torch
     import synth
     import dynamic_sparse_attention_qk_amd as dsa
-    from tests.parity import problem_of, to_device
+    from synth.device import problem_of, to_device
 
     w = synth.workload(args.workload)
     t0 = time.time()

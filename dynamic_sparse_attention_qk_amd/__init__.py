@@ -133,18 +133,124 @@ class Problem:
     def n_blocks(self) -> int:
         return self.seq_len // self.block
 
+    @property
+    def rows(self) -> int:
+        """B * H * N: rows of O, LSE and every [B, H, N, d] tensor."""
+        return self.batch * self.heads * self.seq_len
 
-def _kph(k_per_head: Sequence[int]):
-    arr = (ctypes.c_int32 * len(k_per_head))(*[int(x) for x in k_per_head])
-    return arr
+    @property
+    def elems(self) -> int:
+        """B * H * N * d: elements of Q, K, V, dO, O, dQ, dK, dV."""
+        return self.rows * self.head_dim
+
+    def list_len(self, k_per_head: Sequence[int]) -> int:
+        """Entries of the kept-block list (and of the reverse list): B * NG * sum_h k_h."""
+        return self.batch * self.n_groups * int(sum(int(x) for x in k_per_head))
 
 
-def _ptr(t: Optional[torch.Tensor]):
-    if t is None:
-        return None
-    if not t.is_contiguous():
-        raise ValueError("tensors passed to libdsa must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
+
+
+def _kph(k_per_head: Sequence[int], heads: Optional[int] = None):
+    """Host int32 array of the kept counts; with ``heads``, its length must equal the head count."""
+    if heads is not None and len(k_per_head) != heads:
+        raise ValueError(f"k_per_head has {len(k_per_head)} entries for {heads} heads")
+    return (ctypes.c_int32 * len(k_per_head))(*[int(x) for x in k_per_head])
+
+
+_I32, _F32 = torch.int32, torch.float32
+
+
+def _io(p: "Problem"):
+    """torch dtype of Q, K, V, dO for the problem."""
+    return torch.bfloat16 if p.dtype == DSA_BF16 else torch.float32
+
+
+class _Args:
+    """Pointers for one library call, after checking what the C ABI cannot: dtype, size, layout, device.
+
+    The ABI receives bare pointers, so a short tensor or one of the wrong dtype would let the kernels read or
+    write past an allocation; every such mismatch raises here instead.  dtype, size and layout are checked as
+    each argument is added, the device of all of them when the call is made (so every other mismatch is
+    reported first, also for host tensors).
+    """
+
+    def __init__(self, p: "Problem"):
+        self.p = p
+        self._tensors = []
+
+    def t(self, t: Optional[torch.Tensor], name: str, dtype=None, numel: Optional[int] = None,
+          required: bool = True):
+        if t is None:
+            if required:
+                raise ValueError(f"{name} is required")
+            return None
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if numel is not None and t.numel() < numel:
+            raise ValueError(f"{name} holds {t.numel()} elements, the problem needs {numel}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: tensors passed to libdsa must be contiguous")
+        self._tensors.append((name, t))
+        return ctypes.c_void_p(t.data_ptr())
+
+    # tensors whose sizes the problem fixes
+    def io(self, t, name, required=True):          # Q, K, V, dO: [B, H, N, d] in the problem's dtype
+        return self.t(t, name, _io(self.p), self.p.elems, required)
+
+    def f32(self, t, name, numel, required=True):
+        return self.t(t, name, _F32, numel, required)
+
+    def out(self, t, name, parts=1):              # O, dQ, dK, dV (per part): [B, H, N, d] fp32
+        return self.t(t, name, _F32, parts * self.p.elems)
+
+    def rows(self, t, name, parts=1):             # LSE (per part): [B, H, N] fp32
+        return self.t(t, name, _F32, parts * self.p.rows)
+
+    def weights(self, t, name):                   # Wq, Wk, dWq, dWk: [H, d, r] fp32
+        p = self.p
+        return self.t(t, name, _F32, p.heads * p.head_dim * p.rank)
+
+    def scores(self, t, name="scores", required=False):
+        p = self.p
+        return self.t(t, name, _F32, p.batch * p.heads * p.n_groups * p.n_blocks, required)
+
+    def qhat(self, t, required=False):
+        p = self.p
+        return self.t(t, "qhat", _F32, p.batch * p.heads * p.n_groups * p.rank, required)
+
+    def khat(self, t, required=False):
+        p = self.p
+        return self.t(t, "khat", _F32, p.batch * p.heads * p.n_blocks * p.rank, required)
+
+    def idx(self, t, kph, name="idx"):            # kept-block list / reverse list: B * NG * sum k_h int32
+        return self.t(t, name, _I32, self.p.list_len(kph))
+
+    def rev_ptr(self, t):
+        p = self.p
+        return self.t(t, "rev_ptr", _I32, p.batch * p.heads * (p.n_blocks + 1))
+
+    def cnt(self, t, required=True):
+        p = self.p
+        return self.t(t, "cnt", _I32, p.batch * p.heads * p.n_groups, required)
+
+    def ws(self, t, required=True):
+        """A workspace: any dtype; its byte count goes to the library, which checks it against the call."""
+        return self.t(t, "workspace", None, None, required), _nbytes(t)
+
+    def call(self, fn: str, *args, stream=None) -> int:
+        """Checks that every tensor is on the GPU, then calls libdsa's ``fn`` with ``args`` and the stream (the
+        current one if None) last; raises on a negative status."""
+        for name, t in self._tensors:
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+        st = getattr(library(), fn)(*args, _stream(stream))
+        if st < 0:
+            _check(fn, st)
+        return st
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream(stream=None):
@@ -170,118 +276,124 @@ def index_layout(p: Problem, k_per_head: Sequence[int]) -> np.ndarray:
     """Host int64 [B*H + 1] offsets of each (b, h) region of the kept-block list."""
     out = np.zeros(p.batch * p.heads + 1, dtype=np.int64)
     _check("dsa_index_layout", library().dsa_index_layout(
-        ctypes.byref(p.c()), _kph(k_per_head), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+        ctypes.byref(p.c()), _kph(k_per_head, p.heads), out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
     return out
 
 
 def workspace_bytes(p: Problem, k_per_head: Optional[Sequence[int]], which: int) -> int:
     """Workspace bytes of a call; k_per_head may be None for DSA_WS_FWD / DSA_WS_BWD / DSA_WS_PRED_GRAD."""
-    kph = None if k_per_head is None else _kph(k_per_head)
+    kph = None if k_per_head is None else _kph(k_per_head, p.heads)
     return int(library().dsa_workspace_bytes(ctypes.byref(p.c()), kph, which))
 
 
 def predict_block_scores(p: Problem, Q, K, Wq, Wk, qhat, khat, scores=None, stream=None) -> None:
-    _check("dsa_predict_block_scores", library().dsa_predict_block_scores(
-        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(qhat), _ptr(khat), _ptr(scores),
-        _stream(stream)))
+    a = _Args(p)
+    a.call("dsa_predict_block_scores", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.weights(Wq, "Wq"),
+           a.weights(Wk, "Wk"), a.qhat(qhat, True), a.khat(khat, True), a.scores(scores), stream=stream)
+
+
+def predict_block_scores_pooled(p: Problem, Q, K, Wq, Wk, pooling: int, scores, workspace, stream=None) -> None:
+    """Block scores pooled from the token-level low-rank logits (POOL_MAX or POOL_LSE)."""
+    a = _Args(p)
+    a.call("dsa_predict_block_scores_pooled", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"),
+           a.weights(Wq, "Wq"), a.weights(Wk, "Wk"), int(pooling), a.scores(scores, required=True), *a.ws(workspace),
+           stream=stream)
 
 
 def select_topk_blocks(p: Problem, scores, qhat, khat, k_per_head, idx, rev_ptr, rev_idx, workspace,
                        scores_dump=None, stream=None) -> None:
-    _check("dsa_select_topk_blocks", library().dsa_select_topk_blocks(
-        ctypes.byref(p.c()), _ptr(scores), _ptr(qhat), _ptr(khat), _kph(k_per_head), _ptr(idx), _ptr(rev_ptr),
-        _ptr(rev_idx), _ptr(scores_dump), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+    a = _Args(p)
+    kph = _kph(k_per_head, p.heads)
+    a.call("dsa_select_topk_blocks", ctypes.byref(p.c()), a.scores(scores), a.qhat(qhat), a.khat(khat), kph,
+           a.idx(idx, k_per_head), a.rev_ptr(rev_ptr), a.idx(rev_idx, k_per_head, "rev_idx"),
+           a.scores(scores_dump, "scores_dump"), *a.ws(workspace), stream=stream)
 
 
 def select_coverage_blocks(p: Problem, scores, qhat, khat, k_per_head, coverage: float, idx, cnt, rev_ptr, rev_idx,
                            workspace, scores_dump=None, stream=None) -> None:
     """Per row, the shortest run of blocks in score order whose estimated attention mass reaches coverage
     (at most k_h); counts to cnt [B, H, NG]."""
-    _check("dsa_select_coverage_blocks", library().dsa_select_coverage_blocks(
-        ctypes.byref(p.c()), _ptr(scores), _ptr(qhat), _ptr(khat), _kph(k_per_head), float(coverage), _ptr(idx),
-        _ptr(cnt), _ptr(rev_ptr), _ptr(rev_idx), _ptr(scores_dump), _ptr(workspace), _nbytes(workspace),
-        _stream(stream)))
-
-
-def predict_block_scores_pooled(p: Problem, Q, K, Wq, Wk, pooling: int, scores, workspace, stream=None) -> None:
-    """Block scores pooled from the token-level low-rank logits (POOL_MAX or POOL_LSE)."""
-    _check("dsa_predict_block_scores_pooled", library().dsa_predict_block_scores_pooled(
-        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), int(pooling), _ptr(scores), _ptr(workspace),
-        _nbytes(workspace), _stream(stream)))
+    a = _Args(p)
+    kph = _kph(k_per_head, p.heads)
+    a.call("dsa_select_coverage_blocks", ctypes.byref(p.c()), a.scores(scores), a.qhat(qhat), a.khat(khat), kph,
+           float(coverage), a.idx(idx, k_per_head), a.cnt(cnt), a.rev_ptr(rev_ptr),
+           a.idx(rev_idx, k_per_head, "rev_idx"), a.scores(scores_dump, "scores_dump"), *a.ws(workspace),
+           stream=stream)
 
 
 def select_blocks(p: Problem, scores, qhat, khat, k_per_head, coverage: float, flags: int, idx, cnt, rev_ptr,
                   rev_idx, workspace, scores_dump=None, stream=None) -> None:
     """The general selection: top-k (coverage 0) or by coverage, optionally with the diagonal forced."""
-    _check("dsa_select_blocks", library().dsa_select_blocks(
-        ctypes.byref(p.c()), _ptr(scores), _ptr(qhat), _ptr(khat), _kph(k_per_head), float(coverage), int(flags),
-        _ptr(idx), _ptr(cnt), _ptr(rev_ptr), _ptr(rev_idx), _ptr(scores_dump), _ptr(workspace), _nbytes(workspace),
-        _stream(stream)))
-
-
-def sparse_attn_fwd_varlen(p: Problem, Q, K, V, idx, cnt, k_per_head, O, LSE, workspace=None, stream=None) -> None:
-    nbytes = 0 if workspace is None else _nbytes(workspace)
-    _check("dsa_sparse_attn_fwd_varlen", library().dsa_sparse_attn_fwd_varlen(
-        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(cnt), _kph(k_per_head), _ptr(O), _ptr(LSE),
-        _ptr(workspace), nbytes, _stream(stream)))
-
-
-def sparse_attn_bwd_varlen(p: Problem, Q, K, V, O, dO, LSE, idx, cnt, k_per_head, rev_ptr, rev_idx, dQ, dK, dV,
-                           workspace, stream=None) -> None:
-    _check("dsa_sparse_attn_bwd_varlen", library().dsa_sparse_attn_bwd_varlen(
-        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(idx), _ptr(cnt),
-        _kph(k_per_head), _ptr(rev_ptr), _ptr(rev_idx), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace),
-        _nbytes(workspace), _stream(stream)))
+    a = _Args(p)
+    kph = _kph(k_per_head, p.heads)
+    a.call("dsa_select_blocks", ctypes.byref(p.c()), a.scores(scores), a.qhat(qhat), a.khat(khat), kph,
+           float(coverage), int(flags), a.idx(idx, k_per_head), a.cnt(cnt, required=False), a.rev_ptr(rev_ptr),
+           a.idx(rev_idx, k_per_head, "rev_idx"), a.scores(scores_dump, "scores_dump"), *a.ws(workspace),
+           stream=stream)
 
 
 def sparse_attn_fwd(p: Problem, Q, K, V, idx, k_per_head, O, LSE, workspace=None, stream=None) -> None:
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("dsa_sparse_attn_fwd", library().dsa_sparse_attn_fwd(
-        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _kph(k_per_head), _ptr(O), _ptr(LSE),
-        _ptr(workspace), nbytes, _stream(stream)))
+    a = _Args(p)
+    kph = _kph(k_per_head, p.heads)
+    a.call("dsa_sparse_attn_fwd", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.io(V, "V"),
+           a.idx(idx, k_per_head), kph, a.out(O, "O"), a.rows(LSE, "LSE"), *a.ws(workspace, False),
+           stream=stream)
+
+
+def sparse_attn_fwd_varlen(p: Problem, Q, K, V, idx, cnt, k_per_head, O, LSE, workspace=None, stream=None) -> None:
+    a = _Args(p)
+    kph = _kph(k_per_head, p.heads)
+    a.call("dsa_sparse_attn_fwd_varlen", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.io(V, "V"),
+           a.idx(idx, k_per_head), a.cnt(cnt), kph, a.out(O, "O"), a.rows(LSE, "LSE"), *a.ws(workspace, False),
+           stream=stream)
 
 
 def sparse_attn_fwd_split(p: Problem, Q, K, V, idx, k_per_head, n_split: int, O_part, LSE_part, workspace=None,
                           stream=None) -> None:
     """Partial states over n_split contiguous parts of every row's kept list: O_part [n_split, B, H, N, d],
     LSE_part [n_split, B, H, N] (fp32)."""
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("dsa_sparse_attn_fwd_split", library().dsa_sparse_attn_fwd_split(
-        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _kph(k_per_head), int(n_split), _ptr(O_part),
-        _ptr(LSE_part), _ptr(workspace), nbytes, _stream(stream)))
+    a = _Args(p)
+    kph = _kph(k_per_head, p.heads)
+    n = max(int(n_split), 1)
+    a.call("dsa_sparse_attn_fwd_split", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.io(V, "V"),
+           a.idx(idx, k_per_head), kph, int(n_split), a.out(O_part, "O_part", n), a.rows(LSE_part, "LSE_part", n),
+           *a.ws(workspace, False), stream=stream)
 
 
 def attn_merge(p: Problem, n_parts: int, O_part, LSE_part, O, LSE, stream=None) -> None:
     """O, LSE from n_parts partial states (log-sum-exp weighted)."""
-    _check("dsa_attn_merge", library().dsa_attn_merge(
-        ctypes.byref(p.c()), int(n_parts), _ptr(O_part), _ptr(LSE_part), _ptr(O), _ptr(LSE), _stream(stream)))
+    a = _Args(p)
+    n = max(int(n_parts), 1)
+    a.call("dsa_attn_merge", ctypes.byref(p.c()), int(n_parts), a.out(O_part, "O_part", n),
+           a.rows(LSE_part, "LSE_part", n), a.out(O, "O"), a.rows(LSE, "LSE"), stream=stream)
 
 
 def dense_attn_fwd(p: Problem, Q, K, V, O, LSE, workspace=None, stream=None) -> None:
     """Full attention over every key (the dispatcher's dense branch)."""
-    nbytes = 0 if workspace is None else _nbytes(workspace)
-    _check("dsa_dense_attn_fwd", library().dsa_dense_attn_fwd(
-        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(LSE), _ptr(workspace), nbytes,
-        _stream(stream)))
+    a = _Args(p)
+    a.call("dsa_dense_attn_fwd", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.io(V, "V"), a.out(O, "O"),
+           a.rows(LSE, "LSE"), *a.ws(workspace, False), stream=stream)
 
 
 def dense_attn_bwd(p: Problem, Q, K, V, O, dO, LSE, dQ, dK, dV, workspace, stream=None) -> None:
-    _check("dsa_dense_attn_bwd", library().dsa_dense_attn_bwd(
-        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(dQ), _ptr(dK), _ptr(dV),
-        _ptr(workspace), _nbytes(workspace), _stream(stream)))
+    a = _Args(p)
+    a.call("dsa_dense_attn_bwd", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.io(V, "V"), a.out(O, "O"),
+           a.io(dO, "dO"), a.rows(LSE, "LSE"), a.out(dQ, "dQ"), a.out(dK, "dK"), a.out(dV, "dV"), *a.ws(workspace),
+           stream=stream)
 
 
 def predictor_loss_grad(p: Problem, Q, K, Wq, Wk, loss, dWq, dWk, workspace, stream=None) -> None:
     """Stage-1 predictor training: loss [H] and its gradients dWq, dWk [H, d, r] (all fp32)."""
-    _check("dsa_predictor_loss_grad", library().dsa_predictor_loss_grad(
-        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(Wq), _ptr(Wk), _ptr(loss), _ptr(dWq), _ptr(dWk), _ptr(workspace),
-        _nbytes(workspace), _stream(stream)))
+    a = _Args(p)
+    a.call("dsa_predictor_loss_grad", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.weights(Wq, "Wq"),
+           a.weights(Wk, "Wk"), a.f32(loss, "loss", p.heads), a.weights(dWq, "dWq"), a.weights(dWk, "dWk"),
+           *a.ws(workspace), stream=stream)
 
 
 def choose_path(p: Problem, k_per_head: Sequence[int], min_sparsity: float = -1.0, max_sparse_bytes: int = 0) -> int:
     """PATH_SPARSE or PATH_DENSE for one layer (min_sparsity < 0: the library's measured default)."""
-    st = library().dsa_choose_path(ctypes.byref(p.c()), _kph(k_per_head), float(min_sparsity), int(max_sparse_bytes))
+    st = library().dsa_choose_path(ctypes.byref(p.c()), _kph(k_per_head, p.heads), float(min_sparsity),
+                                   int(max_sparse_bytes))
     if st < 0:
         _check("dsa_choose_path", st)
     return st
@@ -289,32 +401,43 @@ def choose_path(p: Problem, k_per_head: Sequence[int], min_sparsity: float = -1.
 
 def sparse_attn_bwd(p: Problem, Q, K, V, O, dO, LSE, idx, k_per_head, rev_ptr, rev_idx, dQ, dK, dV, workspace,
                     stream=None) -> None:
-    _check("dsa_sparse_attn_bwd", library().dsa_sparse_attn_bwd(
-        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(idx), _kph(k_per_head),
-        _ptr(rev_ptr), _ptr(rev_idx), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+    a = _Args(p)
+    kph = _kph(k_per_head, p.heads)
+    a.call("dsa_sparse_attn_bwd", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.io(V, "V"), a.out(O, "O"),
+           a.io(dO, "dO"), a.rows(LSE, "LSE"), a.idx(idx, k_per_head), kph, a.rev_ptr(rev_ptr),
+           a.idx(rev_idx, k_per_head, "rev_idx"), a.out(dQ, "dQ"), a.out(dK, "dK"), a.out(dV, "dV"),
+           *a.ws(workspace), stream=stream)
 
 
-def _nbytes(t) -> int:
-    return t.numel() * t.element_size()
+def sparse_attn_bwd_varlen(p: Problem, Q, K, V, O, dO, LSE, idx, cnt, k_per_head, rev_ptr, rev_idx, dQ, dK, dV,
+                           workspace, stream=None) -> None:
+    a = _Args(p)
+    kph = _kph(k_per_head, p.heads)
+    a.call("dsa_sparse_attn_bwd_varlen", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.io(V, "V"),
+           a.out(O, "O"), a.io(dO, "dO"), a.rows(LSE, "LSE"), a.idx(idx, k_per_head), a.cnt(cnt), kph,
+           a.rev_ptr(rev_ptr), a.idx(rev_idx, k_per_head, "rev_idx"), a.out(dQ, "dQ"), a.out(dK, "dK"),
+           a.out(dV, "dV"), *a.ws(workspace), stream=stream)
 
 
 def sparse_attn_bwd_preprocess(p: Problem, Q, K, V, O, dO, LSE, workspace, stream=None) -> None:
-    _check("dsa_sparse_attn_bwd_preprocess", library().dsa_sparse_attn_bwd_preprocess(
-        ctypes.byref(p.c()), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(workspace),
-        _nbytes(workspace), _stream(stream)))
+    a = _Args(p)
+    a.call("dsa_sparse_attn_bwd_preprocess", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.io(V, "V"),
+           a.out(O, "O"), a.io(dO, "dO"), a.rows(LSE, "LSE"), *a.ws(workspace), stream=stream)
 
 
 def sparse_attn_bwd_dkdv(p: Problem, k_per_head, rev_ptr, rev_idx, dK, dV, workspace, stream=None) -> None:
-    _check("dsa_sparse_attn_bwd_dkdv", library().dsa_sparse_attn_bwd_dkdv(
-        ctypes.byref(p.c()), _kph(k_per_head), _ptr(rev_ptr), _ptr(rev_idx), _ptr(dK), _ptr(dV), _ptr(workspace),
-        _nbytes(workspace), _stream(stream)))
+    a = _Args(p)
+    kph = _kph(k_per_head, p.heads)
+    a.call("dsa_sparse_attn_bwd_dkdv", ctypes.byref(p.c()), kph, a.rev_ptr(rev_ptr),
+           a.idx(rev_idx, k_per_head, "rev_idx"), a.out(dK, "dK"), a.out(dV, "dV"), *a.ws(workspace),
+           stream=stream)
 
 
 def sparse_attn_bwd_dq(p: Problem, idx, k_per_head, dQ, workspace, stream=None) -> None:
-    _check("dsa_sparse_attn_bwd_dq", library().dsa_sparse_attn_bwd_dq(
-        ctypes.byref(p.c()), _ptr(idx), _kph(k_per_head), _ptr(dQ), _ptr(workspace), _nbytes(workspace),
-        _stream(stream)))
+    a = _Args(p)
+    kph = _kph(k_per_head, p.heads)
+    a.call("dsa_sparse_attn_bwd_dq", ctypes.byref(p.c()), a.idx(idx, k_per_head), kph, a.out(dQ, "dQ"),
+           *a.ws(workspace), stream=stream)
 
 
 class SparseAttentionPlan:

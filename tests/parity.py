@@ -21,32 +21,12 @@ import torch
 import oracle
 import synth
 import dynamic_sparse_attention_qk_amd as dsa
+from synth.device import f64, problem_of, to_device  # noqa: F401 (re-exported for the tests)
 
 SCORE_TOL = 1e-3
 BF16_REL_L2 = 1e-2
 BF16_MAX_ABS = 2e-2
 F32_MAX_ABS = 1e-4
-
-
-def problem_of(w: synth.Workload, heads: Optional[int] = None) -> dsa.Problem:
-    return dsa.Problem(batch=w.batch, heads=w.heads if heads is None else heads, seq_len=w.seq_len,
-                       head_dim=w.head_dim, rank=w.rank, group=w.group,
-                       dtype=dsa.DSA_BF16 if w.dtype == "bf16" else dsa.DSA_F32)
-
-
-def to_device(a: Optional[np.ndarray], device="cuda") -> Optional[torch.Tensor]:
-    if a is None:
-        return None
-    t = torch.from_numpy(np.ascontiguousarray(a))
-    if a.dtype == np.uint16:
-        t = t.view(torch.int16).view(torch.bfloat16)
-    return t.to(device)
-
-
-def f64(a: np.ndarray) -> np.ndarray:
-    if a.dtype == np.uint16:
-        return synth.bf16_bits_to_f32(a).astype(np.float64)
-    return a.astype(np.float64)
 
 
 @dataclass

@@ -65,6 +65,7 @@ def library() -> ctypes.CDLL:
         lib.dsa_predict_block_scores.argtypes = [pp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp]
         lib.dsa_select_topk_blocks.argtypes = [pp, f32p, f32p, f32p, kph, i32p, i32p, i32p, f32p, vp,
                                                ctypes.c_size_t, vp]
+        lib.dsa_select_topk_blocks_noalloc.argtypes = [pp, f32p, f32p, f32p, kph, i32p, i32p, i32p, f32p, vp]
         lib.dsa_sparse_attn_fwd.argtypes = [pp, vp, vp, vp, i32p, kph, f32p, f32p, vp, ctypes.c_size_t, vp]
         lib.dsa_sparse_attn_bwd.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, kph, i32p, i32p, f32p, f32p,
                                             f32p, vp, ctypes.c_size_t, vp]
@@ -91,7 +92,8 @@ def library() -> ctypes.CDLL:
                      "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_fwd_split",
                      "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd", "dsa_choose_path",
                      "dsa_predictor_loss_grad", "dsa_select_coverage_blocks", "dsa_sparse_attn_fwd_varlen",
-                     "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks", "dsa_predict_block_scores_pooled"):
+                     "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks", "dsa_predict_block_scores_pooled",
+                     "dsa_select_topk_blocks_noalloc"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -102,7 +104,9 @@ EXPORTED = ("dsa_version", "dsa_status_string", "dsa_index_layout", "dsa_workspa
             "dsa_sparse_attn_bwd_preprocess", "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq",
             "dsa_sparse_attn_fwd_split", "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd",
             "dsa_choose_path", "dsa_predictor_loss_grad", "dsa_select_coverage_blocks", "dsa_sparse_attn_fwd_varlen",
-            "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks", "dsa_predict_block_scores_pooled")
+            "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks", "dsa_predict_block_scores_pooled",
+            "dsa_select_topk_blocks_noalloc")
+NOALLOC_SCRATCH_BYTES = 16 << 20  # DSA_NOALLOC_SCRATCH_BYTES
 SELECT_DIAGONAL = 1  # DSA_SELECT_DIAGONAL
 POOL_MAX, POOL_LSE = 1, 2  # DSA_POOL_MAX, DSA_POOL_LSE
 MAX_SPLIT = 64  # DSA_MAX_SPLIT
@@ -307,6 +311,17 @@ def select_topk_blocks(p: Problem, scores, qhat, khat, k_per_head, idx, rev_ptr,
     a.call("dsa_select_topk_blocks", ctypes.byref(p.c()), a.scores(scores), a.qhat(qhat), a.khat(khat), kph,
            a.idx(idx, k_per_head), a.rev_ptr(rev_ptr), a.idx(rev_idx, k_per_head, "rev_idx"),
            a.scores(scores_dump, "scores_dump"), *a.ws(workspace), stream=stream)
+
+
+def select_topk_blocks_noalloc(p: Problem, scores, qhat, khat, k_per_head, idx, rev_ptr, rev_idx, scores_dump=None,
+                               stream=None) -> None:
+    """select_topk_blocks without a workspace (the library's static per-GPU scratch; calls that overlap on one
+    GPU race)."""
+    a = _Args(p)
+    kph = _kph(k_per_head, p.heads)
+    a.call("dsa_select_topk_blocks_noalloc", ctypes.byref(p.c()), a.scores(scores), a.qhat(qhat), a.khat(khat), kph,
+           a.idx(idx, k_per_head), a.rev_ptr(rev_ptr), a.idx(rev_idx, k_per_head, "rev_idx"),
+           a.scores(scores_dump, "scores_dump"), stream=stream)
 
 
 def select_coverage_blocks(p: Problem, scores, qhat, khat, k_per_head, coverage: float, idx, cnt, rev_ptr, rev_idx,

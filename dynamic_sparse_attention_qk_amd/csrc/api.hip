@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "dsa.h"
 #include "launch.hpp"
 
@@ -141,6 +143,38 @@ size_t sparse_extra_bytes(const Shape& s, const HeadTable& ht) {
 
 }  // namespace
 
+// ---------------------------------------------------------------- the selection without a caller workspace
+//
+// For callers that cannot allocate: its scratch (the reverse index's counters and scatter buffer) is this
+// static device array, one per GPU the library runs on, held until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for the device symbol): the
+// device address comes from hipGetSymbolAddress, looked up once per device with that device current.
+static __device__ __align__(256) char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the device of `stream` (the current device for the null stream).
+static int scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DSA_ERR_HIP;
+  const int cur = dev;
+  if (stream && hipStreamGetDevice(stream, &dev) != hipSuccess) return DSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return DSA_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) hipSetDevice(cur);
+    if (e != hipSuccess || !ptr) return DSA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
 extern "C" {
 
 const char* dsa_version(void) { return "dsa-mi355x 0.1.0 (gfx950)"; }
@@ -155,6 +189,7 @@ const char* dsa_status_string(int status) {
     case DSA_ERR_UNSUPPORTED: return "problem outside the supported limits";
     case DSA_ERR_WORKSPACE: return "workspace missing or too small";
     case DSA_ERR_HIP: return "HIP runtime or launch error";
+    case DSA_ERR_SCRATCH_LIMIT: return "problem needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -205,37 +240,54 @@ int dsa_predict_block_scores(const dsa_problem* p, const void* Q, const void* K,
   return hip_status(e);
 }
 
+// Validates a selection call; fills the shape, head table, largest k and the diagonal group size.
+static int select_check(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,
+                        const int32_t* k_per_head, int32_t* idx, int flags, int32_t* rev_ptr, int32_t* rev_idx,
+                        float* scores_dump, Shape* s, HeadTable* ht, int* kmax, int* diag) {
+  int st = check_problem(p, s);
+  if (st) return st;
+  if ((st = check_heads(*s, k_per_head, ht, kmax))) return st;
+  if (flags & ~DSA_SELECT_DIAGONAL) return DSA_ERR_INVALID_ARG;
+  *diag = (flags & DSA_SELECT_DIAGONAL) ? s->G : 0;
+  for (int h = 0; *diag && h < s->H; ++h)
+    if (ht->k[h] < s->G / dsa::kBlock) return DSA_ERR_SHAPE;  // room for the forced blocks
+  if (!idx || !rev_ptr || !rev_idx) return DSA_ERR_INVALID_ARG;
+  if (!scores && (!qhat || !khat)) return DSA_ERR_INVALID_ARG;
+  if ((scores && !aligned16(scores)) || (!scores && (!aligned16(qhat) || !aligned16(khat))) || !aligned16(idx) ||
+      !aligned16(rev_ptr) || !aligned16(rev_idx) || (scores_dump && !aligned16(scores_dump)))
+    return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+// The selection's launches, scratch given as a select-layout workspace (counters, then the scatter buffer).
+static int select_launch(const Shape& s, const HeadTable& ht, int kmax, int diag, const float* scores,
+                         const float* qhat, const float* khat, int32_t* idx, int32_t* cnt, float coverage,
+                         int32_t* rev_ptr, int32_t* rev_idx, float* scores_dump, void* workspace, hipStream_t hs) {
+  const float tau = 1.0f / sqrtf((float)s.D);
+  int32_t* counters = static_cast<int32_t*>(workspace);
+  int32_t* scatter = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                                align256((size_t)s.B * s.H * s.NB * sizeof(int32_t)));
+  hipError_t e = dsa::launch_topk_select(s, scores, qhat, khat, idx, scores ? nullptr : scores_dump, ht, tau, kmax, hs,
+                                         cnt, coverage, diag);
+  if (e == hipSuccess) e = dsa::launch_reverse_index(s, idx, rev_ptr, rev_idx, counters, scatter, ht, kmax, hs);
+  return hip_status(e);
+}
+
 static int select_impl(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,
                        const int32_t* k_per_head, int32_t* idx, int32_t* cnt, float coverage, int flags,
                        int32_t* rev_ptr, int32_t* rev_idx, float* scores_dump, void* workspace,
                        size_t workspace_bytes, void* stream) {
   Shape s;
   HeadTable ht;
-  int kmax = 0;
-  int st = check_problem(p, &s);
+  int kmax = 0, diag = 0;
+  int st = select_check(p, scores, qhat, khat, k_per_head, idx, flags, rev_ptr, rev_idx, scores_dump, &s, &ht, &kmax,
+                        &diag);
   if (st) return st;
-  if ((st = check_heads(s, k_per_head, &ht, &kmax))) return st;
-  if (flags & ~DSA_SELECT_DIAGONAL) return DSA_ERR_INVALID_ARG;
-  const int diag = (flags & DSA_SELECT_DIAGONAL) ? s.G : 0;
-  for (int h = 0; diag && h < s.H; ++h)
-    if (ht.k[h] < s.G / dsa::kBlock) return DSA_ERR_SHAPE;  // room for the forced blocks
-  if (!idx || !rev_ptr || !rev_idx) return DSA_ERR_INVALID_ARG;
-  if (!scores && (!qhat || !khat)) return DSA_ERR_INVALID_ARG;
-  if ((scores && !aligned16(scores)) || (!scores && (!aligned16(qhat) || !aligned16(khat))) || !aligned16(idx) ||
-      !aligned16(rev_ptr) || !aligned16(rev_idx) || (scores_dump && !aligned16(scores_dump)))
-    return DSA_ERR_ALIGN;
   const size_t need = select_ws(s, ht);
   if (!workspace || workspace_bytes < need) return DSA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return DSA_ERR_ALIGN;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  const float tau = 1.0f / sqrtf((float)s.D);
-  int32_t* counters = static_cast<int32_t*>(workspace);
-  int32_t* scratch = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                                align256((size_t)s.B * s.H * s.NB * sizeof(int32_t)));
-  hipError_t e = dsa::launch_topk_select(s, scores, qhat, khat, idx, scores ? nullptr : scores_dump, ht, tau, kmax, hs,
-                                         cnt, coverage, diag);
-  if (e == hipSuccess) e = dsa::launch_reverse_index(s, idx, rev_ptr, rev_idx, counters, scratch, ht, kmax, hs);
-  return hip_status(e);
+  return select_launch(s, ht, kmax, diag, scores, qhat, khat, idx, cnt, coverage, rev_ptr, rev_idx, scores_dump,
+                       workspace, static_cast<hipStream_t>(stream));
 }
 
 int dsa_predict_block_scores_pooled(const dsa_problem* p, const void* Q, const void* K, const float* Wq,
@@ -260,6 +312,23 @@ int dsa_select_topk_blocks(const dsa_problem* p, const float* scores, const floa
                            float* scores_dump, void* workspace, size_t workspace_bytes, void* stream) {
   return select_impl(p, scores, qhat, khat, k_per_head, idx, nullptr, 1.0f, 0, rev_ptr, rev_idx, scores_dump,
                      workspace, workspace_bytes, stream);
+}
+
+int dsa_select_topk_blocks_noalloc(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,
+                                   const int32_t* k_per_head, int32_t* idx, int32_t* rev_ptr, int32_t* rev_idx,
+                                   float* scores_dump, void* stream) {
+  Shape s;
+  HeadTable ht;
+  int kmax = 0, diag = 0;
+  int st = select_check(p, scores, qhat, khat, k_per_head, idx, 0, rev_ptr, rev_idx, scores_dump, &s, &ht, &kmax,
+                        &diag);
+  if (st) return st;
+  if (select_ws(s, ht) > (size_t)DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_SCRATCH_LIMIT;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if ((st = scratch_for_stream(hs, &ws))) return st;
+  return select_launch(s, ht, kmax, diag, scores, qhat, khat, idx, nullptr, 1.0f, rev_ptr, rev_idx, scores_dump, ws,
+                       hs);
 }
 
 int dsa_select_blocks(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,

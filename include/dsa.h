@@ -21,7 +21,9 @@
  *    ascending order, starting at element row_base[b*H + h] + g * k_h, where
  *    row_base is given by dsa_index_layout.  rev_idx has the same total length.
  *  - All pointers except k_per_head are DEVICE pointers owned by the caller;
- *    the library never allocates, frees or retains memory.  k_per_head is a
+ *    the library never allocates, frees or retains memory (beside the one
+ *    static per-GPU scratch array of dsa_select_topk_blocks_noalloc, part of
+ *    the loaded code object).  k_per_head is a
  *    HOST array of H int32, read during the call only.  Device buffers must be
  *    16-byte aligned.  Scratch memory comes from a caller-provided workspace
  *    whose size dsa_workspace_bytes returns.
@@ -30,7 +32,7 @@
  *    synchronise.  Arguments are validated on the host before anything is
  *    launched; on error nothing is launched and a negative status is returned.
  *  - Calls on one stream may be issued from any thread; the library holds no
- *    mutable global state.
+ *    mutable global state other than that scratch array (see its call).
  *  - Limits: d in {64, 128}; rank r in {8, 16, 32, 64}; H <= 128;
  *    NB <= 8192 (N <= 524288); B*H*NG*max(k_h) < 2^31.
  */
@@ -52,7 +54,8 @@ typedef enum {
   DSA_ERR_ALIGN = -4,         /* a device pointer not 16-byte aligned */
   DSA_ERR_UNSUPPORTED = -5,   /* combination outside the limits above */
   DSA_ERR_WORKSPACE = -6,     /* workspace missing or too small */
-  DSA_ERR_HIP = -7            /* a HIP launch or runtime call failed */
+  DSA_ERR_HIP = -7,           /* a HIP launch or runtime call failed */
+  DSA_ERR_SCRATCH_LIMIT = -8  /* a call without a workspace needs more than its static scratch */
 } dsa_status;
 
 typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;
@@ -189,6 +192,28 @@ int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, cons
                         const int32_t* k_per_head, const int32_t* rev_ptr, const int32_t* rev_idx,
                         float* dQ, float* dK, float* dV, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* Bytes of the static per-GPU scratch of dsa_select_topk_blocks_noalloc. */
+#define DSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * dsa_select_topk_blocks_noalloc -- dsa_select_topk_blocks for callers that
+ * cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments (minus the workspace), same results bit for bit; no allocating
+ * call is made.  Its scratch (what DSA_WS_SELECT would hold) is a static
+ * device array of DSA_NOALLOC_SCRATCH_BYTES on each GPU the library runs
+ * on, kept until the process ends; problems whose DSA_WS_SELECT size exceeds
+ * it return DSA_ERR_SCRATCH_LIMIT before anything is launched (16 MiB holds
+ * the 57,600-token layer with k = 90 and the 131,072-token layer with
+ * k = 102, 24 heads each).  Every call on one GPU shares that array: calls
+ * that overlap on one GPU (on different streams, or from several threads
+ * without ordering) race and give undefined lists; calls ordered on one
+ * stream do not (the counters are cleared by a kernel at each call).
+ */
+int dsa_select_topk_blocks_noalloc(const dsa_problem* p, const float* scores, const float* qhat,
+                                   const float* khat, const int32_t* k_per_head, int32_t* idx,
+                                   int32_t* rev_ptr, int32_t* rev_idx, float* scores_dump, void* stream);
 
 /*
  * Selection by attention coverage (hi §2.A: the critical KV pairs are the

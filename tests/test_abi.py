@@ -323,3 +323,15 @@ def test_pooled_scores_validation():
     assert need == 2 * ((2 * 1024 * 16 * 2 + 255) // 256 * 256)       # fp16 projections of Q and K
     assert lib.dsa_predict_block_scores_pooled(pc, FAKE, FAKE, FAKE, FAKE, 1, FAKE, FAKE, need - 1, None) == -6
     assert lib.dsa_predict_block_scores_pooled(pc, FAKE, FAKE, FAKE, FAKE, 1, FAKE, None, big, None) == -6
+
+
+def test_noalloc_select_rejects_problems_beyond_its_scratch():
+    # 520,000 tokens, 24 heads, 840 kept blocks per row: the selection's scratch would be ~655 MB
+    lib = dsa.library()
+    p = dsa.Problem(batch=1, heads=24, seq_len=8125 * 64, head_dim=128, rank=32, group=64)
+    kph = dsa._kph([840] * 24)
+    st = lib.dsa_select_topk_blocks_noalloc(ctypes.byref(p.c()), FAKE, None, None, kph, FAKE, FAKE, FAKE, None, None)
+    assert st == -8 and "scratch" in dsa.status_string(st)
+    # and the usual validation comes first
+    assert lib.dsa_select_topk_blocks_noalloc(ctypes.byref(p.c()), None, None, None, kph, FAKE, FAKE, FAKE, None,
+                                              None) == -1

@@ -17,7 +17,7 @@ from .dsv_oracle import (
     predict_head, predictor_loss_grad, predictor_loss_grad_head, predictor_loss_head, reverse_index, reverse_list,
     select, select_row, sparsity, split_bounds, use_sparse, block_mass, select_coverage_row, select_coverage,
     diagonal_blocks, select_order, select_row_diag, select_coverage_row_diag, predict_head_pooled,
-    predict_head_pooled_groups, predict_head_pooled_rows,
+    predict_head_pooled_groups, predict_head_pooled_rows, select_rows, reverse_index_csr, dkdv_block_part,
 )
 
 __all__ = [
@@ -29,5 +29,5 @@ __all__ = [
     "dq_groups", "forward",
     "forward_head", "forward_split_head", "group_backward", "group_forward", "kept_keys", "merge_states",
     "partial_state", "pool_mean", "predict", "predict_head", "reverse_index", "reverse_list", "select",
-    "select_row", "split_bounds",
+    "select_row", "split_bounds", "select_rows", "reverse_index_csr", "dkdv_block_part",
 ]

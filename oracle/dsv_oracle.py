@@ -160,6 +160,19 @@ def select_row(scores_row: np.ndarray, k: int) -> np.ndarray:
     return np.sort(order[:k]).astype(np.int64)
 
 
+def select_rows(scores: np.ndarray, k: int) -> np.ndarray:
+    """select_row for every row of an [NG, NB] score matrix at once: [NG, k] ascending ids.
+
+    The same definition (order by -s, ties to the lowest id, keep the first k): a stable sort of -s keeps
+    equal scores in id order, and -0.0, +0.0 compare equal in it.
+    """
+    s = np.asarray(scores)
+    nb = s.shape[1]
+    assert 1 <= k <= nb
+    order = np.argsort(-s, axis=1, kind="stable")[:, :k]
+    return np.sort(order, axis=1).astype(np.int64)
+
+
 def diagonal_blocks(g: int, group: int, n_blocks: int, block: int = BLOCK) -> np.ndarray:
     """The KV blocks that hold query group g's own tokens."""
     return np.arange(g * group // block, min((g + 1) * group // block, n_blocks))
@@ -209,6 +222,19 @@ def reverse_index(idx_bh, n_blocks: int) -> List[np.ndarray]:
         for j in idx_bh[g]:
             lists[int(j)].append(g)
     return [np.asarray(l, dtype=np.int64) for l in lists]
+
+
+def reverse_index_csr(idx_bh: np.ndarray, n_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
+    """reverse_index of an [NG, k] list array in compressed form: (ptr [NB + 1], groups), block j's groups
+    being groups[ptr[j]:ptr[j + 1]], ascending.  The (block, group) pairs are read row by row, i.e. in
+    ascending group order, and stably sorted by block."""
+    a = np.asarray(idx_bh, dtype=np.int64)
+    ng, kk = a.shape
+    flat = a.ravel()
+    groups = np.repeat(np.arange(ng, dtype=np.int64), kk)
+    order = np.argsort(flat, kind="stable")
+    ptr = np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=n_blocks))]).astype(np.int64)
+    return ptr, groups[order]
 
 
 def reverse_list(idx_bh: np.ndarray, j: int) -> np.ndarray:
@@ -410,6 +436,23 @@ def dkdv_blocks(q, k, v, do, idx_bh, group, blocks, block=BLOCK) -> Dict[int, Tu
             dv += dv_p[pos:pos + block]
         out[j] = (dk, dv)
     return out
+
+
+def dkdv_block_part(q, k, v, do, idx_row, group, g, j, block=BLOCK) -> Tuple[np.ndarray, np.ndarray]:
+    """What query group g adds to the dK and dV rows of KV block j (a block of g's kept list ``idx_row``):
+    the group's softmax over all its kept keys gives LSE and O, hence D = dO . O; then on block j's keys only
+    P = exp(tau q k^T - LSE), dS = P (dO v^T - D), dK_j += tau dS^T Q_g, dV_j += P^T dO_g.  Summed over the
+    groups of block j's reverse list this is dkdv_blocks' result; one group at a time, so a caller can spread
+    the groups of a long list over threads."""
+    tau = 1.0 / np.sqrt(q.shape[1])
+    rows = slice(g * group, (g + 1) * group)
+    qg, dog = q[rows], do[rows]
+    og, lse, _ = group_forward(qg, k, v, kept_keys(idx_row, block))
+    dvec = (dog * og).sum(axis=1)
+    kj, vj = k[j * block:(j + 1) * block], v[j * block:(j + 1) * block]
+    p = np.exp(tau * (qg @ kj.T) - lse[:, None])
+    ds = p * (dog @ vj.T - dvec[:, None])
+    return tau * (ds.T @ qg), p.T @ dog
 
 
 # ----------------------------------------------------------------------------

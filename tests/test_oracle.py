@@ -80,6 +80,20 @@ def check_select_special():
     assert list(O.select_row(row1, 1)) == [1]
 
 
+def check_select_rows_vectorised(seed=31):
+    # the whole-matrix selection equals the Python sort row by row: heavy ties, +-0.0, tiny values, k = 1, NB
+    rng = _rng(seed)
+    vals = np.array([0.0, -0.0, 1.5, -2.0, 3.25, 1e-30, -1e-30, 7.0])
+    for trial in range(12):
+        ng, nb = int(rng.integers(1, 20)), int(rng.integers(1, 90))
+        s = rng.choice(vals, size=(ng, nb)) if trial % 2 else rng.standard_normal((ng, nb))
+        for kk in {1, nb, int(rng.integers(1, nb + 1))}:
+            got = O.select_rows(s, kk)
+            assert got.shape == (ng, kk)
+            for g in range(ng):
+                assert list(got[g]) == brute.topk_sorted(s[g], kk), (trial, g, kk)
+
+
 def check_duplicate_blocks_tie():
     q, k, _, _, wq, wk = _tiny(4, n=512, d=16)
     # blocks 1, 4 and 6 are bitwise copies of block 6's keys: their scores are equal
@@ -210,6 +224,34 @@ def check_reverse_index(seed=12):
     for j in range(nb):
         assert list(rev[j]) == [g for g in range(ng) if j in set(idx[g])]
         assert list(O.reverse_list(idx, j)) == list(rev[j])
+
+
+def check_reverse_index_csr(seed=32):
+    # the compressed reverse index equals a membership scan block by block, on ragged random lists
+    rng = _rng(seed)
+    for nb, ng, kk in ((13, 9, 4), (40, 25, 1), (7, 30, 7), (64, 3, 20)):
+        idx = np.stack([np.sort(rng.choice(nb, kk, replace=False)) for _ in range(ng)])
+        ptr, groups = O.reverse_index_csr(idx, nb)
+        assert ptr[0] == 0 and ptr[-1] == idx.size and (np.diff(ptr) >= 0).all()
+        for j in range(nb):
+            assert list(groups[ptr[j]:ptr[j + 1]]) == [g for g in range(ng) if j in set(idx[g].tolist())]
+
+
+def check_dkdv_block_part(seed=33, n=768, group=64, kk=4):
+    # the per-group parts of a block, summed over its reverse list, equal the full backward's dK, dV rows
+    q, k, v, do, wq, wk = _tiny(seed, n=n)
+    _, _, s = O.predict_head(q, k, wq, wk, group)
+    idx = _sel(s, kk)
+    _, dk, dv = O.backward_head(q, k, v, do, idx, group)
+    ptr, groups = O.reverse_index_csr(idx, n // 64)
+    for j in range(n // 64):
+        gk, gv = np.zeros((64, 16)), np.zeros((64, 16))
+        for g in groups[ptr[j]:ptr[j + 1]]:
+            pk, pv = O.dkdv_block_part(q, k, v, do, idx[g], group, int(g), j)
+            gk += pk
+            gv += pv
+        np.testing.assert_allclose(gk, dk[j * 64:(j + 1) * 64], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(gv, dv[j * 64:(j + 1) * 64], rtol=1e-11, atol=1e-12)
 
 
 def check_batched_api(seed=13):
@@ -577,7 +619,8 @@ ALL_CHECKS = [
     check_split_merge_equals_unsplit, check_partial_states_brute, check_merge_algebra, check_dense_sdpa,
     check_dense_brute, check_dense_closed_forms, check_dense_sampled, check_dispatch_rule,
     check_pred_loss_brute, check_pred_loss_closed_forms, check_coverage_brute, check_coverage_closed_forms,
-    check_ragged_attention_brute, check_diagonal_brute, check_pooled_scores_brute,
+    check_ragged_attention_brute, check_diagonal_brute, check_pooled_scores_brute, check_select_rows_vectorised,
+    check_reverse_index_csr, check_dkdv_block_part,
 ]
 
 
@@ -832,3 +875,41 @@ def test_mutation_pooled_lse_without_mean(monkeypatch):
         out = orig(q, k, wq, wk, group, pooling, block)
         return out + math.log(group * block) if pooling == "lse" else out
     assert _fails_some_pin(monkeypatch, "predict_head_pooled", bad, [check_pooled_scores_brute])
+
+
+def test_mutation_select_rows_ties_to_highest_id(monkeypatch):
+    def bad(scores, k):
+        s = np.asarray(scores)[:, ::-1]
+        order = np.argsort(-s, axis=1, kind="stable")[:, :k]
+        return np.sort(s.shape[1] - 1 - order, axis=1)
+    monkeypatch.setattr(O, "select_rows", bad)
+    with pytest.raises(AssertionError):
+        check_select_rows_vectorised()
+
+
+def test_mutation_reverse_csr_groups_unsorted(monkeypatch):
+    real = O.reverse_index_csr
+
+    def bad(idx_bh, n_blocks):
+        ptr, groups = real(idx_bh, n_blocks)
+        out = groups.copy()
+        for j in range(n_blocks):
+            out[ptr[j]:ptr[j + 1]] = out[ptr[j]:ptr[j + 1]][::-1]
+        return ptr, out
+    monkeypatch.setattr(O, "reverse_index_csr", bad)
+    with pytest.raises(AssertionError):
+        check_reverse_index_csr()
+
+
+def test_mutation_block_part_without_D(monkeypatch):
+    def bad(q, k, v, do, idx_row, group, g, j, block=64):
+        tau = 1.0 / np.sqrt(q.shape[1])
+        rows = slice(g * group, (g + 1) * group)
+        _, lse, _ = O.group_forward(q[rows], k, v, O.kept_keys(idx_row, block))
+        kj, vj = k[j * block:(j + 1) * block], v[j * block:(j + 1) * block]
+        p = np.exp(tau * (q[rows] @ kj.T) - lse[:, None])
+        ds = p * (do[rows] @ vj.T)
+        return tau * (ds.T @ q[rows]), p.T @ do[rows]
+    monkeypatch.setattr(O, "dkdv_block_part", bad)
+    with pytest.raises(AssertionError):
+        check_dkdv_block_part()

@@ -451,7 +451,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
       }
     // P = exp2(S tau log2 e), dS = P (dP - D); A operands per key half kk:
     // element e' <-> query 32*qh + 16*(e'/4) + 4*q4 + e'%4
-    f16x8 pa[2], dh[2], dl[2];
+    // P and dS both enter their products as an fp16 hi + lo pair (about 22 significant bits): dV sums P
+    // against dO and dK sums a cancelling dS against clustered Q, and one fp16 rounding of either
+    // (2^-12 relative) leaves errors of a few 1e-2 on gradients of magnitude 100-200
+    f16x8 ph[2], pl[2], dh[2], dl[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
@@ -460,8 +463,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
         for (int e = 0; e < 4; ++e) {
           const float p = __builtin_amdgcn_exp2f(s[kk][qq][e] * scale_log2);
           const float ds = p * dp[kk][qq][e];
-          const _Float16 hv = (_Float16)ds;
-          pa[kk][4 * qq + e] = (_Float16)p;
+          const _Float16 hp = (_Float16)p, hv = (_Float16)ds;
+          ph[kk][4 * qq + e] = hp;
+          pl[kk][4 * qq + e] = (_Float16)(p - (float)hp);
           dh[kk][4 * qq + e] = hv;
           dl[kk][4 * qq + e] = (_Float16)(ds - (float)hv);
         }
@@ -473,7 +477,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
       const f16x8 qb = join_f16(lds_read_tr16(q), lds_read_tr16(q + 16 * RB));
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        dv[kk][c] = mfma16h(pa[kk], ob, dv[kk][c]);
+        dv[kk][c] = mfma16h(ph[kk], ob, dv[kk][c]);
+        dv[kk][c] = mfma16h(pl[kk], ob, dv[kk][c]);
         dk[kk][c] = mfma16h(dh[kk], qb, dk[kk][c]);
         dk[kk][c] = mfma16h(dl[kk], qb, dk[kk][c]);
       }

@@ -7,6 +7,7 @@ cheap and on seeded samples of rows and blocks for the float outputs.
 """
 from __future__ import annotations
 
+import functools
 import json
 
 import numpy as np
@@ -188,64 +189,29 @@ def test_unkept_blocks_get_zero_gradient():
     P.assert_float_parity(rep, bf16=True)
 
 
-# ------------------------------------------------------------------ full-size workloads (sampled)
+# ------------------------------------------------------------------ full-size workloads, whole
 
-def _sample_groups(rng, ng, n):
-    return sorted(set([0, ng - 1] + list(rng.choice(ng, size=n, replace=False))))
-
-
-def _full(cid, heads=None, n_groups=4, dkdv_heads=(0, 1), short_lists=False):
+@functools.lru_cache(maxsize=1)
+def _full_run(cid):
+    """The workload's inputs and one GPU pass (predict, select, fwd, bwd), kept for the tests of that workload."""
     w = synth.workload(cid)
-    print(f"CASE full workload {cid} ({w.name}) N={w.seq_len} heads={heads or w.heads}", flush=True)
-    inp = synth.generate(w, heads=heads)
-    stream_mode = w.streamed
-    run = P.run_gpu(inp, materialise=not stream_mode, dump=stream_mode)
-    p = run.plan.p
-    rng = np.random.default_rng(1000 + cid)
+    print(f"CASE full workload {cid} ({w.name}) N={w.seq_len} heads={w.heads}", flush=True)
+    inp = synth.generate(w, threads=16)
+    run = P.run_gpu(inp, materialise=not w.streamed, dump=w.streamed, scores_on_device=True)
+    return w, run
+
+
+@pytest.mark.parametrize("cid,heads", [(2, None), (3, range(0, 12)), (3, range(12, 24)), (4, range(0, 12)),
+                                       (4, range(12, 24))],
+                         ids=["w2_all_heads", "w3_heads_0_11", "w3_heads_12_23", "w4_heads_0_11", "w4_heads_12_23"])
+def test_full_workload_every_element(cid, heads):
+    """Every row's scores, kept ids and reverse lists, and every element of O, LSE (and dQ, dK, dV for the
+    training workloads) of the listed heads, against the oracle run with the GPU's lists."""
+    w, run = _full_run(cid)
+    hl = None if heads is None else list(heads)
     rep = P.Report()
-    groups = {h: _sample_groups(rng, p.n_groups, n_groups) for h in range(p.heads)}
-    rows = None if not stream_mode else _sample_groups(rng, p.n_groups, 64)
-    for h in range(p.heads):
-        revb = list(rng.choice(p.n_blocks, size=8, replace=False))
-        P.check_predict_select(run, rep, heads=[h], rows=rows if rows is not None else range(p.n_groups),
-                               rev_blocks=revb)
-    P.check_forward(run, rep, groups=groups)
-    if w.backward:
-        blocks = {}
-        for h in dkdv_heads:
-            lens = np.diff(run.host["rev_ptr"][h])
-            order = np.argsort(lens, kind="stable")
-            picks = {int(order[0]), int(order[len(order) // 4])}
-            if not short_lists:
-                picks |= {int(order[-1]), int(rng.integers(p.n_blocks))}
-            blocks[h] = sorted(picks)
-        P.check_backward(run, rep, groups={h: groups[h][:2] for h in range(p.heads)}, blocks=blocks)
-    _print(f"full_{cid}", rep, {"k_per_head": [int(x) for x in inp.k_per_head]})
-    return rep
-
-
-def test_full_workload_2():
-    rep = _full(2)
-    P.assert_float_parity(rep, bf16=True)
-
-
-def test_full_workload_3():
-    rep = _full(3)
-    P.assert_float_parity(rep, bf16=True)
-
-
-def test_full_workload_4():
-    rep = _full(4, heads=list(range(0, 24, 3)))
-    P.assert_float_parity(rep, bf16=True)
-
-
-def test_full_workload_5_heads_subset():
-    # the heaviest, the lightest and one middle head at the full 520k-token shape;
-    # dK/dV sampled on the lightest head's shorter reverse lists (each costs a
-    # full float64 group forward per listed group)
-    kph = synth.per_head_k(synth.workload(5))
-    order = np.argsort(kph)
-    heads = sorted({int(order[-1]), int(order[0]), int(order[len(order) // 2])})
-    light = heads.index(int(order[0]))
-    rep = _full(5, heads=heads, n_groups=2, dkdv_heads=(light,), short_lists=True)
+    P.check_selection_full(run, rep, heads=hl)
+    P.check_attention_full(run, rep, heads=hl)
+    _print(f"full_{cid}" + ("" if hl is None else f"_heads_{hl[0]}_{hl[-1]}"), rep,
+           {"k_per_head": sorted(set(int(x) for x in run.inp.k_per_head)), "every_element": True})
     P.assert_float_parity(rep, bf16=True)

@@ -408,11 +408,14 @@ def main():
         plan.forward(Q, K, V, stream)
         rec(3)
         if backward:
-            dsa.sparse_attn_bwd_preprocess(p, Q, K, V, plan.O, dO, plan.LSE, plan.ws_bwd, stream)
+            # the forward wrote its scaled fp16 copy of V into the backward's workspace (plan.reuse_v)
+            dsa.sparse_attn_bwd_preprocess(p, Q, K, V, plan.O, dO, plan.LSE, plan.ws_bwd, stream,
+                                           flags=dsa.BWD_V_FROM_FORWARD if plan.reuse_v else 0)
             rec(4)
-            dsa.sparse_attn_bwd_dkdv(p, kph, plan.rev_ptr, plan.rev_idx, plan.dK, plan.dV, plan.ws_bwd, stream)
+            dsa.sparse_attn_bwd_dkdv(p, Q, K, V, dO, kph, plan.rev_ptr, plan.rev_idx, plan.dK, plan.dV, plan.ws_bwd,
+                                     stream)
             rec(5)
-            dsa.sparse_attn_bwd_dq(p, plan.idx, kph, plan.dQ, plan.ws_bwd, stream)
+            dsa.sparse_attn_bwd_dq(p, Q, dO, plan.idx, kph, plan.dQ, plan.ws_bwd, stream)
             rec(6)
 
     # first pass checked on the host: every kept-block id in range before the attention kernels read them

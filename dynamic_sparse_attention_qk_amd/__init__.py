@@ -70,9 +70,12 @@ def library() -> ctypes.CDLL:
         lib.dsa_sparse_attn_bwd.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, kph, i32p, i32p, f32p, f32p,
                                             f32p, vp, ctypes.c_size_t, vp]
         sz = ctypes.c_size_t
+        lib.dsa_sparse_attn_bwd_ex.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, kph, i32p, i32p, f32p, f32p,
+                                               f32p, ctypes.c_int, vp, ctypes.c_size_t, vp]
         lib.dsa_sparse_attn_bwd_preprocess.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, vp, sz, vp]
-        lib.dsa_sparse_attn_bwd_dkdv.argtypes = [pp, kph, i32p, i32p, f32p, f32p, vp, sz, vp]
-        lib.dsa_sparse_attn_bwd_dq.argtypes = [pp, i32p, kph, f32p, vp, sz, vp]
+        lib.dsa_sparse_attn_bwd_preprocess_ex.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, ctypes.c_int, vp, sz, vp]
+        lib.dsa_sparse_attn_bwd_dkdv.argtypes = [pp, vp, vp, vp, vp, kph, i32p, i32p, f32p, f32p, vp, sz, vp]
+        lib.dsa_sparse_attn_bwd_dq.argtypes = [pp, vp, vp, i32p, kph, f32p, vp, sz, vp]
         lib.dsa_sparse_attn_fwd_split.argtypes = [pp, vp, vp, vp, i32p, kph, ctypes.c_int, f32p, f32p, vp, sz, vp]
         lib.dsa_attn_merge.argtypes = [pp, ctypes.c_int, f32p, f32p, f32p, f32p, vp]
         lib.dsa_dense_attn_fwd.argtypes = [pp, vp, vp, vp, f32p, f32p, vp, sz, vp]
@@ -93,7 +96,8 @@ def library() -> ctypes.CDLL:
                      "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd", "dsa_choose_path",
                      "dsa_predictor_loss_grad", "dsa_select_coverage_blocks", "dsa_sparse_attn_fwd_varlen",
                      "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks", "dsa_predict_block_scores_pooled",
-                     "dsa_select_topk_blocks_noalloc"):
+                     "dsa_select_topk_blocks_noalloc", "dsa_sparse_attn_bwd_ex",
+                     "dsa_sparse_attn_bwd_preprocess_ex"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -105,7 +109,8 @@ EXPORTED = ("dsa_version", "dsa_status_string", "dsa_index_layout", "dsa_workspa
             "dsa_sparse_attn_fwd_split", "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd",
             "dsa_choose_path", "dsa_predictor_loss_grad", "dsa_select_coverage_blocks", "dsa_sparse_attn_fwd_varlen",
             "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks", "dsa_predict_block_scores_pooled",
-            "dsa_select_topk_blocks_noalloc")
+            "dsa_select_topk_blocks_noalloc", "dsa_sparse_attn_bwd_ex", "dsa_sparse_attn_bwd_preprocess_ex")
+BWD_V_FROM_FORWARD = 1  # DSA_BWD_V_FROM_FORWARD
 NOALLOC_SCRATCH_BYTES = 16 << 20  # DSA_NOALLOC_SCRATCH_BYTES
 SELECT_DIAGONAL = 1  # DSA_SELECT_DIAGONAL
 POOL_MAX, POOL_LSE = 1, 2  # DSA_POOL_MAX, DSA_POOL_LSE
@@ -415,13 +420,17 @@ def choose_path(p: Problem, k_per_head: Sequence[int], min_sparsity: float = -1.
 
 
 def sparse_attn_bwd(p: Problem, Q, K, V, O, dO, LSE, idx, k_per_head, rev_ptr, rev_idx, dQ, dK, dV, workspace,
-                    stream=None) -> None:
+                    stream=None, flags: int = 0) -> None:
+    """flags: BWD_V_FROM_FORWARD when ``workspace`` went to the forward of these inputs (V's copy reused)."""
     a = _Args(p)
     kph = _kph(k_per_head, p.heads)
-    a.call("dsa_sparse_attn_bwd", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.io(V, "V"), a.out(O, "O"),
-           a.io(dO, "dO"), a.rows(LSE, "LSE"), a.idx(idx, k_per_head), kph, a.rev_ptr(rev_ptr),
-           a.idx(rev_idx, k_per_head, "rev_idx"), a.out(dQ, "dQ"), a.out(dK, "dK"), a.out(dV, "dV"),
-           *a.ws(workspace), stream=stream)
+    args = [ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.io(V, "V"), a.out(O, "O"), a.io(dO, "dO"),
+            a.rows(LSE, "LSE"), a.idx(idx, k_per_head), kph, a.rev_ptr(rev_ptr), a.idx(rev_idx, k_per_head, "rev_idx"),
+            a.out(dQ, "dQ"), a.out(dK, "dK"), a.out(dV, "dV")]
+    if flags:
+        a.call("dsa_sparse_attn_bwd_ex", *args, int(flags), *a.ws(workspace), stream=stream)
+    else:
+        a.call("dsa_sparse_attn_bwd", *args, *a.ws(workspace), stream=stream)
 
 
 def sparse_attn_bwd_varlen(p: Problem, Q, K, V, O, dO, LSE, idx, cnt, k_per_head, rev_ptr, rev_idx, dQ, dK, dV,
@@ -434,34 +443,42 @@ def sparse_attn_bwd_varlen(p: Problem, Q, K, V, O, dO, LSE, idx, cnt, k_per_head
            a.out(dV, "dV"), *a.ws(workspace), stream=stream)
 
 
-def sparse_attn_bwd_preprocess(p: Problem, Q, K, V, O, dO, LSE, workspace, stream=None) -> None:
+def sparse_attn_bwd_preprocess(p: Problem, Q, K, V, O, dO, LSE, workspace, stream=None, flags: int = 0) -> None:
     a = _Args(p)
-    a.call("dsa_sparse_attn_bwd_preprocess", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.io(V, "V"),
-           a.out(O, "O"), a.io(dO, "dO"), a.rows(LSE, "LSE"), *a.ws(workspace), stream=stream)
+    args = [ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.io(V, "V"), a.out(O, "O"), a.io(dO, "dO"),
+            a.rows(LSE, "LSE")]
+    if flags:
+        a.call("dsa_sparse_attn_bwd_preprocess_ex", *args, int(flags), *a.ws(workspace), stream=stream)
+    else:
+        a.call("dsa_sparse_attn_bwd_preprocess", *args, *a.ws(workspace), stream=stream)
 
 
-def sparse_attn_bwd_dkdv(p: Problem, k_per_head, rev_ptr, rev_idx, dK, dV, workspace, stream=None) -> None:
-    a = _Args(p)
-    kph = _kph(k_per_head, p.heads)
-    a.call("dsa_sparse_attn_bwd_dkdv", ctypes.byref(p.c()), kph, a.rev_ptr(rev_ptr),
-           a.idx(rev_idx, k_per_head, "rev_idx"), a.out(dK, "dK"), a.out(dV, "dV"), *a.ws(workspace),
-           stream=stream)
-
-
-def sparse_attn_bwd_dq(p: Problem, idx, k_per_head, dQ, workspace, stream=None) -> None:
+def sparse_attn_bwd_dkdv(p: Problem, Q, K, V, dO, k_per_head, rev_ptr, rev_idx, dK, dV, workspace,
+                         stream=None) -> None:
     a = _Args(p)
     kph = _kph(k_per_head, p.heads)
-    a.call("dsa_sparse_attn_bwd_dq", ctypes.byref(p.c()), a.idx(idx, k_per_head), kph, a.out(dQ, "dQ"),
-           *a.ws(workspace), stream=stream)
+    a.call("dsa_sparse_attn_bwd_dkdv", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(K, "K"), a.io(V, "V"),
+           a.io(dO, "dO"), kph, a.rev_ptr(rev_ptr), a.idx(rev_idx, k_per_head, "rev_idx"), a.out(dK, "dK"),
+           a.out(dV, "dV"), *a.ws(workspace), stream=stream)
+
+
+def sparse_attn_bwd_dq(p: Problem, Q, dO, idx, k_per_head, dQ, workspace, stream=None) -> None:
+    a = _Args(p)
+    kph = _kph(k_per_head, p.heads)
+    a.call("dsa_sparse_attn_bwd_dq", ctypes.byref(p.c()), a.io(Q, "Q"), a.io(dO, "dO"), a.idx(idx, k_per_head), kph,
+           a.out(dQ, "dQ"), *a.ws(workspace), stream=stream)
 
 
 class SparseAttentionPlan:
     """Outputs and workspaces of one problem, allocated once with torch, plus the calls in order."""
 
     def __init__(self, p: Problem, k_per_head: Sequence[int], device="cuda", materialise_scores: bool = True,
-                 backward: bool = True, coverage: Optional[float] = None, select_flags: int = 0):
+                 backward: bool = True, coverage: Optional[float] = None, select_flags: int = 0,
+                 reuse_v: bool = True):
         """coverage: select by attention coverage (k_per_head is then each row's capacity) and run the
-        per-row-count forward and backward; select_flags: SELECT_DIAGONAL keeps each group's own blocks."""
+        per-row-count forward and backward; select_flags: SELECT_DIAGONAL keeps each group's own blocks;
+        reuse_v (training plans, bf16): the forward writes its scaled fp16 copy of V into the backward's
+        workspace and the backward reuses it (BWD_V_FROM_FORWARD) instead of converting V again."""
         self.p = p
         self.k_per_head = [int(x) for x in k_per_head]
         self.coverage = coverage
@@ -485,12 +502,15 @@ class SparseAttentionPlan:
                                   device=device)
         self.O = torch.empty(B, H, N, D, **f32)
         self.LSE = torch.empty(B, H, N, **f32)
+        self.reuse_v = bool(reuse_v and backward and p.dtype == DSA_BF16 and coverage is None)
         if backward:
             self.dQ = torch.empty(B, H, N, D, **f32)
             self.dK = torch.empty(B, H, N, D, **f32)
             self.dV = torch.empty(B, H, N, D, **f32)
             self.ws_bwd = torch.empty(workspace_bytes(p, self.k_per_head, DSA_WS_BWD), dtype=torch.uint8,
                                       device=device)
+            if self.reuse_v:
+                self.ws_fwd = self.ws_bwd   # the forward's layout is the start of the backward's
 
     def predict(self, Q, K, Wq, Wk, stream=None):
         predict_block_scores(self.p, Q, K, Wq, Wk, self.qhat, self.khat, self.scores, stream)
@@ -521,16 +541,18 @@ class SparseAttentionPlan:
                                    self.rev_ptr, self.rev_idx, self.dQ, self.dK, self.dV, self.ws_bwd, stream)
         else:
             sparse_attn_bwd(self.p, Q, K, V, self.O, dO, self.LSE, self.idx, self.k_per_head, self.rev_ptr,
-                            self.rev_idx, self.dQ, self.dK, self.dV, self.ws_bwd, stream)
+                            self.rev_idx, self.dQ, self.dK, self.dV, self.ws_bwd, stream,
+                            flags=BWD_V_FROM_FORWARD if self.reuse_v else 0)
 
     def backward_stages(self, Q, K, V, dO, stream=None):
         """The backward as its three stages (same result as backward()); top-k selection only."""
         if self.cnt is not None:
             raise ValueError("the staged backward takes no per-row counts: use backward()")
-        sparse_attn_bwd_preprocess(self.p, Q, K, V, self.O, dO, self.LSE, self.ws_bwd, stream)
-        sparse_attn_bwd_dkdv(self.p, self.k_per_head, self.rev_ptr, self.rev_idx, self.dK, self.dV, self.ws_bwd,
-                             stream)
-        sparse_attn_bwd_dq(self.p, self.idx, self.k_per_head, self.dQ, self.ws_bwd, stream)
+        sparse_attn_bwd_preprocess(self.p, Q, K, V, self.O, dO, self.LSE, self.ws_bwd, stream,
+                                   flags=BWD_V_FROM_FORWARD if self.reuse_v else 0)
+        sparse_attn_bwd_dkdv(self.p, Q, K, V, dO, self.k_per_head, self.rev_ptr, self.rev_idx, self.dK, self.dV,
+                             self.ws_bwd, stream)
+        sparse_attn_bwd_dq(self.p, Q, dO, self.idx, self.k_per_head, self.dQ, self.ws_bwd, stream)
 
     def step(self, Q, K, V, Wq, Wk, dO=None, stream=None):
         """predict -> select -> fwd (-> bwd): one pass of the whole hot path."""

@@ -66,22 +66,42 @@ size_t select_ws(const Shape& s, const HeadTable& ht) {
   return align256((size_t)s.B * s.H * s.NB * sizeof(int32_t)) + align256((size_t)s.B * s.NG * ht.ksum * sizeof(int32_t));
 }
 
-size_t bwd_row_bytes(const Shape& s) { return align256((size_t)s.B * s.H * s.N * sizeof(float)); }
+// The forward's workspace (bf16 inputs) and the start of the backward's: the exponent table of the scaled
+// fp16 copies [4][B*H] int32, the partial maxima [4][B*H][kAmaxChunks] uint32, the copy of V.
+size_t ex_bytes(const Shape& s) { return align256((size_t)4 * s.B * s.H * sizeof(int32_t)); }
+size_t part_bytes(const Shape& s) { return align256((size_t)4 * s.B * s.H * dsa::kAmaxChunks * sizeof(uint32_t)); }
 size_t bwd_tensor_bytes(const Shape& s) { return align256((size_t)s.B * s.H * s.N * s.D * 2); }
+size_t fwd_prefix_bytes(const Shape& s) { return ex_bytes(s) + part_bytes(s) + bwd_tensor_bytes(s); }
+
+// forward: the prefix above (bf16 inputs only)
+size_t fwd_ws(const Shape& s) { return s.bf16 ? fwd_prefix_bytes(s) : 0; }
+
+dsa::FwdWork fwd_work(const Shape& s, void* ws) {
+  char* p = static_cast<char*>(ws);
+  dsa::FwdWork w;
+  w.ex = reinterpret_cast<int32_t*>(p);
+  w.part = reinterpret_cast<uint32_t*>(p + ex_bytes(s));
+  w.V16 = reinterpret_cast<uint16_t*>(p + ex_bytes(s) + part_bytes(s));
+  return w;
+}
+
+size_t bwd_row_bytes(const Shape& s) { return align256((size_t)s.B * s.H * s.N * sizeof(float)); }
 size_t bwd_order_bytes(const Shape& s) { return align256((size_t)s.B * s.H * s.NB * sizeof(int32_t)); }
-size_t bwd_ws(const Shape& s) { return 2 * bwd_row_bytes(s) + 4 * bwd_tensor_bytes(s) + bwd_order_bytes(s); }
+// the forward's part, then D, -LSE*log2(e), the scaled fp16 copy of K and the dK/dV task order
+size_t bwd_ws(const Shape& s) { return fwd_prefix_bytes(s) + 2 * bwd_row_bytes(s) + bwd_tensor_bytes(s) + bwd_order_bytes(s); }
 
 dsa::BwdWork bwd_work(const Shape& s, void* ws) {
-  char* p = static_cast<char*>(ws);
+  const dsa::FwdWork f = fwd_work(s, ws);
+  char* p = static_cast<char*>(ws) + fwd_prefix_bytes(s);
   dsa::BwdWork w;
+  w.ex = f.ex;
+  w.part = f.part;
+  w.V16 = f.V16;
   w.Dvec = reinterpret_cast<float*>(p);
   w.nl2 = reinterpret_cast<float*>(p + bwd_row_bytes(s));
   char* t = p + 2 * bwd_row_bytes(s);
-  w.Q16 = reinterpret_cast<uint16_t*>(t);
-  w.K16 = reinterpret_cast<uint16_t*>(t + bwd_tensor_bytes(s));
-  w.V16 = reinterpret_cast<uint16_t*>(t + 2 * bwd_tensor_bytes(s));
-  w.dO16 = reinterpret_cast<uint16_t*>(t + 3 * bwd_tensor_bytes(s));
-  w.order = reinterpret_cast<int32_t*>(t + 4 * bwd_tensor_bytes(s));
+  w.K16 = reinterpret_cast<uint16_t*>(t);
+  w.order = reinterpret_cast<int32_t*>(t + bwd_tensor_bytes(s));
   return w;
 }
 
@@ -117,9 +137,6 @@ dsa::PredWork pred_work(const Shape& s, void* ws) {
 
 // pooled scores: fp16 token projections of Q and K
 size_t pooled_ws(const Shape& s) { return 2 * align256((size_t)s.B * s.H * s.N * s.R * 2); }
-
-// forward: an fp16 copy of V (bf16 inputs only)
-size_t fwd_ws(const Shape& s) { return s.bf16 ? align256((size_t)s.B * s.H * s.N * s.D * 2) : 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_HIP; }
 
@@ -369,7 +386,7 @@ static int fwd_impl(const dsa_problem* p, const void* Q, const void* K, const vo
   const size_t need = fwd_ws(s);
   if (need && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
   if (need && !aligned16(workspace)) return DSA_ERR_ALIGN;
-  return hip_status(dsa::launch_attn_fwd(s, Q, K, V, idx, O, LSE, static_cast<uint16_t*>(workspace), ht, 1,
+  return hip_status(dsa::launch_attn_fwd(s, Q, K, V, idx, O, LSE, fwd_work(s, workspace), ht, 1,
                                          static_cast<hipStream_t>(stream), cnt));
 }
 
@@ -403,8 +420,8 @@ int dsa_sparse_attn_fwd_split(const dsa_problem* p, const void* Q, const void* K
   const size_t need = fwd_ws(s);
   if (need && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
   if (need && !aligned16(workspace)) return DSA_ERR_ALIGN;
-  return hip_status(dsa::launch_attn_fwd(s, Q, K, V, idx, O_part, LSE_part, static_cast<uint16_t*>(workspace), ht,
-                                         n_split, static_cast<hipStream_t>(stream)));
+  return hip_status(dsa::launch_attn_fwd(s, Q, K, V, idx, O_part, LSE_part, fwd_work(s, workspace), ht, n_split,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int dsa_attn_merge(const dsa_problem* p, int n_parts, const float* O_part, const float* LSE_part, float* O,
@@ -430,55 +447,66 @@ static int check_ws(const Shape& s, const void* workspace, size_t workspace_byte
   return aligned16(workspace) ? DSA_OK : DSA_ERR_ALIGN;
 }
 
-int dsa_sparse_attn_bwd_preprocess(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
-                                   const void* dO, const float* LSE, void* workspace, size_t workspace_bytes,
-                                   void* stream) {
+int dsa_sparse_attn_bwd_preprocess_ex(const dsa_problem* p, const void* Q, const void* K, const void* V,
+                                      const float* O, const void* dO, const float* LSE, int flags, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
   Shape s;
   int st = check_problem(p, &s);
   if (st) return st;
   if (!s.bf16) return DSA_ERR_DTYPE;
+  if (flags & ~DSA_BWD_V_FROM_FORWARD) return DSA_ERR_INVALID_ARG;
   if (!Q || !K || !V || !O || !dO || !LSE) return DSA_ERR_INVALID_ARG;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(LSE))
     return DSA_ERR_ALIGN;
   if ((st = check_ws(s, workspace, workspace_bytes))) return st;
   return hip_status(dsa::launch_bwd_pre(s, Q, K, V, O, dO, LSE, bwd_work(s, workspace),
-                                        static_cast<hipStream_t>(stream)));
+                                        (flags & DSA_BWD_V_FROM_FORWARD) != 0, static_cast<hipStream_t>(stream)));
 }
 
-int dsa_sparse_attn_bwd_dkdv(const dsa_problem* p, const int32_t* k_per_head, const int32_t* rev_ptr,
-                             const int32_t* rev_idx, float* dK, float* dV, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+int dsa_sparse_attn_bwd_preprocess(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
+                                   const void* dO, const float* LSE, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return dsa_sparse_attn_bwd_preprocess_ex(p, Q, K, V, O, dO, LSE, 0, workspace, workspace_bytes, stream);
+}
+
+int dsa_sparse_attn_bwd_dkdv(const dsa_problem* p, const void* Q, const void* K, const void* V, const void* dO,
+                             const int32_t* k_per_head, const int32_t* rev_ptr, const int32_t* rev_idx, float* dK,
+                             float* dV, void* workspace, size_t workspace_bytes, void* stream) {
   Shape s;
   HeadTable ht;
   int st = check_bwd_common(p, k_per_head, &s, &ht);
   if (st) return st;
-  if (!rev_ptr || !rev_idx || !dK || !dV) return DSA_ERR_INVALID_ARG;
-  if (!aligned16(rev_ptr) || !aligned16(rev_idx) || !aligned16(dK) || !aligned16(dV)) return DSA_ERR_ALIGN;
+  if (!Q || !K || !V || !dO || !rev_ptr || !rev_idx || !dK || !dV) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(rev_ptr) ||
+      !aligned16(rev_idx) || !aligned16(dK) || !aligned16(dV))
+    return DSA_ERR_ALIGN;
   if ((st = check_ws(s, workspace, workspace_bytes))) return st;
-  return hip_status(dsa::launch_bwd_dkdv(s, bwd_work(s, workspace), rev_ptr, rev_idx, dK, dV, ht,
+  return hip_status(dsa::launch_bwd_dkdv(s, bwd_work(s, workspace), Q, K, V, dO, rev_ptr, rev_idx, dK, dV, ht,
                                          static_cast<hipStream_t>(stream)));
 }
 
-int dsa_sparse_attn_bwd_dq(const dsa_problem* p, const int32_t* idx, const int32_t* k_per_head, float* dQ,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+int dsa_sparse_attn_bwd_dq(const dsa_problem* p, const void* Q, const void* dO, const int32_t* idx,
+                           const int32_t* k_per_head, float* dQ, void* workspace, size_t workspace_bytes,
+                           void* stream) {
   Shape s;
   HeadTable ht;
   int st = check_bwd_common(p, k_per_head, &s, &ht);
   if (st) return st;
-  if (!idx || !dQ) return DSA_ERR_INVALID_ARG;
-  if (!aligned16(idx) || !aligned16(dQ)) return DSA_ERR_ALIGN;
+  if (!Q || !dO || !idx || !dQ) return DSA_ERR_INVALID_ARG;
+  if (!aligned16(Q) || !aligned16(dO) || !aligned16(idx) || !aligned16(dQ)) return DSA_ERR_ALIGN;
   if ((st = check_ws(s, workspace, workspace_bytes))) return st;
-  return hip_status(dsa::launch_bwd_dq(s, bwd_work(s, workspace), idx, dQ, ht, static_cast<hipStream_t>(stream)));
+  return hip_status(dsa::launch_bwd_dq(s, bwd_work(s, workspace), Q, dO, idx, dQ, ht, static_cast<hipStream_t>(stream)));
 }
 
 static int bwd_impl(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O, const void* dO,
                     const float* LSE, const int32_t* idx, const int32_t* cnt, const int32_t* k_per_head,
-                    const int32_t* rev_ptr, const int32_t* rev_idx, float* dQ, float* dK, float* dV, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    const int32_t* rev_ptr, const int32_t* rev_idx, float* dQ, float* dK, float* dV, int flags,
+                    void* workspace, size_t workspace_bytes, void* stream) {
   Shape s;
   HeadTable ht;
   int st = check_bwd_common(p, k_per_head, &s, &ht);
   if (st) return st;
+  if (flags & ~DSA_BWD_V_FROM_FORWARD) return DSA_ERR_INVALID_ARG;
   if (!Q || !K || !V || !O || !dO || !LSE || !idx || !rev_ptr || !rev_idx || !dQ || !dK || !dV)
     return DSA_ERR_INVALID_ARG;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(dO) || !aligned16(LSE) ||
@@ -488,9 +516,9 @@ static int bwd_impl(const dsa_problem* p, const void* Q, const void* K, const vo
   if ((st = check_ws(s, workspace, workspace_bytes))) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const dsa::BwdWork w = bwd_work(s, workspace);
-  hipError_t e = dsa::launch_bwd_pre(s, Q, K, V, O, dO, LSE, w, hs);
-  if (e == hipSuccess) e = dsa::launch_bwd_dkdv(s, w, rev_ptr, rev_idx, dK, dV, ht, hs);
-  if (e == hipSuccess) e = dsa::launch_bwd_dq(s, w, idx, dQ, ht, hs, cnt);
+  hipError_t e = dsa::launch_bwd_pre(s, Q, K, V, O, dO, LSE, w, (flags & DSA_BWD_V_FROM_FORWARD) != 0, hs);
+  if (e == hipSuccess) e = dsa::launch_bwd_dkdv(s, w, Q, K, V, dO, rev_ptr, rev_idx, dK, dV, ht, hs);
+  if (e == hipSuccess) e = dsa::launch_bwd_dq(s, w, Q, dO, idx, dQ, ht, hs, cnt);
   return hip_status(e);
 }
 
@@ -498,7 +526,15 @@ int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, cons
                         const void* dO, const float* LSE, const int32_t* idx, const int32_t* k_per_head,
                         const int32_t* rev_ptr, const int32_t* rev_idx, float* dQ, float* dK, float* dV,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(p, Q, K, V, O, dO, LSE, idx, nullptr, k_per_head, rev_ptr, rev_idx, dQ, dK, dV, workspace,
+  return bwd_impl(p, Q, K, V, O, dO, LSE, idx, nullptr, k_per_head, rev_ptr, rev_idx, dQ, dK, dV, 0, workspace,
+                  workspace_bytes, stream);
+}
+
+int dsa_sparse_attn_bwd_ex(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
+                           const void* dO, const float* LSE, const int32_t* idx, const int32_t* k_per_head,
+                           const int32_t* rev_ptr, const int32_t* rev_idx, float* dQ, float* dK, float* dV, int flags,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(p, Q, K, V, O, dO, LSE, idx, nullptr, k_per_head, rev_ptr, rev_idx, dQ, dK, dV, flags, workspace,
                   workspace_bytes, stream);
 }
 
@@ -508,7 +544,7 @@ int dsa_sparse_attn_bwd_varlen(const dsa_problem* p, const void* Q, const void* 
                                float* dK, float* dV, void* workspace, size_t workspace_bytes, void* stream) {
   if (!cnt) return DSA_ERR_INVALID_ARG;
   if (!aligned16(cnt)) return DSA_ERR_ALIGN;
-  return bwd_impl(p, Q, K, V, O, dO, LSE, idx, cnt, k_per_head, rev_ptr, rev_idx, dQ, dK, dV, workspace,
+  return bwd_impl(p, Q, K, V, O, dO, LSE, idx, cnt, k_per_head, rev_ptr, rev_idx, dQ, dK, dV, 0, workspace,
                   workspace_bytes, stream);
 }
 
@@ -522,8 +558,8 @@ int dsa_dense_attn_fwd(const dsa_problem* p, const void* Q, const void* K, const
   const size_t need = fwd_ws(s);
   if (need && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
   if (need && !aligned16(workspace)) return DSA_ERR_ALIGN;
-  return hip_status(dsa::launch_attn_fwd(s, Q, K, V, nullptr, O, LSE, static_cast<uint16_t*>(workspace),
-                                         dense_heads(s), 1, static_cast<hipStream_t>(stream)));
+  return hip_status(dsa::launch_attn_fwd(s, Q, K, V, nullptr, O, LSE, fwd_work(s, workspace), dense_heads(s), 1,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 int dsa_dense_attn_bwd(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
@@ -541,9 +577,9 @@ int dsa_dense_attn_bwd(const dsa_problem* p, const void* Q, const void* K, const
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const dsa::BwdWork w = bwd_work(s, workspace);
   const HeadTable ht = dense_heads(s);
-  hipError_t e = dsa::launch_bwd_pre(s, Q, K, V, O, dO, LSE, w, hs);
-  if (e == hipSuccess) e = dsa::launch_bwd_dkdv(s, w, nullptr, nullptr, dK, dV, ht, hs);
-  if (e == hipSuccess) e = dsa::launch_bwd_dq(s, w, nullptr, dQ, ht, hs);
+  hipError_t e = dsa::launch_bwd_pre(s, Q, K, V, O, dO, LSE, w, false, hs);
+  if (e == hipSuccess) e = dsa::launch_bwd_dkdv(s, w, Q, K, V, dO, nullptr, nullptr, dK, dV, ht, hs);
+  if (e == hipSuccess) e = dsa::launch_bwd_dq(s, w, Q, dO, nullptr, dQ, ht, hs);
   return hip_status(e);
 }
 

@@ -7,52 +7,63 @@
 //   D_i = dO_i . O_i,  dP = dO V^T,  dS = P (dP - D),
 //   dV_j = sum_g P^T dO_g,  dK_j = tau sum_g dS^T Q_g,  dQ_g = tau sum_j dS K_j.
 //
-// bwd_pre computes D and -LSE*log2(e) and writes exact fp16 copies of Q, K, V
-// and dO into the workspace, so every product below runs on fp16 MFMA with
-// tiles DMA-loaded into XOR-swizzled LDS (no register staging or conversion in
-// the loops) and transposed operands read with ds_read_b64_tr_b16.
+// bwd_pre computes D and -LSE*log2(e) and the scaled fp16 copies of K (and of V
+// when the forward's copy is not reused), each (b, h) slice multiplied by a
+// power of two (common.hpp).
 //
 // bwd_dq: one workgroup per (b, h, group) over the group's kept blocks; waves
-// = 32-row tile x key half, partial dQ of the two halves summed at the end.
+// = 32-row tile x key half, partial dQ of the two halves summed at the end.  Its
+// products run on fp16 MFMA: K and V tiles from the scaled copies, the wave's own
+// Q and dO rows converted in registers with a power of two from the wave's
+// largest magnitude, dS rounded once to fp16.
 // bwd_dkdv: one workgroup per (b, h, KV block) over the block's reverse list;
 // each wave owns 32 keys and half of every 64-row query tile, dK/dV in
-// registers.  dK's dS operand is split hi + lo in fp16 (dK sums a cancelling
-// dS against clustered Q rows).
+// registers.  Its products run on bf16 MFMA straight from the bf16 inputs (bf16
+// spans fp32's range: no scaling), with P (for dV) and dS (for dK) each split
+// into a bf16 hi + lo pair: 16 significant bits.
+// Tiles are DMA-loaded into XOR-swizzled LDS (no register staging or conversion
+// in the loops) and transposed operands read with ds_read_b64_tr_b16.
 #include "launch.hpp"
 
 namespace dsa {
 
 namespace {
 
-// D_i = sum_c dO_ic O_ic, nl2_i = -LSE_i * log2(e), and the exact fp16 copies
-// of Q, K, V, dO, in one pass over the rows; one 16-lane slice per row
-// (D = 128) or 8 (D = 64), 8 columns per lane.
+// D_i = sum_c dO_ic O_ic, nl2_i = -LSE_i * log2(e), and the scaled fp16 copies of K (and of V unless the
+// forward's copy is reused), in one pass over the rows of one (b, h) slice per grid row; one 16-lane slice
+// per row (D = 128) or 8 (D = 64), 8 columns per lane.  The slice's exponents come from the partial maxima;
+// its first workgroup records them in ex.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K,
-                                                      const bf16_t* __restrict__ V, const bf16_t* __restrict__ dO,
-                                                      const float* __restrict__ O, const float* __restrict__ LSE,
-                                                      float* __restrict__ Dvec, float* __restrict__ nl2,
-                                                      uint16_t* __restrict__ Q16, uint16_t* __restrict__ K16,
-                                                      uint16_t* __restrict__ V16, uint16_t* __restrict__ dO16,
-                                                      int64_t rows) {
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+                                                      const bf16_t* __restrict__ dO, const float* __restrict__ O,
+                                                      const float* __restrict__ LSE, float* __restrict__ Dvec,
+                                                      float* __restrict__ nl2, uint16_t* __restrict__ K16,
+                                                      uint16_t* __restrict__ V16, const uint32_t* __restrict__ part,
+                                                      int32_t* __restrict__ ex, int N, int BH, int convert_v) {
   constexpr int LPR = D / 8;           // lanes per row
   constexpr int RPB = 256 / LPR;       // rows per workgroup pass
+  const int bh = blockIdx.y;
+  const int eK = slice_exponent(part, kTK, bh, BH, kExpTargetQK);
+  const int eV = convert_v ? slice_exponent(part, kTV, bh, BH, kExpTargetV) : 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    ex[kTK * BH + bh] = eK;
+    if (convert_v) ex[kTV * BH + bh] = eV;
+  }
   const int sub = threadIdx.x % LPR;
-  for (int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR; row < rows; row += (int64_t)gridDim.x * RPB) {
+  const int64_t r0 = (int64_t)bh * N + (int64_t)N * blockIdx.x / gridDim.x;
+  const int64_t r1 = (int64_t)bh * N + (int64_t)N * (blockIdx.x + 1) / gridDim.x;
+  for (int64_t row = r0 + threadIdx.x / LPR; row < r1; row += RPB) {
     const int64_t at = row * D + 8 * sub;
-    const uint4 q = ldg16(Q + at), k = ldg16(K + at), v = ldg16(V + at);
-    *reinterpret_cast<uint4*>(Q16 + at) = bf16x8_to_f16x8(q);
-    *reinterpret_cast<uint4*>(K16 + at) = bf16x8_to_f16x8(k);
-    *reinterpret_cast<uint4*>(V16 + at) = bf16x8_to_f16x8(v);
-    const uint4 d = ldg16(dO + row * D + 8 * sub);
-    const float4 o0 = *reinterpret_cast<const float4*>(O + row * D + 8 * sub);
-    const float4 o1 = *reinterpret_cast<const float4*>(O + row * D + 8 * sub + 4);
+    *reinterpret_cast<uint4*>(K16 + at) = bf16x8_to_f16x8_scaled(ldg16(K + at), eK);
+    if (convert_v) *reinterpret_cast<uint4*>(V16 + at) = bf16x8_to_f16x8_scaled(ldg16(V + at), eV);
+    const uint4 d = ldg16(dO + at);
+    const float4 o0 = *reinterpret_cast<const float4*>(O + at);
+    const float4 o1 = *reinterpret_cast<const float4*>(O + at + 4);
     const uint32_t* w = reinterpret_cast<const uint32_t*>(&d);
     float s = __uint_as_float(w[0] << 16) * o0.x + __uint_as_float(w[0] & 0xFFFF0000u) * o0.y +
               __uint_as_float(w[1] << 16) * o0.z + __uint_as_float(w[1] & 0xFFFF0000u) * o0.w +
               __uint_as_float(w[2] << 16) * o1.x + __uint_as_float(w[2] & 0xFFFF0000u) * o1.y +
               __uint_as_float(w[3] << 16) * o1.z + __uint_as_float(w[3] & 0xFFFF0000u) * o1.w;
-    *reinterpret_cast<uint4*>(dO16 + row * D + 8 * sub) = bf16x8_to_f16x8(d);
 #pragma unroll
     for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off);
     if (sub == 0) {
@@ -62,7 +73,20 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__
   }
 }
 
-__device__ __forceinline__ f16x8 ldg_f16x8(const uint16_t* p) { return __builtin_bit_cast(f16x8, ldg16(p)); }
+// Largest |bf16| (bit pattern, sign cleared) among the 8 values of each of n registers, over the wave.
+template <int n>
+__device__ __forceinline__ uint32_t wave_amax_bf16(const uint4 (&v)[n]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int t = 0; t < n; ++t) {
+    const uint32_t w[4] = {v[t].x & 0x7FFF7FFFu, v[t].y & 0x7FFF7FFFu, v[t].z & 0x7FFF7FFFu, v[t].w & 0x7FFF7FFFu};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m = max(m, max(w[q] & 0xFFFFu, w[q] >> 16));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  return m;
+}
 
 // ---------------------------------------------------------------- dQ
 
@@ -70,15 +94,15 @@ __device__ __forceinline__ f16x8 ldg_f16x8(const uint16_t* p) { return __builtin
 // kMerge: phase `phase` of n_phase launches in sequence, each over one segment of every row's list (for
 // heads whose K and V fill more than half the MALL); launches after the first add into the stored dQ.
 template <int D, int G, bool kLists, bool kMerge>
-__global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __restrict__ Q16,
+__global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const bf16_t* __restrict__ Q,
                                                           const uint16_t* __restrict__ K16,
                                                           const uint16_t* __restrict__ V16,
-                                                          const uint16_t* __restrict__ dO16,
+                                                          const bf16_t* __restrict__ dO,
                                                           const float* __restrict__ NL2, const float* __restrict__ Dvec,
                                                           const int32_t* __restrict__ idx,
                                                           const int32_t* __restrict__ cnt, float* __restrict__ dQ,
-                                                          HeadTable ht, XcdSplit sp, int N, int H, int B, float scale_log2,
-                                                          float tau, int n_phase, int phase) {
+                                                          const int32_t* __restrict__ ex, HeadTable ht, XcdSplit sp,
+                                                          int N, int H, int B, float tau, int n_phase, int phase) {
   constexpr int NRT = G / 32;
   constexpr int NW = 2 * NRT;
   constexpr int RB = 2 * D;
@@ -123,14 +147,32 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
     else return kbeg + min(t, k - 1);
   };
 
+  // The wave's Q and dO rows (B operands of S^T and dP^T) as fp16, each multiplied by the power of two that
+  // puts the wave's largest magnitude in the target range (the two key-half waves of a row tile read the
+  // same rows and find the same exponents).  K16, V16 carry their slices' 2^eK, 2^eV.  So S^T accumulates
+  // 2^(eQ+eK) S, dP and D (scaled here) 2^(eO+eV), dQ^T 2^(eO+eV+eK) dQ^T / tau.
   f16x8 qreg[D / 16], oreg[D / 16];
+  int eQ, eO;
+  {
+    uint4 qraw[D / 16], oraw[D / 16];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    qreg[t] = ldg_f16x8(Q16 + qrow * D + 16 * t + 8 * hh);
-    oreg[t] = ldg_f16x8(dO16 + qrow * D + 16 * t + 8 * hh);
+    for (int t = 0; t < D / 16; ++t) {
+      qraw[t] = ldg16(Q + qrow * D + 16 * t + 8 * hh);
+      oraw[t] = ldg16(dO + qrow * D + 16 * t + 8 * hh);
+    }
+    eQ = scale_exponent(wave_amax_bf16(qraw), kExpTargetQK);
+    eO = scale_exponent(wave_amax_bf16(oraw), kExpTargetDO);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      qreg[t] = __builtin_bit_cast(f16x8, bf16x8_to_f16x8_scaled(qraw[t], eQ));
+      oreg[t] = __builtin_bit_cast(f16x8, bf16x8_to_f16x8_scaled(oraw[t], eO));
+    }
   }
+  const int BHn = B * H;
+  const int eK = ex[kTK * BHn + bh], eV = ex[kTV * BHn + bh];
+  const float scale_log2 = __builtin_ldexpf(tau * kLog2e, -(eQ + eK));
   const float nl2 = NL2[qrow];
-  const float dvec = Dvec[qrow];
+  const float dvec = __builtin_ldexpf(Dvec[qrow], eO + eV);
 
   int kofs[D / 16];  // K and V rows (keys of this half) as A operands
 #pragma unroll
@@ -236,7 +278,8 @@ __global__ __launch_bounds__(G * 4, 2) void bwd_dq_kernel(const uint16_t* __rest
         if (kMerge && phase > 0) prev = *reinterpret_cast<const float4*>(op);
         float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (acc[c][4 * q4 + r] + mb[(c * 16 + 4 * q4 + r) * 64 + lane]) * tau;
+        for (int r = 0; r < 4; ++r)
+          v[r] = __builtin_ldexpf((acc[c][4 * q4 + r] + mb[(c * 16 + 4 * q4 + r) * 64 + lane]) * tau, -(eO + eV + eK));
         *reinterpret_cast<float4*>(op) = make_float4(prev.x + v[0], prev.y + v[1], prev.z + v[2], prev.w + v[3]);
       }
   }
@@ -314,21 +357,21 @@ __global__ __launch_bounds__(256) void dkdv_order_kernel(const int32_t* __restri
 // kMerge: phase `phase` of n_phase launches in sequence, each over one segment of every reverse list
 // (for heads whose Q and dO fill more than half the MALL); launches after the first add into dK, dV.
 template <int D, int G, bool kLists, bool kMerge>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q16,
-                                                          const uint16_t* __restrict__ K16,
-                                                          const uint16_t* __restrict__ V16,
-                                                          const uint16_t* __restrict__ dO16,
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const bf16_t* __restrict__ Q,
+                                                          const bf16_t* __restrict__ K,
+                                                          const bf16_t* __restrict__ V,
+                                                          const bf16_t* __restrict__ dO,
                                                           const float* __restrict__ NL2,
                                                           const float* __restrict__ Dvec,
                                                           const int32_t* __restrict__ rev_ptr,
                                                           const int32_t* __restrict__ rev_idx,
                                                           const int32_t* __restrict__ order, float* __restrict__ dK,
-                                                          float* __restrict__ dV, HeadTable ht, XcdSplit sp, int N, int H, int NB,
-                                                          int B, float tau, int n_phase, int phase) {
+                                                          float* __restrict__ dV, HeadTable ht, XcdSplit sp, int N,
+                                                          int H, int NB, int B, float tau, int n_phase, int phase) {
   constexpr int NW = 4;
   constexpr int RB = 2 * D;
   constexpr int TILE = 64 * RB;
-  constexpr int STAGE = 2 * TILE + 512;  // Q16 tile, dO16 tile, -LSE*log2e row, D row
+  constexpr int STAGE = 2 * TILE + 512;  // Q tile, dO tile, -LSE*log2e row, D row
   constexpr int SUB = G / 64;            // 64-row query tiles per group
   constexpr int NT = D / 32;             // 32-wide steps of the head dimension (S, dP)
   constexpr int NC = D / 16;             // 16-wide column tiles of dK, dV
@@ -336,8 +379,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
   static_assert(2 * XBUF <= STAGE, "the partials of one key half must fit in one stage");
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
-  const float scale_log2 = tau * kLog2e;
-  const float inv_scale = 1.0f / scale_log2;
 
   const int64_t slot = xcd_task(sp, blockIdx.x);
   if (slot < 0) return;
@@ -351,6 +392,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
   const int l16 = lane & 15, q4 = lane >> 4;
   const int kh = wave & 1, qh = wave >> 1;
   const int32_t total = NG * ht.k[h];  // size of the (b, h) region of the reverse list
+  const float scale_log2 = tau * kLog2e;
+  const float inv_scale = 1.0f / scale_log2;
   int32_t s0 = 0, s1 = NG;
   const int32_t* rlist = nullptr;
   if constexpr (kLists) {
@@ -369,14 +412,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
 
   // this wave's keys as B operands (half kk: keys 32*kh + 16*kk + l16): K for
   // S = Q K^T, V for dP = dO V^T
-  f16x8 kreg[2][NT], vreg[2][NT];
+  bf16x8 kreg[2][NT], vreg[2][NT];
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     const size_t key = bh * N + (size_t)j * kBlock + 32 * kh + 16 * kk + l16;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      kreg[kk][t] = ldg_f16x8(K16 + key * D + 32 * t + 8 * q4);
-      vreg[kk][t] = ldg_f16x8(V16 + key * D + 32 * t + 8 * q4);
+      kreg[kk][t] = __builtin_bit_cast(bf16x8, ldg16(K + key * D + 32 * t + 8 * q4));
+      vreg[kk][t] = __builtin_bit_cast(bf16x8, ldg16(V + key * D + 32 * t + 8 * q4));
     }
   }
   // A operands of S and dP: query row 32*qh + 16*qq + l16, logical chunk 4t + q4,
@@ -404,8 +447,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
   auto fetch = [&](int it, int graw, char* dst) {
     const int g = min(max(__builtin_amdgcn_readfirstlane(graw), 0), NG - 1);
     const size_t row0 = bh * N + (size_t)g * G + (size_t)(it % SUB) * 64;
-    dma_tile<D, NW>(Q16 + row0 * D, dst, wave, lane);
-    dma_tile<D, NW>(dO16 + row0 * D, dst + TILE, wave, lane);
+    dma_tile<D, NW>(Q + row0 * D, dst, wave, lane);
+    dma_tile<D, NW>(dO + row0 * D, dst + TILE, wave, lane);
     if (wave == 0) dma_row64_f32(NL2 + row0, dst + 2 * TILE, lane);
     if (wave == 1) dma_row64_f32(Dvec + row0, dst + 2 * TILE + 256, lane);
   };
@@ -437,50 +480,49 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
     for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(cur + 16 * qq * RB + (ab ^ (64 * t)));
-        s[0][qq] = mfma16h(a, kreg[0][t], s[0][qq]);
-        s[1][qq] = mfma16h(a, kreg[1][t], s[1][qq]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(cur + 16 * qq * RB + (ab ^ (64 * t)));
+        s[0][qq] = mfma16b(a, kreg[0][t], s[0][qq]);
+        s[1][qq] = mfma16b(a, kreg[1][t], s[1][qq]);
       }
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const f16x8 a = *reinterpret_cast<const f16x8*>(cur + TILE + 16 * qq * RB + (ab ^ (64 * t)));
-        dp[0][qq] = mfma16h(a, vreg[0][t], dp[0][qq]);
-        dp[1][qq] = mfma16h(a, vreg[1][t], dp[1][qq]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(cur + TILE + 16 * qq * RB + (ab ^ (64 * t)));
+        dp[0][qq] = mfma16b(a, vreg[0][t], dp[0][qq]);
+        dp[1][qq] = mfma16b(a, vreg[1][t], dp[1][qq]);
       }
     // P = exp2(S tau log2 e), dS = P (dP - D); A operands per key half kk:
     // element e' <-> query 32*qh + 16*(e'/4) + 4*q4 + e'%4
-    // P and dS both enter their products as an fp16 hi + lo pair (about 22 significant bits): dV sums P
-    // against dO and dK sums a cancelling dS against clustered Q, and one fp16 rounding of either
-    // (2^-12 relative) leaves errors of a few 1e-2 on gradients of magnitude 100-200
-    f16x8 ph[2], pl[2], dh[2], dl[2];
+    // P and dS each enter their products as a bf16 hi + lo pair (16 significant bits, fp32's range): dV sums
+    // P against dO and dK sums a cancelling dS against clustered Q, and one 11-bit rounding of either
+    // (fp16, 2^-12 relative) left errors of a few 1e-2 on gradients of magnitude 100-200
+    bf16x8 ph[2], pl[2], dh[2], dl[2];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < 2; ++kk) {
+      float pv[8], dsv[8];
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p = __builtin_amdgcn_exp2f(s[kk][qq][e] * scale_log2);
-          const float ds = p * dp[kk][qq][e];
-          const _Float16 hp = (_Float16)p, hv = (_Float16)ds;
-          ph[kk][4 * qq + e] = hp;
-          pl[kk][4 * qq + e] = (_Float16)(p - (float)hp);
-          dh[kk][4 * qq + e] = hv;
-          dl[kk][4 * qq + e] = (_Float16)(ds - (float)hv);
+          pv[4 * qq + e] = __builtin_amdgcn_exp2f(s[kk][qq][e] * scale_log2);
+          dsv[4 * qq + e] = pv[4 * qq + e] * dp[kk][qq][e];
         }
+      split_bf16x8(pv, ph[kk], pl[kk]);
+      split_bf16x8(dsv, dh[kk], dl[kk]);
+    }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const char* o = cur + TILE + (tb ^ (32 * c));
-      const f16x8 ob = join_f16(lds_read_tr16(o), lds_read_tr16(o + 16 * RB));
+      const bf16x8 ob = join_bf16(lds_read_tr16(o), lds_read_tr16(o + 16 * RB));
       const char* q = cur + (tb ^ (32 * c));
-      const f16x8 qb = join_f16(lds_read_tr16(q), lds_read_tr16(q + 16 * RB));
+      const bf16x8 qb = join_bf16(lds_read_tr16(q), lds_read_tr16(q + 16 * RB));
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        dv[kk][c] = mfma16h(ph[kk], ob, dv[kk][c]);
-        dv[kk][c] = mfma16h(pl[kk], ob, dv[kk][c]);
-        dk[kk][c] = mfma16h(dh[kk], qb, dk[kk][c]);
-        dk[kk][c] = mfma16h(dl[kk], qb, dk[kk][c]);
+        dv[kk][c] = mfma16b(ph[kk], ob, dv[kk][c]);
+        dv[kk][c] = mfma16b(pl[kk], ob, dv[kk][c]);
+        dk[kk][c] = mfma16b(dh[kk], qb, dk[kk][c]);
+        dk[kk][c] = mfma16b(dl[kk], qb, dk[kk][c]);
       }
     }
     // (no scheduling groups: at this register load the compiler's own order is faster, 9.33 vs 9.71 ms)
@@ -527,19 +569,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(const uint16_t* __rest
 }
 
 template <int D>
-hipError_t pre_launch(const Shape& s, const bf16_t* Q, const bf16_t* K, const bf16_t* V, const float* O,
-                      const bf16_t* dO, const float* LSE, const BwdWork& w, hipStream_t st) {
-  const int64_t rows = (int64_t)s.B * s.H * s.N;
+hipError_t pre_launch(const Shape& s, const bf16_t* K, const bf16_t* V, const float* O, const bf16_t* dO,
+                      const float* LSE, const BwdWork& w, bool v_from_fwd, hipStream_t st) {
+  const int BH = s.B * s.H;
+  const int64_t n_per_bh = (int64_t)s.N * D;
+  AmaxSrc a = {{nullptr, K, v_from_fwd ? nullptr : V, nullptr}};
+  hipError_t e = launch_amax(a, w.part, n_per_bh, BH, st);
+  if (e != hipSuccess) return e;
   constexpr int RPB = 256 / (D / 8);
-  const int64_t nwg = (rows + RPB - 1) / RPB;
-  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)(nwg < 65536 ? nwg : 65536)), dim3(256), 0, st, Q, K, V, dO,
-                     O, LSE, w.Dvec, w.nl2, w.Q16, w.K16, w.V16, w.dO16, rows);
+  const int64_t passes = ((int64_t)s.N + RPB - 1) / RPB;  // workgroup passes over one slice's rows
+  const unsigned chunks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(256, passes / 4));
+  hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3(chunks, BH), dim3(256), 0, st, K, V, dO, O, LSE, w.Dvec, w.nl2, w.K16,
+                     w.V16, w.part, w.ex, s.N, BH, v_from_fwd ? 0 : 1);
   return hipGetLastError();
 }
 
 template <int D, int G>
-hipError_t dkdv_launch(const Shape& s, const BwdWork& w, const int32_t* rev_ptr, const int32_t* rev_idx, float* dK,
-                       float* dV, const HeadTable& ht, hipStream_t st) {
+hipError_t dkdv_launch(const Shape& s, const BwdWork& w, const bf16_t* Q, const bf16_t* K, const bf16_t* V,
+                       const bf16_t* dO, const int32_t* rev_ptr, const int32_t* rev_idx, float* dK, float* dV,
+                       const HeadTable& ht, hipStream_t st) {
   const float tau = 1.0f / sqrtf((float)D);
   // a KV block costs its reverse-list length, NG * k_h / NB on average, + 1; a head streams its Q and dO
   unsigned nwg = 0;
@@ -553,19 +601,19 @@ hipError_t dkdv_launch(const Shape& s, const BwdWork& w, const int32_t* rev_ptr,
   if (nph > 1) {
     auto kern = rev_ptr ? bwd_dkdv_kernel<D, G, true, true> : bwd_dkdv_kernel<D, G, false, true>;
     for (int ph = 0; ph < nph; ++ph)
-      hipLaunchKernelGGL(kern, dim3(nwg), dim3(256), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, rev_ptr,
-                         rev_idx, w.order, dK, dV, ht, sp, s.N, s.H, s.NB, s.B, tau, nph, ph);
+      hipLaunchKernelGGL(kern, dim3(nwg), dim3(256), 0, st, Q, K, V, dO, w.nl2, w.Dvec, rev_ptr, rev_idx, w.order,
+                         dK, dV, ht, sp, s.N, s.H, s.NB, s.B, tau, nph, ph);
     return hipGetLastError();
   }
   auto kern = rev_ptr ? bwd_dkdv_kernel<D, G, true, false> : bwd_dkdv_kernel<D, G, false, false>;
-  hipLaunchKernelGGL(kern, dim3(nwg), dim3(256), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, rev_ptr, rev_idx,
-                     w.order, dK, dV, ht, sp, s.N, s.H, s.NB, s.B, tau, 1, -1);
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(256), 0, st, Q, K, V, dO, w.nl2, w.Dvec, rev_ptr, rev_idx, w.order, dK,
+                     dV, ht, sp, s.N, s.H, s.NB, s.B, tau, 1, -1);
   return hipGetLastError();
 }
 
 template <int D, int G>
-hipError_t dq_launch(const Shape& s, const BwdWork& w, const int32_t* idx, const int32_t* cnt, float* dQ,
-                     const HeadTable& ht, hipStream_t st) {
+hipError_t dq_launch(const Shape& s, const BwdWork& w, const bf16_t* Q, const bf16_t* dO, const int32_t* idx,
+                     const int32_t* cnt, float* dQ, const HeadTable& ht, hipStream_t st) {
   const float tau = 1.0f / sqrtf((float)D);
   unsigned nwg = 0;
   const double head_bytes = 4.0 * s.N * D;  // one head's K and V (fp16 copies)
@@ -573,42 +621,52 @@ hipError_t dq_launch(const Shape& s, const BwdWork& w, const int32_t* idx, const
     const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0 / kMallPhasesKV, 1.0, head_bytes, &nwg);
     auto kern = idx ? bwd_dq_kernel<D, G, true, true> : bwd_dq_kernel<D, G, false, true>;
     for (int ph = 0; ph < kMallPhasesKV; ++ph)
-      hipLaunchKernelGGL(kern, dim3(nwg), dim3(G * 4), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, idx, cnt, dQ,
-                         ht, sp, s.N, s.H, s.B, tau * kLog2e, tau, kMallPhasesKV, ph);
+      hipLaunchKernelGGL(kern, dim3(nwg), dim3(G * 4), 0, st, Q, w.K16, w.V16, dO, w.nl2, w.Dvec, idx, cnt, dQ, w.ex,
+                         ht, sp, s.N, s.H, s.B, tau, kMallPhasesKV, ph);
     return hipGetLastError();
   }
   const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0, 1.0, head_bytes, &nwg);  // a group costs k_h + 1
   auto kern = idx ? bwd_dq_kernel<D, G, true, false> : bwd_dq_kernel<D, G, false, false>;
-  hipLaunchKernelGGL(kern, dim3(nwg), dim3(G * 4), 0, st, w.Q16, w.K16, w.V16, w.dO16, w.nl2, w.Dvec, idx, cnt, dQ, ht,
-                     sp, s.N, s.H, s.B, tau * kLog2e, tau, 1, -1);
+  hipLaunchKernelGGL(kern, dim3(nwg), dim3(G * 4), 0, st, Q, w.K16, w.V16, dO, w.nl2, w.Dvec, idx, cnt, dQ, w.ex, ht,
+                     sp, s.N, s.H, s.B, tau, 1, -1);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd_pre(const Shape& s, const void* Q, const void* K, const void* V, const float* O,
-                          const void* dO, const float* LSE, const BwdWork& w, hipStream_t st) {
+                          const void* dO, const float* LSE, const BwdWork& w, bool v_from_fwd, hipStream_t st) {
+  (void)Q;
+  const bf16_t* k = static_cast<const bf16_t*>(K);
+  const bf16_t* v = static_cast<const bf16_t*>(V);
+  const bf16_t* o = static_cast<const bf16_t*>(dO);
+  return s.D == 64 ? pre_launch<64>(s, k, v, O, o, LSE, w, v_from_fwd, st)
+                   : pre_launch<128>(s, k, v, O, o, LSE, w, v_from_fwd, st);
+}
+
+hipError_t launch_bwd_dkdv(const Shape& s, const BwdWork& w, const void* Q, const void* K, const void* V,
+                           const void* dO, const int32_t* rev_ptr, const int32_t* rev_idx, float* dK, float* dV,
+                           const HeadTable& ht, hipStream_t st) {
   const bf16_t* q = static_cast<const bf16_t*>(Q);
   const bf16_t* k = static_cast<const bf16_t*>(K);
   const bf16_t* v = static_cast<const bf16_t*>(V);
   const bf16_t* o = static_cast<const bf16_t*>(dO);
-  return s.D == 64 ? pre_launch<64>(s, q, k, v, O, o, LSE, w, st) : pre_launch<128>(s, q, k, v, O, o, LSE, w, st);
+  if (s.D == 64)
+    return s.G == 64 ? dkdv_launch<64, 64>(s, w, q, k, v, o, rev_ptr, rev_idx, dK, dV, ht, st)
+                     : dkdv_launch<64, 128>(s, w, q, k, v, o, rev_ptr, rev_idx, dK, dV, ht, st);
+  return s.G == 64 ? dkdv_launch<128, 64>(s, w, q, k, v, o, rev_ptr, rev_idx, dK, dV, ht, st)
+                   : dkdv_launch<128, 128>(s, w, q, k, v, o, rev_ptr, rev_idx, dK, dV, ht, st);
 }
 
-hipError_t launch_bwd_dkdv(const Shape& s, const BwdWork& w, const int32_t* rev_ptr, const int32_t* rev_idx,
-                           float* dK, float* dV, const HeadTable& ht, hipStream_t st) {
+hipError_t launch_bwd_dq(const Shape& s, const BwdWork& w, const void* Q, const void* dO, const int32_t* idx,
+                         float* dQ, const HeadTable& ht, hipStream_t st, const int32_t* cnt) {
+  const bf16_t* q = static_cast<const bf16_t*>(Q);
+  const bf16_t* o = static_cast<const bf16_t*>(dO);
   if (s.D == 64)
-    return s.G == 64 ? dkdv_launch<64, 64>(s, w, rev_ptr, rev_idx, dK, dV, ht, st)
-                     : dkdv_launch<64, 128>(s, w, rev_ptr, rev_idx, dK, dV, ht, st);
-  return s.G == 64 ? dkdv_launch<128, 64>(s, w, rev_ptr, rev_idx, dK, dV, ht, st)
-                   : dkdv_launch<128, 128>(s, w, rev_ptr, rev_idx, dK, dV, ht, st);
-}
-
-hipError_t launch_bwd_dq(const Shape& s, const BwdWork& w, const int32_t* idx, float* dQ, const HeadTable& ht,
-                         hipStream_t st, const int32_t* cnt) {
-  if (s.D == 64)
-    return s.G == 64 ? dq_launch<64, 64>(s, w, idx, cnt, dQ, ht, st) : dq_launch<64, 128>(s, w, idx, cnt, dQ, ht, st);
-  return s.G == 64 ? dq_launch<128, 64>(s, w, idx, cnt, dQ, ht, st) : dq_launch<128, 128>(s, w, idx, cnt, dQ, ht, st);
+    return s.G == 64 ? dq_launch<64, 64>(s, w, q, o, idx, cnt, dQ, ht, st)
+                     : dq_launch<64, 128>(s, w, q, o, idx, cnt, dQ, ht, st);
+  return s.G == 64 ? dq_launch<128, 64>(s, w, q, o, idx, cnt, dQ, ht, st)
+                   : dq_launch<128, 128>(s, w, q, o, idx, cnt, dQ, ht, st);
 }
 
 }  // namespace dsa

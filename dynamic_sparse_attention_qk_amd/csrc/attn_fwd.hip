@@ -82,6 +82,7 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
                                                                  const int32_t* __restrict__ idx,
                                                                  const int32_t* __restrict__ cnt,
                                                                  float* __restrict__ O, float* __restrict__ LSE,
+                                                                 const int32_t* __restrict__ ex,
                                                                  HeadTable ht, XcdSplit sp, int N, int H, int B,
                                                                  int n_split, int phase, float scale_log2) {
   constexpr int NRT = G / 32;                  // 32-row tiles of the group
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(G * 4, 2) void attn_fwd_bf16_kernel(const bf16_t* _
       wp = ep / W;
       lse2 = M + __log2f(W);
     }
-    const float inv = wc / lsum;
+    const float inv = __builtin_ldexpf(wc / lsum, -ex[kTV * B * H + bh]);  // V16 carries 2^eV
     const float w0 = a0 * inv, w1 = a1 * inv;
     float* orow = O + (bh * N + qrow) * (size_t)D;
 #pragma unroll
@@ -433,7 +434,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
 
 template <int D, int G>
 hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx,
-                      const int32_t* cnt, float* O, float* LSE, uint16_t* V16, const HeadTable& ht, int n_split,
+                      const int32_t* cnt, float* O, float* LSE, const FwdWork& w, const HeadTable& ht, int n_split,
                       hipStream_t st) {
   const float scale_log2 = (1.0f / sqrtf((float)D)) * kLog2e;
   unsigned nwg = 0;
@@ -443,7 +444,7 @@ hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* 
   const XcdSplit sp = make_xcd_split(s.B * n_split, s.H, s.NG, ht, 1.0 / n_split, 1.0, head_bytes, &nwg);
   dim3 grid(nwg);
   if (s.bf16) {
-    const hipError_t e = launch_cvt_f16(V, V16, (int64_t)s.B * s.H * s.N * D, st);
+    const hipError_t e = launch_cvt_scaled_v(V, w.V16, w.part, w.ex, (int64_t)s.N * D, s.B * s.H, st);
     if (e != hipSuccess) return e;
     auto kern = idx ? attn_fwd_bf16_kernel<D, G, true, false> : attn_fwd_bf16_kernel<D, G, false, false>;
     // the plain forward over heads whose K and V fill more than half the MALL: kMallPhasesKV launches in sequence
@@ -453,12 +454,12 @@ hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* 
       auto kern_m = idx ? attn_fwd_bf16_kernel<D, G, true, true> : attn_fwd_bf16_kernel<D, G, false, true>;
       for (int ph = 0; ph < kMallPhasesKV; ++ph)
         hipLaunchKernelGGL(kern_m, dim3(nwg_p), dim3(G * 4), 0, st, static_cast<const bf16_t*>(Q),
-                           static_cast<const bf16_t*>(K), V16, idx, cnt, O, LSE, ht, spp, s.N, s.H, s.B, kMallPhasesKV, ph,
-                           scale_log2);
+                           static_cast<const bf16_t*>(K), w.V16, idx, cnt, O, LSE, w.ex, ht, spp, s.N, s.H, s.B,
+                           kMallPhasesKV, ph, scale_log2);
       return hipGetLastError();
     }
     hipLaunchKernelGGL(kern, grid, dim3(G * 4), 0, st, static_cast<const bf16_t*>(Q), static_cast<const bf16_t*>(K),
-                       V16, idx, cnt, O, LSE, ht, sp, s.N, s.H, s.B, n_split, -1, scale_log2);
+                       w.V16, idx, cnt, O, LSE, w.ex, ht, sp, s.N, s.H, s.B, n_split, -1, scale_log2);
   } else {
     auto kern = idx ? attn_fwd_f32_kernel<D, G, true> : attn_fwd_f32_kernel<D, G, false>;
     hipLaunchKernelGGL(kern, grid, dim3(G * 2), 0, st, static_cast<const float*>(Q), static_cast<const float*>(K),
@@ -470,14 +471,14 @@ hipError_t fwd_launch(const Shape& s, const void* Q, const void* K, const void* 
 }  // namespace
 
 hipError_t launch_attn_fwd(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx, float* O,
-                           float* LSE, uint16_t* V16, const HeadTable& ht, int n_split, hipStream_t st,
+                           float* LSE, const FwdWork& w, const HeadTable& ht, int n_split, hipStream_t st,
                            const int32_t* cnt) {
   if (s.D == 64)
-    return s.G == 64 ? fwd_launch<64, 64>(s, Q, K, V, idx, cnt, O, LSE, V16, ht, n_split, st)
-                     : fwd_launch<64, 128>(s, Q, K, V, idx, cnt, O, LSE, V16, ht, n_split, st);
+    return s.G == 64 ? fwd_launch<64, 64>(s, Q, K, V, idx, cnt, O, LSE, w, ht, n_split, st)
+                     : fwd_launch<64, 128>(s, Q, K, V, idx, cnt, O, LSE, w, ht, n_split, st);
   if (s.D == 128)
-    return s.G == 64 ? fwd_launch<128, 64>(s, Q, K, V, idx, cnt, O, LSE, V16, ht, n_split, st)
-                     : fwd_launch<128, 128>(s, Q, K, V, idx, cnt, O, LSE, V16, ht, n_split, st);
+    return s.G == 64 ? fwd_launch<128, 64>(s, Q, K, V, idx, cnt, O, LSE, w, ht, n_split, st)
+                     : fwd_launch<128, 128>(s, Q, K, V, idx, cnt, O, LSE, w, ht, n_split, st);
   return hipErrorInvalidValue;
 }
 

@@ -90,6 +90,29 @@ __device__ __forceinline__ f32x4 mfma16h(const f16x8& a, const f16x8& b, const f
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// hi + lo bf16 split of 8 fp32 values (two MFMA operands): hi = the upper 16 bits of each value (rounded
+// toward zero: one byte permute per pair), lo = the exact remainder x - hi rounded to the nearest bf16 (one
+// packed conversion per pair).  hi + lo carries 16 significant bits, in fp32's exponent range.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t a = __float_as_uint(x[2 * q]), b = __float_as_uint(x[2 * q + 1]);
+    h[q] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // [a.bits 16-31, b.bits 16-31]
+    const f32x2 r = {x[2 * q] - __uint_as_float(a & 0xFFFF0000u), x[2 * q + 1] - __uint_as_float(b & 0xFFFF0000u)};
+    l[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// 16x16x32 bf16: the same operand and result layout as the fp16 one.
+__device__ __forceinline__ f32x4 mfma16b(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x16 mfma32_f32(float a, float b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
@@ -101,22 +124,6 @@ __device__ __forceinline__ f16x8 pack_f16(const f32x16& x, int c) {
   for (int e = 0; e < 8; ++e) r[e] = (_Float16)x[8 * c + e];
   return r;
 }
-
-
-// Exact conversion of 8 bf16 values (one 16-byte register) to fp16: every
-// bf16 value of magnitude in [2^-14, 65504] is representable in fp16.
-__device__ __forceinline__ uint4 bf16x8_to_f16x8(const uint4& v) {
-  uint4 r;
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(&v);
-  uint32_t* o = reinterpret_cast<uint32_t*>(&r);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float lo = __uint_as_float(w[q] << 16), hi = __uint_as_float(w[q] & 0xFFFF0000u);
-    o[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-  }
-  return r;
-}
-
 
 
 // 16-byte global load / store helpers.
@@ -215,6 +222,11 @@ __device__ __forceinline__ f16x8 join_f16(i16x4 a, i16x4 b) {
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(f16x8, v);
+}
+__device__ __forceinline__ bf16x8 join_bf16(i16x4 a, i16x4 b) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 
@@ -322,20 +334,124 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t w, uint32_t n) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
 }
 
-// bf16 -> fp16 shadow copy (exact for |x| in [2^-14, 65504]); 8 values per thread step.
+// ---------------------------------------------------------------- scaled fp16 copies of bf16 tensors
+//
+// The products with a probability or its gradient run on fp16 MFMA, whose operands span [2^-24, 65504]
+// only (normal from 2^-14), while bf16 spans fp32's range: activations of any magnitude, and gradients
+// dO that are typically 1e-6..1e-8 in training.  Each (b, h) slice of a tensor is therefore copied to fp16
+// multiplied by a power of two 2^e chosen from the slice's largest magnitude, so that it lands in
+// [2^a, 2^(a+1)); the kernels undo the scales exactly (ldexp) on their fp32 results.  Power-of-two scaling
+// is exact for every value that stays normal in fp16.  The targets a per tensor:
+//   Q, K:  14  -- the widest range fp16 allows: values down to 2^-28 of the slice's largest stay normal;
+//   V:      3  -- and dO: 2, so that |dO.V^T - D| <= 2 d max|dO| max|V| < 2^(1+7+3+4) = 2^15 for d <= 128
+//              (|D| = |dO.O| <= d max|dO| max|V|: O is a convex combination of V rows), i.e. dS = P (dP - D)
+//              and its fp16 hi part stay below 2^15.
+// The exponent table [4][B*H] (Q, K, V, dO) is written once per call and read by the attention kernels.
+constexpr int kExpTargetQK = 14;
+constexpr int kExpTargetV = 3;
+constexpr int kExpTargetDO = 2;
+constexpr int kAmaxChunks = 32;  // partial maxima per (tensor, b, h) slice
+enum { kTQ = 0, kTK = 1, kTV = 2, kTDO = 3 };
+
+// The scale exponent for a slice whose largest |bf16| has the bit pattern amax (sign cleared): 2^e * amax
+// lies in [2^target, 2^(target+1)).  An all-zero slice keeps e = 0; bf16 subnormals are treated as 2^-126;
+// e is clamped to [-100, 100] (slices beyond that lose resolution, as they would in any fp16 copy).
+__host__ __device__ __forceinline__ int scale_exponent(uint32_t amax, int target) {
+  if (amax == 0u) return 0;
+  const int E = (int)(amax >> 7);  // biased exponent of a bf16 (0 for subnormals)
+  const int e = target - ((E < 1 ? 1 : E) - 127);
+  return e < -100 ? -100 : (e > 100 ? 100 : e);
+}
+
+// Up to four bf16 tensors [B*H, n_per_bh] whose per-slice maxima are wanted (null: skipped).
+struct AmaxSrc {
+  const uint16_t* t[4];
+};
+
 namespace {
-__global__ __launch_bounds__(256) void cvt_bf16_f16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                                           int64_t n16) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
-    dst[i] = bf16x8_to_f16x8(src[i]);
+// Partial maxima of |x| per (tensor, b*h, chunk): part[(t * BH + bh) * kAmaxChunks + chunk] (bf16 bit
+// patterns with the sign cleared, which order like the magnitudes).  Grid (kAmaxChunks, BH, 4).
+__global__ __launch_bounds__(256) void amax_kernel(AmaxSrc src, uint32_t* __restrict__ part, int64_t n_per_bh,
+                                                   int BH) {
+  __shared__ uint32_t wmax[4];
+  const int t = blockIdx.z, bh = blockIdx.y, chunk = blockIdx.x;
+  if (!src.t[t]) return;  // uniform over the workgroup
+  const int64_t n16 = n_per_bh / 8;
+  const int64_t lo = n16 * chunk / kAmaxChunks, hi = n16 * (chunk + 1) / kAmaxChunks;
+  const uint4* p = reinterpret_cast<const uint4*>(src.t[t] + (int64_t)bh * n_per_bh);
+  uint32_t m = 0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
+    const uint4 v = p[i];
+    const uint32_t w[4] = {v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) m = max(m, max(w[q] & 0xFFFFu, w[q] >> 16));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    part[((int64_t)t * BH + bh) * kAmaxChunks + chunk] = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
 }
 }  // namespace
 
-inline hipError_t launch_cvt_f16(const void* src, void* dst, int64_t elems, hipStream_t st) {
-  const int64_t n16 = elems / 8;
-  const int64_t nwg = (n16 + 255) / 256;
-  hipLaunchKernelGGL(cvt_bf16_f16_kernel, dim3((unsigned)(nwg < 8192 ? nwg : 8192)), dim3(256), 0, st,
-                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), n16);
+inline hipError_t launch_amax(const AmaxSrc& src, uint32_t* part, int64_t n_per_bh, int BH, hipStream_t st) {
+  hipLaunchKernelGGL(amax_kernel, dim3(kAmaxChunks, BH, 4), dim3(256), 0, st, src, part, n_per_bh, BH);
+  return hipGetLastError();
+}
+
+// The exponent of slice (t, bh) from its partial maxima.
+__device__ __forceinline__ int slice_exponent(const uint32_t* __restrict__ part, int t, int bh, int BH, int target) {
+  const uint32_t* pp = part + ((int64_t)t * BH + bh) * kAmaxChunks;
+  uint32_t m = 0;
+#pragma unroll 8
+  for (int c = 0; c < kAmaxChunks; ++c) m = max(m, pp[c]);
+  return scale_exponent(m, target);
+}
+
+// 8 bf16 values (one 16-byte register) times 2^e, rounded to fp16 (nearest even; exact while the scaled
+// value is a normal fp16 number, which the exponent choice makes true for the slice's larger values).
+__device__ __forceinline__ uint4 bf16x8_to_f16x8_scaled(const uint4& v, int e) {
+  uint4 r;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&v);
+  uint32_t* o = reinterpret_cast<uint32_t*>(&r);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float lo = __builtin_ldexpf(__uint_as_float(w[q] << 16), e);
+    const float hi = __builtin_ldexpf(__uint_as_float(w[q] & 0xFFFF0000u), e);
+    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    o[q] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+  return r;
+}
+
+namespace {
+// Scaled fp16 copy of one bf16 tensor [B*H, n_per_bh] (tensor slot t of the exponent table).  Grid
+// (chunks, BH); the first workgroup of each slice also writes its exponent to ex[t * BH + bh].
+__global__ __launch_bounds__(256) void cvt_scaled_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                         const uint32_t* __restrict__ part, int32_t* __restrict__ ex,
+                                                         int t, int target, int64_t n_per_bh, int BH) {
+  const int bh = blockIdx.y;
+  const int e = slice_exponent(part, t, bh, BH, target);
+  if (blockIdx.x == 0 && threadIdx.x == 0) ex[t * BH + bh] = e;
+  const int64_t n16 = n_per_bh / 8;
+  const int64_t lo = n16 * blockIdx.x / gridDim.x, hi = n16 * (blockIdx.x + 1) / gridDim.x;
+  const uint4* s = reinterpret_cast<const uint4*>(src + (int64_t)bh * n_per_bh);
+  uint4* d = reinterpret_cast<uint4*>(dst + (int64_t)bh * n_per_bh);
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 256) d[i] = bf16x8_to_f16x8_scaled(s[i], e);
+}
+}  // namespace
+
+// The forward's V: per-slice maxima, then the scaled copy and its exponent (slot kTV of ex).
+inline hipError_t launch_cvt_scaled_v(const void* V, uint16_t* V16, uint32_t* part, int32_t* ex, int64_t n_per_bh,
+                                      int BH, hipStream_t st) {
+  AmaxSrc a = {{nullptr, nullptr, static_cast<const uint16_t*>(V), nullptr}};
+  hipError_t e = launch_amax(a, part, n_per_bh, BH, st);
+  if (e != hipSuccess) return e;
+  const int64_t per = n_per_bh / 8 / 256;  // 256-thread passes per slice
+  const unsigned chunks = (unsigned)std::max<int64_t>(1, std::min<int64_t>(64, per / 4));
+  hipLaunchKernelGGL(cvt_scaled_kernel, dim3(chunks, BH), dim3(256), 0, st, static_cast<const uint16_t*>(V), V16,
+                     part, ex, (int)kTV, kExpTargetV, n_per_bh, BH);
   return hipGetLastError();
 }
 

@@ -27,29 +27,41 @@ hipError_t launch_topk_select(const Shape& s, const float* scores, const float* 
 hipError_t launch_reverse_index(const Shape& s, const int32_t* idx, int32_t* rev_ptr, int32_t* rev_idx,
                                 int32_t* counters, int32_t* scratch, const HeadTable& ht, int kmax,
                                 hipStream_t st);
+// The forward's workspace (bf16 inputs): the exponent table [4][B*H] (the forward writes the V entry), the
+// partial maxima [4][B*H][kAmaxChunks] and the scaled fp16 copy of V.  Its layout is the start of the
+// backward's, so a backward given the same workspace can reuse the copy.
+struct FwdWork {
+  int32_t* ex;
+  uint32_t* part;
+  uint16_t* V16;
+};
+
 // cnt (if not null): per-row kept counts [B,H,NG] within the k_h-entry rows of idx
 hipError_t launch_attn_fwd(const Shape& s, const void* Q, const void* K, const void* V, const int32_t* idx,
-                           float* O, float* LSE, uint16_t* V16, const HeadTable& ht, int n_split, hipStream_t st,
+                           float* O, float* LSE, const FwdWork& w, const HeadTable& ht, int n_split, hipStream_t st,
                            const int32_t* cnt = nullptr);
 hipError_t launch_attn_merge(const Shape& s, int n_parts, const float* O_part, const float* LSE_part, float* O,
                              float* LSE, hipStream_t st);
-// Backward workspace: D, -LSE*log2(e) and exact fp16 copies of Q, K, V, dO.
+// Backward workspace: the forward's part (exponent table, partial maxima, V16), then D, -LSE*log2(e), the
+// scaled fp16 copy of K (for dQ) and the dK/dV task order.  dK/dV read the bf16 inputs themselves.
 struct BwdWork {
+  int32_t* ex;
+  uint32_t* part;
   float* Dvec;
   float* nl2;
-  uint16_t* Q16;
   uint16_t* K16;
   uint16_t* V16;
-  uint16_t* dO16;
   int32_t* order;  // dK/dV task order: per XCD range, long reverse lists first
 };
 
+// v_from_fwd: V16 and its exponent were left in the workspace by the forward (not converted again)
 hipError_t launch_bwd_pre(const Shape& s, const void* Q, const void* K, const void* V, const float* O,
-                          const void* dO, const float* LSE, const BwdWork& w, hipStream_t st);
-hipError_t launch_bwd_dkdv(const Shape& s, const BwdWork& w, const int32_t* rev_ptr, const int32_t* rev_idx,
-                           float* dK, float* dV, const HeadTable& ht, hipStream_t st);
-hipError_t launch_bwd_dq(const Shape& s, const BwdWork& w, const int32_t* idx, float* dQ, const HeadTable& ht,
-                         hipStream_t st, const int32_t* cnt = nullptr);
+                          const void* dO, const float* LSE, const BwdWork& w, bool v_from_fwd, hipStream_t st);
+hipError_t launch_bwd_dkdv(const Shape& s, const BwdWork& w, const void* Q, const void* K, const void* V,
+                           const void* dO, const int32_t* rev_ptr, const int32_t* rev_idx, float* dK, float* dV,
+                           const HeadTable& ht, hipStream_t st);
+hipError_t launch_bwd_dq(const Shape& s, const BwdWork& w, const void* Q, const void* dO, const int32_t* idx,
+                         float* dQ, const HeadTable& ht, hipStream_t st, const int32_t* cnt = nullptr);
 
 // Block scores pooled from token-level logits (pooling 1: max, 2: log-mean-exp); pq, pk: fp16 [B,H,N,r]
 hipError_t launch_pooled_scores(const Shape& s, const void* Q, const void* K, const float* Wq, const float* Wk,

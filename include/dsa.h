@@ -161,10 +161,21 @@ int dsa_select_topk_blocks(const dsa_problem* p, const float* scores, const floa
  * blocks in idx row (b,h,g): l_im = tau Q_i.K_m, LSE_i = ln sum_m exp(l_im),
  * O_i = sum_m exp(l_im - LSE_i) V_m.  No causal mask.
  * O: [B,H,N,d] fp32; LSE: [B,H,N] fp32 (natural log).
- * Workspace: dsa_workspace_bytes(p, k_per_head, DSA_WS_FWD) (an fp16 copy of V
- * for bf16 inputs; 0 bytes, NULL allowed, for fp32 inputs).  bf16 V, and every
- * bf16 input of the backward, must be below 65504 in magnitude (products with
- * softmax probabilities run on fp16 operands, converted exactly from bf16).
+ * Workspace: dsa_workspace_bytes(p, k_per_head, DSA_WS_FWD) (for bf16 inputs:
+ * a scaled fp16 copy of V and its per-(b, h) exponent; 0 bytes, NULL allowed,
+ * for fp32 inputs).  A DSA_WS_BWD workspace is accepted as well: the
+ * forward's part is its first part, so the backward can reuse the copy
+ * (DSA_BWD_V_FROM_FORWARD).
+ * Input range: any finite bf16 values.  The forward's P V and the backward's
+ * dQ products run on fp16 operands: V and K are copied to fp16 per (b, h)
+ * slice, and the dQ kernel converts each wave's 32 rows of Q and dO, each
+ * multiplied by the power of two that puts the largest magnitude of its
+ * slice (or rows) in [2^a, 2^(a+1)) (a = 3 for V, 2 for dO, 14 for Q and K);
+ * the results are scaled back exactly.  Values more than 2^-(a+14) below
+ * that largest magnitude (fp16 subnormals after scaling) keep fewer
+ * significant bits, and below 2^-(a+24) of it they count as zero.  The
+ * backward's dK/dV products run on bf16 operands (fp32's range) straight
+ * from the inputs.
  * When one head's K and V copies (4*N*d bytes) fill more than half of the
  * 256 MiB Infinity Cache, the call runs as several launches over segments of
  * every list, the later ones merging into O and LSE in place; O and LSE hold
@@ -192,6 +203,23 @@ int dsa_sparse_attn_bwd(const dsa_problem* p, const void* Q, const void* K, cons
                         const int32_t* k_per_head, const int32_t* rev_ptr, const int32_t* rev_idx,
                         float* dQ, float* dK, float* dV, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/* Flags of dsa_sparse_attn_bwd_ex and dsa_sparse_attn_bwd_preprocess_ex. */
+#define DSA_BWD_V_FROM_FORWARD 1
+
+/*
+ * dsa_sparse_attn_bwd_ex -- dsa_sparse_attn_bwd with flags (0: the same call).
+ * DSA_BWD_V_FROM_FORWARD: the workspace is the one the forward of these inputs
+ * (the same problem and V) was given, and nothing has written it since; the
+ * backward then reuses the scaled fp16 copy of V the forward left there
+ * instead of converting V again (a training step converts V once).  The
+ * results are the same bits either way.  Other flags: DSA_ERR_INVALID_ARG.
+ */
+int dsa_sparse_attn_bwd_ex(const dsa_problem* p, const void* Q, const void* K, const void* V,
+                           const float* O, const void* dO, const float* LSE, const int32_t* idx,
+                           const int32_t* k_per_head, const int32_t* rev_ptr, const int32_t* rev_idx,
+                           float* dQ, float* dK, float* dV, int flags, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* Bytes of the static per-GPU scratch of dsa_select_topk_blocks_noalloc. */
 #define DSA_NOALLOC_SCRATCH_BYTES (16u << 20)
@@ -320,24 +348,33 @@ int dsa_attn_merge(const dsa_problem* p, int n_parts, const float* O_part, const
 
 /*
  * The three stages dsa_sparse_attn_bwd runs, exposed one launch group each,
- * sharing the DSA_WS_BWD workspace (D_i = dO_i . O_i, -LSE*log2(e) and exact
- * fp16 copies of Q, K, V, dO, written by the preprocess stage):
- *   dsa_sparse_attn_bwd_preprocess  fills the workspace from Q, K, V, O, dO, LSE;
- *   dsa_sparse_attn_bwd_dkdv        dK, dV from the reverse index (every key
- *                                   row of every block is written); it also
- *                                   writes its own task order (blocks with
- *                                   long reverse lists first) into the
- *                                   workspace before the dK/dV launch;
- *   dsa_sparse_attn_bwd_dq          dQ from the kept-block lists.
+ * sharing the DSA_WS_BWD workspace (D_i = dO_i . O_i, -LSE*log2(e) and the
+ * scaled fp16 copies of K and V with their exponents, written by the
+ * preprocess stage; V's copy may come from the forward, see
+ * DSA_BWD_V_FROM_FORWARD):
+ *   dsa_sparse_attn_bwd_preprocess  fills the workspace from K, V, O, dO, LSE
+ *                                   (Q is not read; _ex: with the flags of
+ *                                   dsa_sparse_attn_bwd_ex);
+ *   dsa_sparse_attn_bwd_dkdv        dK, dV from the reverse index and the bf16
+ *                                   inputs Q, K, V, dO (every key row of every
+ *                                   block is written); it also writes its own
+ *                                   task order (blocks with long reverse lists
+ *                                   first) into the workspace before the launch;
+ *   dsa_sparse_attn_bwd_dq          dQ from the kept-block lists, Q, dO and the
+ *                                   workspace.
  */
 int dsa_sparse_attn_bwd_preprocess(const dsa_problem* p, const void* Q, const void* K, const void* V, const float* O,
                                    const void* dO, const float* LSE, void* workspace, size_t workspace_bytes,
                                    void* stream);
-int dsa_sparse_attn_bwd_dkdv(const dsa_problem* p, const int32_t* k_per_head, const int32_t* rev_ptr,
-                             const int32_t* rev_idx, float* dK, float* dV, void* workspace, size_t workspace_bytes,
-                             void* stream);
-int dsa_sparse_attn_bwd_dq(const dsa_problem* p, const int32_t* idx, const int32_t* k_per_head, float* dQ,
-                           void* workspace, size_t workspace_bytes, void* stream);
+int dsa_sparse_attn_bwd_preprocess_ex(const dsa_problem* p, const void* Q, const void* K, const void* V,
+                                      const float* O, const void* dO, const float* LSE, int flags, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+int dsa_sparse_attn_bwd_dkdv(const dsa_problem* p, const void* Q, const void* K, const void* V, const void* dO,
+                             const int32_t* k_per_head, const int32_t* rev_ptr, const int32_t* rev_idx, float* dK,
+                             float* dV, void* workspace, size_t workspace_bytes, void* stream);
+int dsa_sparse_attn_bwd_dq(const dsa_problem* p, const void* Q, const void* dO, const int32_t* idx,
+                           const int32_t* k_per_head, float* dQ, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * The OP dispatcher's branches (hi and nl §2.A, stage 2: per transformer

@@ -80,18 +80,23 @@ def test_required_arguments():
     with pytest.raises(ValueError, match="idx"):
         dsa.sparse_attn_fwd(P, **_fwd_args(idx=None))
     with pytest.raises(ValueError, match="workspace"):
-        dsa.sparse_attn_bwd_dq(P, _t(torch.int32, P.list_len(KPH)), KPH, _t(torch.float32, P.elems), None)
+        dsa.sparse_attn_bwd_dq(P, _t(torch.bfloat16, P.elems), _t(torch.bfloat16, P.elems),
+                               _t(torch.int32, P.list_len(KPH)), KPH, _t(torch.float32, P.elems), None)
 
 
 def test_backward_and_selection_checks():
     n = P.list_len(KPH)
     grads = dict(dQ=_t(torch.float32, P.elems), dK=_t(torch.float32, P.elems), dV=_t(torch.float32, P.elems))
+    qkvo = [_t(torch.bfloat16, P.elems) for _ in range(4)]
     with pytest.raises(TypeError, match="dK"):
-        dsa.sparse_attn_bwd_dkdv(P, KPH, _t(torch.int32, 2 * 17), _t(torch.int32, n), _t(torch.float16, P.elems),
-                                 grads["dV"], _t(torch.uint8, 16))
+        dsa.sparse_attn_bwd_dkdv(P, *qkvo, KPH, _t(torch.int32, 2 * 17), _t(torch.int32, n),
+                                 _t(torch.float16, P.elems), grads["dV"], _t(torch.uint8, 16))
     with pytest.raises(ValueError, match="rev_ptr"):
-        dsa.sparse_attn_bwd_dkdv(P, KPH, _t(torch.int32, 2 * 17 - 1), _t(torch.int32, n), grads["dK"], grads["dV"],
-                                 _t(torch.uint8, 16))
+        dsa.sparse_attn_bwd_dkdv(P, *qkvo, KPH, _t(torch.int32, 2 * 17 - 1), _t(torch.int32, n), grads["dK"],
+                                 grads["dV"], _t(torch.uint8, 16))
+    with pytest.raises(TypeError, match="dO"):
+        dsa.sparse_attn_bwd_dkdv(P, *qkvo[:3], _t(torch.float32, P.elems), KPH, _t(torch.int32, 34),
+                                 _t(torch.int32, n), grads["dK"], grads["dV"], _t(torch.uint8, 16))
     scores = _t(torch.float32, 2 * 16 * 16)
     with pytest.raises(ValueError, match="scores"):
         dsa.select_topk_blocks(P, scores[:-1], None, None, KPH, _t(torch.int32, n), _t(torch.int32, 34),

@@ -62,8 +62,12 @@ int check_heads(const Shape& s, const int32_t* kph, HeadTable* ht, int* kmax) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// the selection's scratch: per-block counts [B*H*NB] int32, then the membership bitmaps of every 32 groups
+// [B*H, ceil(NG/32), NB] uint32 (the reverse index is built from them)
+size_t select_counts_bytes(const Shape& s) { return align256((size_t)s.B * s.H * s.NB * sizeof(int32_t)); }
 size_t select_ws(const Shape& s, const HeadTable& ht) {
-  return align256((size_t)s.B * s.H * s.NB * sizeof(int32_t)) + align256((size_t)s.B * s.NG * ht.ksum * sizeof(int32_t));
+  (void)ht;
+  return select_counts_bytes(s) + align256((size_t)s.B * s.H * ((s.NG + 31) / 32) * s.NB * sizeof(uint32_t));
 }
 
 // The forward's workspace (bf16 inputs) and the start of the backward's: the exponent table of the scaled
@@ -162,7 +166,7 @@ size_t sparse_extra_bytes(const Shape& s, const HeadTable& ht) {
 
 // ---------------------------------------------------------------- the selection without a caller workspace
 //
-// For callers that cannot allocate: its scratch (the reverse index's counters and scatter buffer) is this
+// For callers that cannot allocate: its scratch (the reverse index's counts and membership bitmaps) is this
 // static device array, one per GPU the library runs on, held until the process ends.  Host code never
 // passes the array's name to a kernel (on the host it is only a stand-in for the device symbol): the
 // device address comes from hipGetSymbolAddress, looked up once per device with that device current.
@@ -276,18 +280,15 @@ static int select_check(const dsa_problem* p, const float* scores, const float* 
   return DSA_OK;
 }
 
-// The selection's launches, scratch given as a select-layout workspace (counters, then the scatter buffer).
+// The selection's launches, scratch given as a select-layout workspace (counts, then the bitmaps).
 static int select_launch(const Shape& s, const HeadTable& ht, int kmax, int diag, const float* scores,
                          const float* qhat, const float* khat, int32_t* idx, int32_t* cnt, float coverage,
                          int32_t* rev_ptr, int32_t* rev_idx, float* scores_dump, void* workspace, hipStream_t hs) {
   const float tau = 1.0f / sqrtf((float)s.D);
-  int32_t* counters = static_cast<int32_t*>(workspace);
-  int32_t* scatter = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
-                                                align256((size_t)s.B * s.H * s.NB * sizeof(int32_t)));
-  hipError_t e = dsa::launch_topk_select(s, scores, qhat, khat, idx, scores ? nullptr : scores_dump, ht, tau, kmax, hs,
-                                         cnt, coverage, diag);
-  if (e == hipSuccess) e = dsa::launch_reverse_index(s, idx, rev_ptr, rev_idx, counters, scatter, ht, kmax, hs);
-  return hip_status(e);
+  int32_t* counts = static_cast<int32_t*>(workspace);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + select_counts_bytes(s));
+  return hip_status(dsa::launch_select(s, scores, qhat, khat, idx, scores ? nullptr : scores_dump, ht, tau, kmax,
+                                       rev_ptr, rev_idx, counts, bits, hs, cnt, coverage, diag));
 }
 
 static int select_impl(const dsa_problem* p, const float* scores, const float* qhat, const float* khat,

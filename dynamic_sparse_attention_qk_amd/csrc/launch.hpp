@@ -19,14 +19,13 @@ hipError_t launch_pool_project(const Shape& s, const void* X, const float* W, fl
                                hipStream_t st, float* mean_out = nullptr);
 hipError_t launch_block_scores(const Shape& s, const float* qhat, const float* khat, float* scores,
                                float tau, hipStream_t st);
-// cnt (if not null): select by attention coverage (kept counts per row to cnt [B,H,NG], unused slots -1);
-// diag_group > 0: the blocks holding each group's own diag_group tokens are always kept
-hipError_t launch_topk_select(const Shape& s, const float* scores, const float* qhat, const float* khat,
-                              int32_t* idx, float* dump, const HeadTable& ht, float tau, int kmax,
-                              hipStream_t st, int32_t* cnt = nullptr, float coverage = 1.0f, int diag_group = 0);
-hipError_t launch_reverse_index(const Shape& s, const int32_t* idx, int32_t* rev_ptr, int32_t* rev_idx,
-                                int32_t* counters, int32_t* scratch, const HeadTable& ht, int kmax,
-                                hipStream_t st);
+// Selection and its reverse index.  cnt (if not null): select by attention coverage (kept counts per row to
+// cnt [B,H,NG], unused slots -1); diag_group > 0: the blocks holding each group's own diag_group tokens are
+// always kept.  Scratch: counts [B*H*NB] int32 and the membership bitmaps [B*H, ceil(NG/32), NB] uint32.
+hipError_t launch_select(const Shape& s, const float* scores, const float* qhat, const float* khat, int32_t* idx,
+                         float* dump, const HeadTable& ht, float tau, int kmax, int32_t* rev_ptr, int32_t* rev_idx,
+                         int32_t* counts, uint32_t* bits, hipStream_t st, int32_t* cnt = nullptr,
+                         float coverage = 1.0f, int diag_group = 0);
 // The forward's workspace (bf16 inputs): the exponent table [4][B*H] (the forward writes the V entry), the
 // partial maxima [4][B*H][kAmaxChunks] and the scaled fp16 copy of V.  Its layout is the start of the
 // backward's, so a backward given the same workspace can reuse the copy.

@@ -237,7 +237,7 @@ int dsa_sparse_attn_bwd_ex(const dsa_problem* p, const void* Q, const void* K, c
  * k = 102, 24 heads each).  Every call on one GPU shares that array: calls
  * that overlap on one GPU (on different streams, or from several threads
  * without ordering) race and give undefined lists; calls ordered on one
- * stream do not (the counters are cleared by a kernel at each call).
+ * stream do not (each call writes all the scratch it reads).
  */
 int dsa_select_topk_blocks_noalloc(const dsa_problem* p, const float* scores, const float* qhat,
                                    const float* khat, const int32_t* k_per_head, int32_t* idx,

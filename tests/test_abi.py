@@ -96,7 +96,8 @@ def test_workspace_checks():
     p = _p()
     kph = [4, 4]
     need = dsa.workspace_bytes(p, kph, dsa.DSA_WS_SELECT)
-    assert need >= 2 * 16 * 4 + 16 * 8 * 4  # counters + scratch reverse list
+    # per-block counts [B*H, NB] + membership bitmaps [B*H, ceil(NG/32), NB] (NB = NG = 16 here)
+    assert need >= 2 * 16 * 4 + 2 * 1 * 16 * 4
     assert dsa.workspace_bytes(p, kph, dsa.DSA_WS_BWD) >= 2 * 1024 * 4
     assert dsa.workspace_bytes(_p(seq_len=1000), kph, 0) == 0
     st = lib.dsa_select_topk_blocks(ctypes.byref(p.c()), FAKE, FAKE, FAKE, dsa._kph(kph), FAKE, FAKE, FAKE, None,

@@ -728,23 +728,43 @@ __global__ __launch_bounds__(256) void rev_scan_kernel(const int32_t* __restrict
   if (threadIdx.x == 255) rp[NB] = part[255];
 }
 
-// rev_idx: block j's groups in ascending order (the set bits of its words, word by word), at its offset.
-__global__ __launch_bounds__(256) void rev_write_kernel(const uint32_t* __restrict__ bits,
-                                                        const int32_t* __restrict__ rev_ptr,
-                                                        int32_t* __restrict__ rev_idx, HeadTable ht, int NG, int NB,
-                                                        int W, int H) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
+// rev_idx: block j's groups in ascending order, at its offset.  A workgroup takes 64 consecutive blocks of
+// one (b, h): it copies their W bitmap words into LDS (coalesced rows, transposed by the padded stride), then
+// each wave writes whole lists, one block at a time -- lane l holds words l, l + 64, ..., a wave prefix sum
+// of their bit counts gives each lane its place in the list, and the lanes' stores land in one short span.
+constexpr int kRevBlocks = 64;
+constexpr int kRevWaves = 8;
+__global__ __launch_bounds__(kRevWaves * 64) void rev_write_kernel(const uint32_t* __restrict__ bits,
+                                                                   const int32_t* __restrict__ rev_ptr,
+                                                                   int32_t* __restrict__ rev_idx, HeadTable ht,
+                                                                   int NG, int NB, int W, int H) {
+  extern __shared__ uint32_t tile[];  // [W][kRevBlocks + 1]
+  const int j0 = blockIdx.x * kRevBlocks;
   const int bhi = blockIdx.y;
-  if (j >= NB) return;
   const int b = bhi / H, h = bhi % H;
-  const uint32_t* col = bits + (size_t)bhi * W * NB + j;
-  int32_t* out = rev_idx + row_base(ht, b, h, NG) + rev_ptr[(size_t)bhi * (NB + 1) + j];
-  int32_t pos = 0;
-  for (int w = 0; w < W; ++w) {
-    uint32_t m = col[(size_t)w * NB];
-    while (m) {
-      out[pos++] = 32 * w + __builtin_ctz(m);
-      m &= m - 1u;
+  const uint32_t* src = bits + (size_t)bhi * W * NB;
+  for (int e = threadIdx.x; e < W * kRevBlocks; e += kRevWaves * 64) {
+    const int w = e / kRevBlocks, jj = e % kRevBlocks;
+    tile[w * (kRevBlocks + 1) + jj] = j0 + jj < NB ? src[(size_t)w * NB + j0 + jj] : 0u;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t* out0 = rev_idx + row_base(ht, b, h, NG);
+  const int32_t* rp = rev_ptr + (size_t)bhi * (NB + 1);
+  for (int jj = wave; jj < kRevBlocks && j0 + jj < NB; jj += kRevWaves) {
+    int32_t* out = out0 + rp[j0 + jj];
+    uint32_t off = 0;
+    for (int w0 = 0; w0 < W; w0 += 64) {
+      const int w = w0 + lane;
+      uint32_t m = w < W ? tile[w * (kRevBlocks + 1) + jj] : 0u;
+      const uint32_t c = (uint32_t)__popc(m);
+      const uint32_t incl = wave_incl_sum(c);
+      uint32_t pos = off + incl - c;
+      while (m) {
+        out[pos++] = 32 * w + __builtin_ctz(m);
+        m &= m - 1u;
+      }
+      off += readlane(incl, 63);
     }
   }
 }
@@ -773,7 +793,9 @@ hipError_t launch_select(const Shape& s, const float* scores, const float* qhat,
   const dim3 gcol((s.NB + 255) / 256, s.B * s.H);
   hipLaunchKernelGGL(rev_count_kernel, gcol, dim3(256), 0, st, bits, counts, s.NB, W);
   hipLaunchKernelGGL(rev_scan_kernel, dim3(s.B * s.H), dim3(256), 0, st, counts, rev_ptr, s.NB);
-  hipLaunchKernelGGL(rev_write_kernel, gcol, dim3(256), 0, st, bits, rev_ptr, rev_idx, ht, s.NG, s.NB, W, s.H);
+  const size_t tile = (size_t)W * (kRevBlocks + 1) * sizeof(uint32_t);
+  hipLaunchKernelGGL(rev_write_kernel, dim3((s.NB + kRevBlocks - 1) / kRevBlocks, s.B * s.H), dim3(kRevWaves * 64),
+                     tile, st, bits, rev_ptr, rev_idx, ht, s.NG, s.NB, W, s.H);
   return hipGetLastError();
 }
 

@@ -28,8 +28,9 @@
 // Reverse index without atomics on global memory: each workgroup also builds,
 // in LDS, the membership bitmap of its 32 rows (bit g%32 of word j: row g kept
 // block j) and writes it once.  Then per (b, h): count the set bits of each
-// block's words, scan the counts into rev_ptr, and write each block's groups in
-// ascending order from its words -- deterministic by construction.
+// block's words, then per 64 blocks sum the counts before them and scan their
+// own into rev_ptr, and write each block's groups in ascending order from its
+// words -- deterministic by construction.
 #include "launch.hpp"
 
 namespace dsa {
@@ -287,11 +288,14 @@ __device__ __forceinline__ void kth_largest_scores(const float (&sc)[KPL], float
     auto bin = [](float s, float m0, float iv) {
       return (uint32_t)__builtin_amdgcn_fmed3f((s - m0) * iv, 0.f, 255.f);
     };
+    constexpr bool KEEP = KPL <= 32;  // short rows keep each score's bin (256 + lane: padding) for the gather
+    uint32_t bn[KEEP ? KPL : 1];
     const int lane1 = opaque(lane);
     reinterpret_cast<uint4*>(hist)[lane] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int t = 0; t < KPL; ++t) {
       const uint32_t bi = lane1 + 64 * t < NB ? bin(sc[t], mn, inv) : 256u + (uint32_t)lane;
+      if constexpr (KEEP) bn[t] = bi;
       __hip_atomic_fetch_add(&hist[bi], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       DSA_KEY_GROUP_FENCE(t);
     }
@@ -300,7 +304,10 @@ __device__ __forceinline__ void kth_largest_scores(const float (&sc)[KPL], float
     want -= bk.above;
     const float mn2 = opaque_f(mn), inv2 = opaque_f(inv);
     const int lane2 = opaque(lane);
-    auto in = [&](int t) { return lane2 + 64 * t < NB && bin(sc[t], mn2, inv2) == bk.b; };
+    auto in = [&](int t) {
+      if constexpr (KEEP) return bn[t] == bk.b;
+      else return lane2 + 64 * t < NB && bin(sc[t], mn2, inv2) == bk.b;
+    };
     if (bk.cnt <= 64u && bk.found) {
       const uint32_t nc = gather64<KPL>(hist, lane, in, [&](int t) { return __float_as_uint(sc[t]); });
       const bool real = (uint32_t)lane < nc;
@@ -701,58 +708,56 @@ __global__ __launch_bounds__(256) void rev_count_kernel(const uint32_t* __restri
   counts[bh * NB + j] = c;
 }
 
-// One workgroup per (b, h): exclusive scan of the NB counts into rev_ptr [B*H, NB + 1].
-__global__ __launch_bounds__(256) void rev_scan_kernel(const int32_t* __restrict__ counts,
-                                                       int32_t* __restrict__ rev_ptr, int NB) {
-  __shared__ int32_t part[256];
-  const size_t bh = blockIdx.x;
-  const int32_t* c = counts + bh * NB;
-  int32_t* rp = rev_ptr + bh * (NB + 1);
-  const int per = (NB + 255) / 256;
-  const int j0 = threadIdx.x * per;
-  int32_t local = 0;
-  for (int j = j0; j < j0 + per && j < NB; ++j) local += c[j];
-  part[threadIdx.x] = local;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {  // Hillis-Steele inclusive scan
-    const int32_t v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int32_t run = part[threadIdx.x] - local;
-  for (int j = j0; j < j0 + per && j < NB; ++j) {
-    rp[j] = run;
-    run += c[j];
-  }
-  if (threadIdx.x == 255) rp[NB] = part[255];
-}
-
-// rev_idx: block j's groups in ascending order, at its offset.  A workgroup takes 64 consecutive blocks of
-// one (b, h): it copies their W bitmap words into LDS (coalesced rows, transposed by the padded stride), then
-// each wave writes whole lists, one block at a time -- lane l holds words l, l + 64, ..., a wave prefix sum
-// of their bit counts gives each lane its place in the list, and the lanes' stores land in one short span.
+// rev_ptr and rev_idx: block j's groups in ascending order, at its offset.  A workgroup takes 64 consecutive
+// blocks of one (b, h): it sums the counts of all blocks before them (its list offset) and scans its own 64
+// (writing their rev_ptr entries; the last workgroup also writes the total), copies their W bitmap words into
+// LDS (coalesced rows, transposed by the padded stride), then each wave writes whole lists, one block at a
+// time -- lane l holds words l, l + 64, ..., a wave prefix sum of their bit counts gives each lane its place
+// in the list, and the lanes' stores land in one short span.
 constexpr int kRevBlocks = 64;
 constexpr int kRevWaves = 8;
 __global__ __launch_bounds__(kRevWaves * 64) void rev_write_kernel(const uint32_t* __restrict__ bits,
-                                                                   const int32_t* __restrict__ rev_ptr,
+                                                                   const int32_t* __restrict__ counts,
+                                                                   int32_t* __restrict__ rev_ptr,
                                                                    int32_t* __restrict__ rev_idx, HeadTable ht,
                                                                    int NG, int NB, int W, int H) {
   extern __shared__ uint32_t tile[];  // [W][kRevBlocks + 1]
+  __shared__ int32_t part[kRevWaves];
+  __shared__ int32_t ofs[kRevBlocks + 1];
   const int j0 = blockIdx.x * kRevBlocks;
   const int bhi = blockIdx.y;
   const int b = bhi / H, h = bhi % H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t* cnt = counts + (size_t)bhi * NB;
+  int32_t* rp = rev_ptr + (size_t)bhi * (NB + 1);
+  // entries of the blocks before j0
+  int32_t before = 0;
+  for (int j = threadIdx.x; j < j0; j += kRevWaves * 64) before += cnt[j];
+  before = (int32_t)readlane(wave_incl_sum((uint32_t)before), 63);
+  if (lane == 0) part[wave] = before;
   const uint32_t* src = bits + (size_t)bhi * W * NB;
   for (int e = threadIdx.x; e < W * kRevBlocks; e += kRevWaves * 64) {
     const int w = e / kRevBlocks, jj = e % kRevBlocks;
     tile[w * (kRevBlocks + 1) + jj] = j0 + jj < NB ? src[(size_t)w * NB + j0 + jj] : 0u;
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave == 0) {
+    int32_t base = 0;
+#pragma unroll
+    for (int i = 0; i < kRevWaves; ++i) base += part[i];
+    const int32_t c = j0 + lane < NB ? cnt[j0 + lane] : 0;
+    const int32_t incl = (int32_t)wave_incl_sum((uint32_t)c);
+    ofs[lane] = base + incl - c;
+    if (j0 + lane < NB) rp[j0 + lane] = base + incl - c;
+    if (lane == 63) {
+      ofs[64] = base + incl;
+      if (j0 + kRevBlocks >= NB) rp[NB] = base + incl;
+    }
+  }
+  __syncthreads();
   int32_t* out0 = rev_idx + row_base(ht, b, h, NG);
-  const int32_t* rp = rev_ptr + (size_t)bhi * (NB + 1);
   for (int jj = wave; jj < kRevBlocks && j0 + jj < NB; jj += kRevWaves) {
-    int32_t* out = out0 + rp[j0 + jj];
+    int32_t* out = out0 + ofs[jj];
     uint32_t off = 0;
     for (int w0 = 0; w0 < W; w0 += 64) {
       const int w = w0 + lane;
@@ -792,10 +797,9 @@ hipError_t launch_select(const Shape& s, const float* scores, const float* qhat,
   const int W = (s.NG + kRowsPerWg - 1) / kRowsPerWg;
   const dim3 gcol((s.NB + 255) / 256, s.B * s.H);
   hipLaunchKernelGGL(rev_count_kernel, gcol, dim3(256), 0, st, bits, counts, s.NB, W);
-  hipLaunchKernelGGL(rev_scan_kernel, dim3(s.B * s.H), dim3(256), 0, st, counts, rev_ptr, s.NB);
   const size_t tile = (size_t)W * (kRevBlocks + 1) * sizeof(uint32_t);
   hipLaunchKernelGGL(rev_write_kernel, dim3((s.NB + kRevBlocks - 1) / kRevBlocks, s.B * s.H), dim3(kRevWaves * 64),
-                     tile, st, bits, rev_ptr, rev_idx, ht, s.NG, s.NB, W, s.H);
+                     tile, st, bits, counts, rev_ptr, rev_idx, ht, s.NG, s.NB, W, s.H);
   return hipGetLastError();
 }
 

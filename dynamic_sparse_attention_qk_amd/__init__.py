@@ -25,7 +25,9 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdsa.so")
+# DSA_LIBRARY selects another build of the same library (libdsa_debug.so: list checks; libdsa_san.so: host code
+# under AddressSanitizer and UndefinedBehaviorSanitizer), by name within the package or as a path
+LIB_PATH = os.path.join(_PKG, os.environ.get("DSA_LIBRARY", "libdsa.so"))
 
 DSA_F32, DSA_BF16 = 0, 1
 DSA_WS_SELECT, DSA_WS_BWD, DSA_WS_FWD, DSA_WS_PRED_GRAD, DSA_WS_PRED_POOLED = 0, 1, 2, 3, 4
@@ -46,61 +48,68 @@ _lib = None
 
 
 def library() -> ctypes.CDLL:
-    """The loaded libdsa.so; raises if it has not been built."""
+    """The loaded libdsa.so (or the build DSA_LIBRARY names); raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with "
-                              "`python -m dynamic_sparse_attention_qk_amd.build` (hipcc, gfx950)")
-        lib = ctypes.CDLL(LIB_PATH)
-        vp, i32p, i64p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p
-        pp = ctypes.POINTER(_Problem)
-        kph = ctypes.POINTER(ctypes.c_int32)
-        lib.dsa_version.restype = ctypes.c_char_p
-        lib.dsa_status_string.restype = ctypes.c_char_p
-        lib.dsa_status_string.argtypes = [ctypes.c_int]
-        lib.dsa_index_layout.argtypes = [pp, kph, i64p]
-        lib.dsa_workspace_bytes.restype = ctypes.c_size_t
-        lib.dsa_workspace_bytes.argtypes = [pp, kph, ctypes.c_int]
-        lib.dsa_predict_block_scores.argtypes = [pp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp]
-        lib.dsa_select_topk_blocks.argtypes = [pp, f32p, f32p, f32p, kph, i32p, i32p, i32p, f32p, vp,
-                                               ctypes.c_size_t, vp]
-        lib.dsa_select_topk_blocks_noalloc.argtypes = [pp, f32p, f32p, f32p, kph, i32p, i32p, i32p, f32p, vp]
-        lib.dsa_sparse_attn_fwd.argtypes = [pp, vp, vp, vp, i32p, kph, f32p, f32p, vp, ctypes.c_size_t, vp]
-        lib.dsa_sparse_attn_bwd.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, kph, i32p, i32p, f32p, f32p,
-                                            f32p, vp, ctypes.c_size_t, vp]
-        sz = ctypes.c_size_t
-        lib.dsa_sparse_attn_bwd_ex.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, kph, i32p, i32p, f32p, f32p,
-                                               f32p, ctypes.c_int, vp, ctypes.c_size_t, vp]
-        lib.dsa_sparse_attn_bwd_preprocess.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, vp, sz, vp]
-        lib.dsa_sparse_attn_bwd_preprocess_ex.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, ctypes.c_int, vp, sz, vp]
-        lib.dsa_sparse_attn_bwd_dkdv.argtypes = [pp, vp, vp, vp, vp, kph, i32p, i32p, f32p, f32p, vp, sz, vp]
-        lib.dsa_sparse_attn_bwd_dq.argtypes = [pp, vp, vp, i32p, kph, f32p, vp, sz, vp]
-        lib.dsa_sparse_attn_fwd_split.argtypes = [pp, vp, vp, vp, i32p, kph, ctypes.c_int, f32p, f32p, vp, sz, vp]
-        lib.dsa_attn_merge.argtypes = [pp, ctypes.c_int, f32p, f32p, f32p, f32p, vp]
-        lib.dsa_dense_attn_fwd.argtypes = [pp, vp, vp, vp, f32p, f32p, vp, sz, vp]
-        lib.dsa_dense_attn_bwd.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, f32p, f32p, f32p, vp, sz, vp]
-        lib.dsa_choose_path.argtypes = [pp, kph, ctypes.c_double, sz]
-        lib.dsa_predictor_loss_grad.argtypes = [pp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp, sz, vp]
-        lib.dsa_select_coverage_blocks.argtypes = [pp, f32p, f32p, f32p, kph, ctypes.c_double, i32p, i32p, i32p,
-                                                   i32p, f32p, vp, sz, vp]
-        lib.dsa_sparse_attn_fwd_varlen.argtypes = [pp, vp, vp, vp, i32p, i32p, kph, f32p, f32p, vp, sz, vp]
-        lib.dsa_predict_block_scores_pooled.argtypes = [pp, vp, vp, f32p, f32p, ctypes.c_int, f32p, vp, sz, vp]
-        lib.dsa_select_blocks.argtypes = [pp, f32p, f32p, f32p, kph, ctypes.c_double, ctypes.c_int, i32p, i32p, i32p,
-                                          i32p, f32p, vp, sz, vp]
-        lib.dsa_sparse_attn_bwd_varlen.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, i32p, kph, i32p, i32p,
-                                                   f32p, f32p, f32p, vp, sz, vp]
-        for name in ("dsa_index_layout", "dsa_predict_block_scores", "dsa_select_topk_blocks",
-                     "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_preprocess",
-                     "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_fwd_split",
-                     "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd", "dsa_choose_path",
-                     "dsa_predictor_loss_grad", "dsa_select_coverage_blocks", "dsa_sparse_attn_fwd_varlen",
-                     "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks", "dsa_predict_block_scores_pooled",
-                     "dsa_select_topk_blocks_noalloc", "dsa_sparse_attn_bwd_ex",
-                     "dsa_sparse_attn_bwd_preprocess_ex"):
-            getattr(lib, name).restype = ctypes.c_int
-        _lib = lib
+        _lib = load_library(LIB_PATH)
     return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Loads one build of the library (path, or a name within the package) with the C signatures set."""
+    if not os.path.isabs(path):
+        path = os.path.join(_PKG, path)
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m dynamic_sparse_attention_qk_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    vp, i32p, i64p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p
+    pp = ctypes.POINTER(_Problem)
+    kph = ctypes.POINTER(ctypes.c_int32)
+    lib.dsa_version.restype = ctypes.c_char_p
+    lib.dsa_status_string.restype = ctypes.c_char_p
+    lib.dsa_status_string.argtypes = [ctypes.c_int]
+    lib.dsa_index_layout.argtypes = [pp, kph, i64p]
+    lib.dsa_workspace_bytes.restype = ctypes.c_size_t
+    lib.dsa_workspace_bytes.argtypes = [pp, kph, ctypes.c_int]
+    lib.dsa_predict_block_scores.argtypes = [pp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp]
+    lib.dsa_select_topk_blocks.argtypes = [pp, f32p, f32p, f32p, kph, i32p, i32p, i32p, f32p, vp,
+                                           ctypes.c_size_t, vp]
+    lib.dsa_select_topk_blocks_noalloc.argtypes = [pp, f32p, f32p, f32p, kph, i32p, i32p, i32p, f32p, vp]
+    lib.dsa_sparse_attn_fwd.argtypes = [pp, vp, vp, vp, i32p, kph, f32p, f32p, vp, ctypes.c_size_t, vp]
+    lib.dsa_sparse_attn_bwd.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, kph, i32p, i32p, f32p, f32p,
+                                        f32p, vp, ctypes.c_size_t, vp]
+    sz = ctypes.c_size_t
+    lib.dsa_sparse_attn_bwd_ex.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, kph, i32p, i32p, f32p, f32p,
+                                           f32p, ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.dsa_sparse_attn_bwd_preprocess.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, vp, sz, vp]
+    lib.dsa_sparse_attn_bwd_preprocess_ex.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, ctypes.c_int, vp, sz, vp]
+    lib.dsa_sparse_attn_bwd_dkdv.argtypes = [pp, vp, vp, vp, vp, kph, i32p, i32p, f32p, f32p, vp, sz, vp]
+    lib.dsa_sparse_attn_bwd_dq.argtypes = [pp, vp, vp, i32p, kph, f32p, vp, sz, vp]
+    lib.dsa_sparse_attn_fwd_split.argtypes = [pp, vp, vp, vp, i32p, kph, ctypes.c_int, f32p, f32p, vp, sz, vp]
+    lib.dsa_attn_merge.argtypes = [pp, ctypes.c_int, f32p, f32p, f32p, f32p, vp]
+    lib.dsa_dense_attn_fwd.argtypes = [pp, vp, vp, vp, f32p, f32p, vp, sz, vp]
+    lib.dsa_dense_attn_bwd.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, f32p, f32p, f32p, vp, sz, vp]
+    lib.dsa_choose_path.argtypes = [pp, kph, ctypes.c_double, sz]
+    lib.dsa_predictor_loss_grad.argtypes = [pp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp, sz, vp]
+    lib.dsa_select_coverage_blocks.argtypes = [pp, f32p, f32p, f32p, kph, ctypes.c_double, i32p, i32p, i32p,
+                                               i32p, f32p, vp, sz, vp]
+    lib.dsa_sparse_attn_fwd_varlen.argtypes = [pp, vp, vp, vp, i32p, i32p, kph, f32p, f32p, vp, sz, vp]
+    lib.dsa_predict_block_scores_pooled.argtypes = [pp, vp, vp, f32p, f32p, ctypes.c_int, f32p, vp, sz, vp]
+    lib.dsa_select_blocks.argtypes = [pp, f32p, f32p, f32p, kph, ctypes.c_double, ctypes.c_int, i32p, i32p, i32p,
+                                      i32p, f32p, vp, sz, vp]
+    lib.dsa_sparse_attn_bwd_varlen.argtypes = [pp, vp, vp, vp, f32p, vp, f32p, i32p, i32p, kph, i32p, i32p,
+                                               f32p, f32p, f32p, vp, sz, vp]
+    for name in ("dsa_index_layout", "dsa_predict_block_scores", "dsa_select_topk_blocks",
+                 "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_preprocess",
+                 "dsa_sparse_attn_bwd_dkdv", "dsa_sparse_attn_bwd_dq", "dsa_sparse_attn_fwd_split",
+                 "dsa_attn_merge", "dsa_dense_attn_fwd", "dsa_dense_attn_bwd", "dsa_choose_path",
+                 "dsa_predictor_loss_grad", "dsa_select_coverage_blocks", "dsa_sparse_attn_fwd_varlen",
+                 "dsa_sparse_attn_bwd_varlen", "dsa_select_blocks", "dsa_predict_block_scores_pooled",
+                 "dsa_select_topk_blocks_noalloc", "dsa_sparse_attn_bwd_ex",
+                 "dsa_sparse_attn_bwd_preprocess_ex"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
 
 
 EXPORTED = ("dsa_version", "dsa_status_string", "dsa_index_layout", "dsa_workspace_bytes",

@@ -1,6 +1,12 @@
-"""Builds libdsa.so (all HIP sources, gfx950) in-tree with hipcc.
+"""Builds libdsa.so (all HIP sources, gfx950) in-tree with hipcc, and two variants of it that differ only in
+api.hip (the C ABI's host layer; every other object is shared):
+  libdsa_debug.so  compiled with DSA_DEBUG: the attention calls check their kept-block lists and reverse
+                   index on the device first and return DSA_ERR_BAD_LIST on a malformed one;
+  libdsa_san.so    the host code of api.hip under AddressSanitizer and UndefinedBehaviorSanitizer (device code
+                   unchanged); load it with the sanitizer runtime preloaded (tests/test_sanitized_abi.py).
+The binding loads a variant when DSA_LIBRARY names it.
 
-Usage: python -m dynamic_sparse_attention_qk_amd.build [--verbose]
+Usage: python -m dynamic_sparse_attention_qk_amd.build [--verbose] [--release-only]
 """
 from __future__ import annotations
 
@@ -15,7 +21,12 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
 SOURCES = ["api.hip", "predict.hip", "predict_train.hip", "predict_pooled.hip", "select.hip", "attn_fwd.hip",
-           "attn_bwd.hip"]
+           "attn_bwd.hip", "validate.hip"]
+DEBUG_LIB = os.path.join(PKG, "libdsa_debug.so")
+SAN_LIB = os.path.join(PKG, "libdsa_san.so")
+# host-only sanitizer flags: each -fsanitize applies to the host compilation alone (-Xarch_host)
+SAN_FLAGS = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -40,22 +51,38 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
-def build(verbose: bool = False, jobs: int = 5) -> str:
-    """Compile every HIP source and link libdsa.so; returns the library path."""
-    os.makedirs(OBJ, exist_ok=True)
+def _link(objs, lib, verbose, extra=()):
+    tmp = lib + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", tmp, *objs], verbose)
+    os.replace(tmp, lib)
 
-    def compile_one(src):
-        out = os.path.join(OBJ, src.replace(".hip", ".o"))
-        _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", out], verbose)
+
+def build(verbose: bool = False, jobs: int = 5, variants: bool = True) -> str:
+    """Compile every HIP source and link libdsa.so (and, with variants, libdsa_debug.so and libdsa_san.so);
+    returns the path of libdsa.so."""
+    os.makedirs(OBJ, exist_ok=True)
+    jobs_list = [(src, os.path.join(OBJ, src.replace(".hip", ".o")), FLAGS) for src in SOURCES]
+    if variants:
+        jobs_list += [("api.hip", os.path.join(OBJ, "api_debug.o"), FLAGS + ["-DDSA_DEBUG"]),
+                      ("api.hip", os.path.join(OBJ, "api_san.o"), [f for f in FLAGS if f != "-O3"] + ["-O1"] +
+                       SAN_FLAGS)]
+
+    def compile_one(job):
+        src, out, flags = job
+        _run([HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", out], verbose)
         return out
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
+        outs = list(ex.map(compile_one, jobs_list))
+    objs = outs[:len(SOURCES)]
+    _link(objs, LIB, verbose)
+    if variants:
+        rest = objs[1:]  # every object but api.o
+        _link([outs[len(SOURCES)]] + rest, DEBUG_LIB, verbose)
+        _link([outs[len(SOURCES) + 1]] + rest, SAN_LIB, verbose,
+              extra=["-fsanitize=address,undefined", "-shared-libsan"])
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    print(build(verbose="--verbose" in sys.argv, variants="--release-only" not in sys.argv))

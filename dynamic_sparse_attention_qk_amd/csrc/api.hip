@@ -1,6 +1,7 @@
 // C ABI of libdsa.so: argument validation on the host, then asynchronous
 // launches on the caller's stream.  Nothing here allocates device memory.
 #include <math.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <mutex>
@@ -188,13 +189,65 @@ static int scratch_for_stream(hipStream_t stream, void** out) {
     if (dev != cur && hipSetDevice(dev) != hipSuccess) return DSA_ERR_HIP;
     void* ptr = nullptr;
     const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
-    if (dev != cur) hipSetDevice(cur);
+    if (dev != cur) (void)hipSetDevice(cur);
     if (e != hipSuccess || !ptr) return DSA_ERR_HIP;
     g_scratch_ptr[dev] = ptr;
   }
   *out = g_scratch_ptr[dev];
   return DSA_OK;
 }
+
+// ---------------------------------------------------------------- list checks of the debug build
+#ifdef DSA_DEBUG
+static __device__ uint32_t dbg_err[4];  // first failure: code, where, position, value
+
+static const char* list_check_text(uint32_t code) {
+  switch (code) {
+    case dsa::kListBadCount: return "a per-row count outside [1, k_h]";
+    case dsa::kListOutOfRange: return "a kept block id outside [0, NB)";
+    case dsa::kListNotAscending: return "kept block ids not strictly ascending";
+    case dsa::kListBadPadding: return "a slot past the row's count is not -1";
+    case dsa::kRevBadPointer: return "rev_ptr not starting at 0, decreasing, or past NG * k_h";
+    case dsa::kRevOutOfRange: return "a reverse-list group id outside [0, NG)";
+    case dsa::kRevNotAscending: return "a reverse list not strictly ascending";
+    default: return "unknown list error";
+  }
+}
+
+// Checks the lists a call is about to read (any may be null) on the stream's device and waits for the result.
+static int debug_check_lists(const Shape& s, const HeadTable& ht, const int32_t* idx, const int32_t* cnt,
+                             const int32_t* rev_ptr, const int32_t* rev_idx, void* stream, const char* call) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int dev = 0, cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return DSA_ERR_HIP;
+  dev = cur;
+  if (st && hipStreamGetDevice(st, &dev) != hipSuccess) return DSA_ERR_HIP;
+  if (dev != cur && hipSetDevice(dev) != hipSuccess) return DSA_ERR_HIP;
+  uint32_t* err = nullptr;
+  uint32_t h[4] = {0, 0, 0, 0};
+  hipError_t e = hipGetSymbolAddress(reinterpret_cast<void**>(&err), HIP_SYMBOL(dbg_err));
+  if (e == hipSuccess) e = hipMemsetAsync(err, 0, sizeof(h), st);
+  if (e == hipSuccess) e = dsa::launch_check_lists(s, ht, idx, cnt, rev_ptr, rev_idx, err, st);
+  if (e == hipSuccess) e = hipMemcpyAsync(h, err, sizeof(h), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (dev != cur) (void)hipSetDevice(cur);
+  if (e != hipSuccess) return DSA_ERR_HIP;
+  if (h[0] == 0) return DSA_OK;
+  fprintf(stderr, "dsa (debug build) %s: %s -- %s %u, position %d, value %d\n", call, list_check_text(h[0]),
+          h[0] >= dsa::kRevBadPointer ? "(b*H + h)*NB + block" : "row (b*H + h)*NG + g", h[1], (int)h[2],
+          (int)h[3]);
+  return DSA_ERR_BAD_LIST;
+}
+#define DSA_CHECK_LISTS(...)                          \
+  do {                                                \
+    const int check_status_ = debug_check_lists(__VA_ARGS__); \
+    if (check_status_) return check_status_;          \
+  } while (0)
+#else
+#define DSA_CHECK_LISTS(...) \
+  do {                       \
+  } while (0)
+#endif
 
 extern "C" {
 
@@ -211,6 +264,7 @@ const char* dsa_status_string(int status) {
     case DSA_ERR_WORKSPACE: return "workspace missing or too small";
     case DSA_ERR_HIP: return "HIP runtime or launch error";
     case DSA_ERR_SCRATCH_LIMIT: return "problem needs more scratch than the library's static buffer holds";
+    case DSA_ERR_BAD_LIST: return "malformed kept-block list or reverse index (debug build check)";
     default: return "unknown status";
   }
 }
@@ -387,6 +441,7 @@ static int fwd_impl(const dsa_problem* p, const void* Q, const void* K, const vo
   const size_t need = fwd_ws(s);
   if (need && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
   if (need && !aligned16(workspace)) return DSA_ERR_ALIGN;
+  DSA_CHECK_LISTS(s, ht, idx, cnt, nullptr, nullptr, stream, cnt ? "sparse_attn_fwd_varlen" : "sparse_attn_fwd");
   return hip_status(dsa::launch_attn_fwd(s, Q, K, V, idx, O, LSE, fwd_work(s, workspace), ht, 1,
                                          static_cast<hipStream_t>(stream), cnt));
 }
@@ -421,6 +476,7 @@ int dsa_sparse_attn_fwd_split(const dsa_problem* p, const void* Q, const void* K
   const size_t need = fwd_ws(s);
   if (need && (!workspace || workspace_bytes < need)) return DSA_ERR_WORKSPACE;
   if (need && !aligned16(workspace)) return DSA_ERR_ALIGN;
+  DSA_CHECK_LISTS(s, ht, idx, nullptr, nullptr, nullptr, stream, "sparse_attn_fwd_split");
   return hip_status(dsa::launch_attn_fwd(s, Q, K, V, idx, O_part, LSE_part, fwd_work(s, workspace), ht, n_split,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -482,6 +538,7 @@ int dsa_sparse_attn_bwd_dkdv(const dsa_problem* p, const void* Q, const void* K,
       !aligned16(rev_idx) || !aligned16(dK) || !aligned16(dV))
     return DSA_ERR_ALIGN;
   if ((st = check_ws(s, workspace, workspace_bytes))) return st;
+  DSA_CHECK_LISTS(s, ht, nullptr, nullptr, rev_ptr, rev_idx, stream, "sparse_attn_bwd_dkdv");
   return hip_status(dsa::launch_bwd_dkdv(s, bwd_work(s, workspace), Q, K, V, dO, rev_ptr, rev_idx, dK, dV, ht,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -496,6 +553,7 @@ int dsa_sparse_attn_bwd_dq(const dsa_problem* p, const void* Q, const void* dO, 
   if (!Q || !dO || !idx || !dQ) return DSA_ERR_INVALID_ARG;
   if (!aligned16(Q) || !aligned16(dO) || !aligned16(idx) || !aligned16(dQ)) return DSA_ERR_ALIGN;
   if ((st = check_ws(s, workspace, workspace_bytes))) return st;
+  DSA_CHECK_LISTS(s, ht, idx, nullptr, nullptr, nullptr, stream, "sparse_attn_bwd_dq");
   return hip_status(dsa::launch_bwd_dq(s, bwd_work(s, workspace), Q, dO, idx, dQ, ht, static_cast<hipStream_t>(stream)));
 }
 
@@ -515,6 +573,7 @@ static int bwd_impl(const dsa_problem* p, const void* Q, const void* K, const vo
       !aligned16(dV))
     return DSA_ERR_ALIGN;
   if ((st = check_ws(s, workspace, workspace_bytes))) return st;
+  DSA_CHECK_LISTS(s, ht, idx, cnt, rev_ptr, rev_idx, stream, cnt ? "sparse_attn_bwd_varlen" : "sparse_attn_bwd");
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const dsa::BwdWork w = bwd_work(s, workspace);
   hipError_t e = dsa::launch_bwd_pre(s, Q, K, V, O, dO, LSE, w, (flags & DSA_BWD_V_FROM_FORWARD) != 0, hs);

@@ -84,4 +84,19 @@ struct PredWork {
 hipError_t launch_predictor_loss_grad(const Shape& s, const void* Q, const void* K, const float* Wq, const float* Wk,
                                       const PredWork& w, float* loss, float* dWq, float* dWk, hipStream_t st);
 
+// Debug builds: checks of the kept-block lists (idx, optional per-row counts cnt) and of the reverse index
+// (rev_ptr, rev_idx); either may be null.  The first failure found goes to err[0..3] (code, row or
+// (b, h, block), position, value), which the caller clears beforehand.
+enum ListCheck : uint32_t {
+  kListBadCount = 1,     // a per-row count outside [1, k_h]
+  kListOutOfRange = 2,   // a kept block id outside [0, NB)
+  kListNotAscending = 3, // a row's ids not strictly ascending (a repeat included)
+  kListBadPadding = 4,   // a slot past a row's count not -1
+  kRevBadPointer = 5,    // rev_ptr not starting at 0, decreasing, or past NG * k_h
+  kRevOutOfRange = 6,    // a reverse-list group id outside [0, NG)
+  kRevNotAscending = 7,  // a reverse list not strictly ascending
+};
+hipError_t launch_check_lists(const Shape& s, const HeadTable& ht, const int32_t* idx, const int32_t* cnt,
+                              const int32_t* rev_ptr, const int32_t* rev_idx, uint32_t* err, hipStream_t st);
+
 }  // namespace dsa

@@ -35,6 +35,15 @@
  *    mutable global state other than that scratch array (see its call).
  *  - Limits: d in {64, 128}; rank r in {8, 16, 32, 64}; H <= 128;
  *    NB <= 8192 (N <= 524288); B*H*NG*max(k_h) < 2^31.
+ *  - Lists are taken as written by the selection calls: each idx row strictly
+ *    ascending in [0, NB) (with counts: the first cnt entries, the rest -1),
+ *    rev_ptr starting at 0 and non-decreasing, each reverse list strictly
+ *    ascending in [0, NG).  The release library clamps every id it reads
+ *    into range, so a malformed list gives wrong results, never an access out
+ *    of bounds.  The debug build (libdsa_debug.so, compiled with DSA_DEBUG)
+ *    checks the lists of every attention call on the device first,
+ *    synchronises the stream, prints the first bad entry to stderr and returns
+ *    DSA_ERR_BAD_LIST without launching the attention kernels.
  */
 #ifndef DSA_H_
 #define DSA_H_
@@ -55,7 +64,8 @@ typedef enum {
   DSA_ERR_UNSUPPORTED = -5,   /* combination outside the limits above */
   DSA_ERR_WORKSPACE = -6,     /* workspace missing or too small */
   DSA_ERR_HIP = -7,           /* a HIP launch or runtime call failed */
-  DSA_ERR_SCRATCH_LIMIT = -8  /* a call without a workspace needs more than its static scratch */
+  DSA_ERR_SCRATCH_LIMIT = -8, /* a call without a workspace needs more than its static scratch */
+  DSA_ERR_BAD_LIST = -9       /* debug builds only: a kept-block list or reverse index is malformed */
 } dsa_status;
 
 typedef enum { DSA_F32 = 0, DSA_BF16 = 1 } dsa_dtype;

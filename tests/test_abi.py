@@ -126,7 +126,7 @@ def test_index_layout_ragged():
 
 
 def test_status_strings():
-    for s in range(0, -8, -1):
+    for s in range(0, -10, -1):
         assert dsa.status_string(s) != "unknown status"
     assert dsa.status_string(5) == "unknown status"
 

@@ -50,6 +50,9 @@ def parse():
                     help="also time the step captured once in a HIP graph and replayed")
     ap.add_argument("--predictor-grad", action="store_true",
                     help="also time the stage-1 predictor loss + gradient call on the same inputs")
+    ap.add_argument("--cold-reps", type=int, default=-1,
+                    help="repetitions of the cache-flushed protocol (median and min; -1: 20, or 5 at >= 256k "
+                         "tokens; 0: off)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (counter calibration)")
     return ap.parse_args()
@@ -440,6 +443,26 @@ def main():
     # per-kernel durations from the events recorded between the launches of the timed steps
     stage_ms = {n: float(np.mean([m[i].elapsed_time(m[i + 1]) for m in marks])) for i, n in enumerate(names)}
 
+    # cache-flushed protocol: before each repetition a 512 MiB write (twice the 256 MiB MALL, far above the
+    # 32 MiB of L2) evicts what the previous step left in the caches; each repetition is timed alone and the
+    # median and min are reported beside the K-step mean above
+    cold = None
+    reps = args.cold_reps if args.cold_reps >= 0 else (5 if w.seq_len >= 262144 else 20)
+    if reps > 0:
+        flush = torch.empty(512 << 18, dtype=torch.int32, device=dev)
+        cmarks = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(reps)]
+        for r in range(reps):
+            with torch.cuda.stream(stream):
+                flush.fill_(r)
+            step(cmarks[r])
+        torch.cuda.synchronize()
+        del flush
+        per_rep = [m[0].elapsed_time(m[-1]) for m in cmarks]
+        cold = {"reps": reps, "flush_mib": 512, "ms_per_step_median": float(np.median(per_rep)),
+                "ms_per_step_min": float(np.min(per_rep)),
+                "stage_ms_median": {n: round(float(np.median([m[i].elapsed_time(m[i + 1]) for m in cmarks])), 4)
+                                    for i, n in enumerate(names)}}
+
     pairs = kept_pairs(w, kph)
     unit = 64 * w.group * w.head_dim            # G x Bk x d per kept (group, block) pair
     f_fwd = 4.0 * unit * pairs
@@ -488,6 +511,13 @@ def main():
                         "frac": round(pred_bytes / (stage_ms["predict"] / 1e3) / PEAK_HBM, 4)},
             "select": {"bytes": sel_bytes, "gbs": round(sel_bytes / (stage_ms["select"] / 1e3) / 1e9, 1),
                        "frac": round(sel_bytes / (stage_ms["select"] / 1e3) / PEAK_HBM, 4)}},
+        "cold_cache": None if cold is None else {
+            "reps": cold["reps"], "flush_mib": cold["flush_mib"],
+            "ms_per_step_median": round(cold["ms_per_step_median"], 4),
+            "ms_per_step_min": round(cold["ms_per_step_min"], 4),
+            "tflops_median": round((f_fwd + f_bwd) / (cold["ms_per_step_median"] / 1e3) / 1e12, 3),
+            "tflops_best": round((f_fwd + f_bwd) / (cold["ms_per_step_min"] / 1e3) / 1e12, 3),
+            "stage_ms_median": cold["stage_ms_median"]},
         "roofline": {"kernel": kernel_names[dom], "bound": "mfma", "achieved": round(dom_tflops, 2),
                      "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(dom_tflops * 1e12 / peak, 4),
                      "traffic": traffic},

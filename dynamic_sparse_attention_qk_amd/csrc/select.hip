@@ -58,15 +58,6 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-template <int KPL>
-__device__ __forceinline__ float wave_mass_ge(const uint32_t (&key)[KPL], const float (&e)[KPL], uint32_t cand) {
-  float m = 0.f;
-#pragma unroll
-  for (int t = 0; t < KPL; ++t) m += key[t] >= cand ? e[t] : 0.f;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) m += __shfl_xor(m, off);
-  return m;
-}
 
 // DPP lane moves (GFX9 encodings): row_shr:n shifts within each 16-lane row (lanes shifted in read 0 with
 // bound_ctrl); row_bcast:15 / :31 pass lane 15 / 31 of a row to the rows selected by the row mask.
@@ -148,6 +139,27 @@ __device__ __forceinline__ float wave_max_f(float v) {
   v = fmaxf(v, dppf<0x142, 0xa>(v, I));
   v = fmaxf(v, dppf<0x143, 0xc>(v, I));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Sum over the 64 lanes as a wave-uniform value: an inclusive prefix sum by DPP (a fixed order, so the same
+// inputs always give the same bits), read at lane 63.
+__device__ __forceinline__ float wave_sum_f(float v) {
+  v += dppf<0x111, 0xf>(v, 0.f);
+  v += dppf<0x112, 0xf>(v, 0.f);
+  v += dppf<0x114, 0xf>(v, 0.f);
+  v += dppf<0x118, 0xf>(v, 0.f);
+  v += dppf<0x142, 0xa>(v, 0.f);
+  v += dppf<0x143, 0xc>(v, 0.f);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Mass of the row's keys >= cand (e: each key's mass, 0 for padding).
+template <int KPL>
+__device__ __forceinline__ float wave_mass_ge(const uint32_t (&key)[KPL], const float (&e)[KPL], uint32_t cand) {
+  float m = 0.f;
+#pragma unroll
+  for (int t = 0; t < KPL; ++t) m += key[t] >= cand ? e[t] : 0.f;
+  return wave_sum_f(m);
 }
 
 // The bucket of this wave's 256-bin histogram (just filled) that holds the want-th largest counted key:

@@ -591,7 +591,7 @@ hipError_t dkdv_launch(const Shape& s, const BwdWork& w, const bf16_t* Q, const 
   const float tau = 1.0f / sqrtf((float)D);
   // a KV block costs its reverse-list length, NG * k_h / NB on average, + 1; a head streams its Q and dO
   unsigned nwg = 0;
-  const double head_bytes = 4.0 * s.N * D;  // one head's Q and dO (fp16 copies)
+  const double head_bytes = 4.0 * s.N * D;  // one head's Q and dO (16-bit)
   const int nph = head_bytes > 0.5 * kMallBytes ? kMallPhasesQdO : 1;  // phases over segments of every list
   const XcdSplit sp = make_xcd_split(s.B, s.H, s.NB, ht, (double)s.NG / s.NB / nph, 1.0, head_bytes, &nwg);
   const unsigned nseg = sp.items ? kXcds * (unsigned)sp.runs : kXcds;
@@ -616,7 +616,7 @@ hipError_t dq_launch(const Shape& s, const BwdWork& w, const bf16_t* Q, const bf
                      const int32_t* cnt, float* dQ, const HeadTable& ht, hipStream_t st) {
   const float tau = 1.0f / sqrtf((float)D);
   unsigned nwg = 0;
-  const double head_bytes = 4.0 * s.N * D;  // one head's K and V (fp16 copies)
+  const double head_bytes = 4.0 * s.N * D;  // one head's K and V (their fp16 copies)
   if (head_bytes > 0.5 * kMallBytes) {  // phases over segments of every list, each streaming ~1/kMallPhasesKV
     const XcdSplit sp = make_xcd_split(s.B, s.H, s.NG, ht, 1.0 / kMallPhasesKV, 1.0, head_bytes, &nwg);
     auto kern = idx ? bwd_dq_kernel<D, G, true, true> : bwd_dq_kernel<D, G, false, true>;

@@ -52,23 +52,46 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__
   const int sub = threadIdx.x % LPR;
   const int64_t r0 = (int64_t)bh * N + (int64_t)N * blockIdx.x / gridDim.x;
   const int64_t r1 = (int64_t)bh * N + (int64_t)N * (blockIdx.x + 1) / gridDim.x;
-  for (int64_t row = r0 + threadIdx.x / LPR; row < r1; row += RPB) {
-    const int64_t at = row * D + 8 * sub;
-    *reinterpret_cast<uint4*>(K16 + at) = bf16x8_to_f16x8_scaled(ldg16(K + at), eK);
-    if (convert_v) *reinterpret_cast<uint4*>(V16 + at) = bf16x8_to_f16x8_scaled(ldg16(V + at), eV);
-    const uint4 d = ldg16(dO + at);
-    const float4 o0 = *reinterpret_cast<const float4*>(O + at);
-    const float4 o1 = *reinterpret_cast<const float4*>(O + at + 4);
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(&d);
-    float s = __uint_as_float(w[0] << 16) * o0.x + __uint_as_float(w[0] & 0xFFFF0000u) * o0.y +
-              __uint_as_float(w[1] << 16) * o0.z + __uint_as_float(w[1] & 0xFFFF0000u) * o0.w +
-              __uint_as_float(w[2] << 16) * o1.x + __uint_as_float(w[2] & 0xFFFF0000u) * o1.y +
-              __uint_as_float(w[3] << 16) * o1.z + __uint_as_float(w[3] & 0xFFFF0000u) * o1.w;
+  // two rows per thread per pass (the second RPB rows further), so that both rows' loads are in flight together
+  for (int64_t row = r0 + threadIdx.x / LPR; row < r1; row += 2 * RPB) {
+    const bool two = row + RPB < r1;  // uniform over the row's LPR lanes
+    const int64_t at[2] = {row * D + 8 * sub, (row + (two ? RPB : 0)) * D + 8 * sub};
+    uint4 k[2], v[2], d[2];
+    float4 o[2][2];
 #pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) s += __shfl_xor(s, off);
+    for (int u = 0; u < 2; ++u) {
+      k[u] = ldg16(K + at[u]);
+      if (convert_v) v[u] = ldg16(V + at[u]);
+      d[u] = ldg16(dO + at[u]);
+      o[u][0] = *reinterpret_cast<const float4*>(O + at[u]);
+      o[u][1] = *reinterpret_cast<const float4*>(O + at[u] + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u == 1 && !two) break;
+      *reinterpret_cast<uint4*>(K16 + at[u]) = bf16x8_to_f16x8_scaled(k[u], eK);
+      if (convert_v) *reinterpret_cast<uint4*>(V16 + at[u]) = bf16x8_to_f16x8_scaled(v[u], eV);
+    }
+    float s[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(&d[u]);
+      const float4 o0 = o[u][0], o1 = o[u][1];
+      s[u] = __uint_as_float(w[0] << 16) * o0.x + __uint_as_float(w[0] & 0xFFFF0000u) * o0.y +
+             __uint_as_float(w[1] << 16) * o0.z + __uint_as_float(w[1] & 0xFFFF0000u) * o0.w +
+             __uint_as_float(w[2] << 16) * o1.x + __uint_as_float(w[2] & 0xFFFF0000u) * o1.y +
+             __uint_as_float(w[3] << 16) * o1.z + __uint_as_float(w[3] & 0xFFFF0000u) * o1.w;
+#pragma unroll
+      for (int off = 1; off < LPR; off <<= 1) s[u] += __shfl_xor(s[u], off);
+    }
     if (sub == 0) {
-      Dvec[row] = s;
-      nl2[row] = -LSE[row] * kLog2e;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (u == 1 && !two) break;
+        const int64_t r = row + u * RPB;
+        Dvec[r] = s[u];
+        nl2[r] = -LSE[r] * kLog2e;
+      }
     }
   }
 }

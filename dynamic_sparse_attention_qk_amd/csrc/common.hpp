@@ -379,13 +379,23 @@ __global__ __launch_bounds__(256) void amax_kernel(AmaxSrc src, uint32_t* __rest
   const int64_t n16 = n_per_bh / 8;
   const int64_t lo = n16 * chunk / kAmaxChunks, hi = n16 * (chunk + 1) / kAmaxChunks;
   const uint4* p = reinterpret_cast<const uint4*>(src.t[t] + (int64_t)bh * n_per_bh);
-  uint32_t m = 0;
-  for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
-    const uint4 v = p[i];
+  auto amax8 = [](const uint4& v) {
     const uint32_t w[4] = {v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu, v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu};
+    uint32_t r = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) m = max(m, max(w[q] & 0xFFFFu, w[q] >> 16));
+    for (int q = 0; q < 4; ++q) r = max(r, max(w[q] & 0xFFFFu, w[q] >> 16));
+    return r;
+  };
+  uint32_t m = 0;
+  int64_t i = lo + threadIdx.x;
+  for (; i + 3 * 256 < hi; i += 4 * 256) {  // four loads in flight per thread
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = p[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m = max(m, amax8(v[u]));
   }
+  for (; i < hi; i += 256) m = max(m, amax8(p[i]));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;

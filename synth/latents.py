@@ -27,7 +27,7 @@ from __future__ import annotations
 
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
-from typing import Dict, Optional, Sequence
+from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -60,6 +60,53 @@ def morton_order(grid) -> np.ndarray:
     return np.stack([t[order], y[order], x[order]], axis=1).astype(np.int64)
 
 
+def _morton_keys(t: np.ndarray, y: np.ndarray, x: np.ndarray, nbits: int) -> np.ndarray:
+    key = np.zeros(t.shape, dtype=np.int64)
+    for b in range(nbits):
+        digit = ((t >> b) & 1) * 4 + ((y >> b) & 1) * 2 + ((x >> b) & 1)
+        key |= digit.astype(np.int64) << (3 * b)
+    return key
+
+
+def cube_box(group: int) -> Tuple[int, int, int]:
+    """The (t, y, x) box one query group fills in cube order: 4x4x4 for 64 tokens, 4x4x8 for 128."""
+    if group % 16 or group < 16:
+        raise ValueError("cube order needs a group size that is a multiple of 16")
+    return (4, 4, group // 16)
+
+
+def cube_order(grid, group: int) -> np.ndarray:
+    """Grid cells (t, y, x) as an [N, 3] int64 array in cube order for groups of ``group`` tokens.
+
+    The grid is tiled by aligned boxes of cube_box(group) cells (a union of aligned 2x2x2 cubes).  The boxes
+    that lie wholly inside the grid come first, in Morton order of their box coordinates, each box's cells in
+    Morton order within it, so that every group of ``group`` consecutive tokens among them is exactly one box.
+    The cells of the partial boxes along sides not divisible by the box follow, in Morton order of their grid
+    coordinates.
+    """
+    t_n, y_n, x_n = grid
+    bt, by, bx = cube_box(group)
+    t, y, x = np.meshgrid(np.arange(t_n), np.arange(y_n), np.arange(x_n), indexing="ij")
+    t, y, x = t.ravel(), y.ravel(), x.ravel()
+    full = (t < (t_n // bt) * bt) & (y < (y_n // by) * by) & (x < (x_n // bx) * bx)
+    nb = int(max(t_n, y_n, x_n) - 1).bit_length() + 1
+    box_key = _morton_keys(t // bt, y // by, x // bx, nb)
+    in_key = _morton_keys(t % bt, y % by, x % bx, 4)
+    glob_key = _morton_keys(t, y, x, nb)
+    # full boxes first (by box, then within the box), then the partial-box cells by their own Morton key
+    order = np.lexsort((np.where(full, in_key, glob_key), np.where(full, box_key, 0), ~full))
+    return np.stack([t[order], y[order], x[order]], axis=1).astype(np.int64)
+
+
+def token_order(w: Workload) -> np.ndarray:
+    """The workload's token order: ``w.order`` "morton" (default) or "cubes"."""
+    if w.order == "morton":
+        return morton_order(w.grid)
+    if w.order == "cubes":
+        return cube_order(w.grid, w.group)
+    raise ValueError(f"unknown token order {w.order!r}")
+
+
 def nearest_centre(coords: np.ndarray, centres: np.ndarray, chunk: int = 65536) -> np.ndarray:
     """Index of the nearest centre for each coordinate (exact integer distances, lowest id on ties)."""
     out = np.empty(coords.shape[0], dtype=np.int64)
@@ -79,7 +126,7 @@ class Inputs:
     do: Optional[np.ndarray]
     w: np.ndarray                 # [H, d, r] float32 (W_q = W_k)
     k_per_head: np.ndarray        # [H] int32 kept blocks per (head, group)
-    coords: np.ndarray            # [N, 3] token grid coordinates (Morton order)
+    coords: np.ndarray            # [N, 3] token grid coordinates (in the workload's token order)
     cell_centre: np.ndarray       # [N] nearest-centre id of each token
     head_scale: np.ndarray        # [H] cluster scale per head
     head_keep: np.ndarray         # [H] keep fraction per head (nan when k is explicit)
@@ -127,7 +174,7 @@ def generate(w: Workload, threads: int = 8, heads: Optional[Sequence[int]] = Non
     """
     if w.seq_len % w.block or w.seq_len % w.group:
         raise ValueError("token count must be a multiple of the block and group sizes")
-    coords = morton_order(w.grid)
+    coords = token_order(w)
     root = np.random.SeedSequence(w.seed)
     n_tensors = 4 if w.backward else 3
     children = root.spawn(1 + n_tensors * w.batch * w.heads)
@@ -162,7 +209,7 @@ def generate(w: Workload, threads: int = 8, heads: Optional[Sequence[int]] = Non
 
 def per_head_k(w: Workload) -> np.ndarray:
     """The kept-block counts k_h of a workload without drawing its tensors."""
-    coords = morton_order(w.grid)
+    coords = token_order(w)
     child = np.random.SeedSequence(w.seed).spawn(1)[0]
     return _structure(w, np.random.Generator(np.random.PCG64(child)), coords)[4]
 

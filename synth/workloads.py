@@ -38,6 +38,7 @@ class Workload:
     backward: bool = True
     streamed: bool = False              # block scores streamed through the selection
     block: int = 64
+    order: str = "morton"               # token order: "morton", or "cubes" (groups = aligned 4x4x(G/16) boxes)
 
     @property
     def seq_len(self) -> int:

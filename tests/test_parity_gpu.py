@@ -30,9 +30,9 @@ def _gpu():
 
 
 def _wl(grid, heads, d, group, k=None, rank=16, dtype="bf16", backward=True, centres=8, seed=77, kph=None,
-        batch=1):
-    w = synth.Workload(f"small_{grid}_{heads}_{d}_{group}_{batch}", seed, batch, heads, d, grid, centres, 3.0, rank,
-                       group, k=k, dtype=dtype, backward=backward)
+        batch=1, order="morton"):
+    w = synth.Workload(f"small_{grid}_{heads}_{d}_{group}_{batch}_{order}", seed, batch, heads, d, grid, centres, 3.0,
+                       rank, group, k=k, dtype=dtype, backward=backward, order=order)
     return w
 
 
@@ -62,6 +62,9 @@ SMALL = [
     ("d64_g128_k1", _wl((4, 16, 32), 2, 64, 128, k=1, rank=16), None),
     ("batch3_ragged_heads", _wl((2, 16, 32), 3, 128, 64, k=4, rank=32, batch=3), [2, 7, 4]),
     ("batch2_fp32_fwd", _wl((2, 16, 16), 2, 64, 64, k=3, dtype="f32", backward=False, batch=2), None),
+    # cube-ordered tokens: every group an aligned 4x4x4 (4x4x8) box; rows y = 20, 21 are partial-edge groups
+    ("cubes_g64_edge_rows", _wl((4, 22, 24), 2, 128, 64, k=7, rank=32, order="cubes"), None),
+    ("cubes_g128", _wl((8, 16, 16), 2, 128, 128, k=6, rank=32, order="cubes"), None),
 ]
 
 

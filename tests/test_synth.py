@@ -27,6 +27,25 @@ def test_morton_order_is_a_permutation_and_compact():
     assert np.median(ext) <= 64
 
 
+def test_cube_order_option_changes_only_the_token_order():
+    # on power-of-two sides the two orders coincide; a side of 6 beside a longer one makes them differ
+    assert np.array_equal(synth.cube_order((4, 8, 8), 64), synth.morton_order((4, 8, 8)))
+    w = synth.workload(1).with_(grid=(4, 6, 16), heads=1)
+    wc = w.with_(order="cubes")
+    a, c = synth.generate(w), synth.generate(wc)
+    np.testing.assert_array_equal(a.coords, synth.morton_order(w.grid))
+    np.testing.assert_array_equal(c.coords, synth.cube_order(w.grid, w.group))
+    assert not np.array_equal(a.coords, c.coords)
+    assert sorted(map(tuple, a.coords.tolist())) == sorted(map(tuple, c.coords.tolist()))
+    np.testing.assert_array_equal(c.q, synth.generate(wc).q)       # deterministic
+    try:
+        synth.generate(w.with_(order="raster"))
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("unknown order accepted")
+
+
 def test_generate_deterministic_and_shaped():
     w = synth.workload(1)
     a, b = synth.generate(w), synth.generate(w)

@@ -5,7 +5,10 @@ Recipe (everything derives from ``numpy.random.SeedSequence(workload.seed)``):
 * Token order.  The T x Y x X latent grid is flattened in Morton (Z) order of
   (t, y, x): key = sum_b (t_b*4 + y_b*2 + x_b) * 8**b over the coordinate bits
   b, tokens sorted by key.  Consecutive runs of 64 tokens are then compact 3D
-  neighbourhoods, the adjacency that query grouping relies on.
+  neighbourhoods, the adjacency that query grouping relies on.  Option
+  (``order="cubes"``): the aligned 4x4x(G/16) boxes that lie wholly inside the
+  grid first (boxes in Morton order, cells in Morton order within each box),
+  then the remaining cells in Morton order, so every group is one box.
 * Structure stream (child 0 of the seed sequence), drawn in this order:
   cluster centres (distinct grid cells, uniform without replacement), one
   N(0, I_d) vector per (head, centre) (float64), then -- per-head workloads

@@ -913,3 +913,38 @@ def test_mutation_block_part_without_D(monkeypatch):
     monkeypatch.setattr(O, "dkdv_block_part", bad)
     with pytest.raises(AssertionError):
         check_dkdv_block_part()
+
+
+def test_mutation_backward_dk_without_tau(monkeypatch):
+    def bad(qg, k, v, dog, keys):   # dK misses the logit scale tau = 1/sqrt(d) that dQ keeps
+        tau = 1.0 / np.sqrt(qg.shape[1])
+        og, lse, p = O.group_forward(qg, k, v, keys)
+        dvec = (dog * og).sum(axis=1)
+        ds = p * (dog @ v[keys].T - dvec[:, None])
+        return tau * (ds @ k[keys]), ds.T @ qg, p.T @ dog, og, lse
+    assert _fails_some_pin(monkeypatch, "group_backward", bad, [check_finite_differences,
+                                                                 check_sparse_equals_masked_sdpa])
+
+
+def test_mutation_backward_dq_tau_twice(monkeypatch):
+    def bad(qg, k, v, dog, keys):   # dQ scaled by tau^2
+        tau = 1.0 / np.sqrt(qg.shape[1])
+        og, lse, p = O.group_forward(qg, k, v, keys)
+        dvec = (dog * og).sum(axis=1)
+        ds = p * (dog @ v[keys].T - dvec[:, None])
+        return tau * tau * (ds @ k[keys]), tau * (ds.T @ qg), p.T @ dog, og, lse
+    assert _fails_some_pin(monkeypatch, "group_backward", bad, [check_finite_differences,
+                                                                 check_sparse_equals_masked_sdpa])
+
+
+def test_mutation_backward_dv_unnormalised(monkeypatch):
+    def bad(qg, k, v, dog, keys):   # dV from exp(logits - row max) instead of the normalised P
+        tau = 1.0 / np.sqrt(qg.shape[1])
+        og, lse, p = O.group_forward(qg, k, v, keys)
+        logits = tau * (qg @ k[keys].T)
+        e = np.exp(logits - logits.max(axis=1, keepdims=True))
+        dvec = (dog * og).sum(axis=1)
+        ds = p * (dog @ v[keys].T - dvec[:, None])
+        return tau * (ds @ k[keys]), tau * (ds.T @ qg), e.T @ dog, og, lse
+    assert _fails_some_pin(monkeypatch, "group_backward", bad, [check_finite_differences,
+                                                                 check_sparse_equals_masked_sdpa])
